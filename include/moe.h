@@ -1,0 +1,219 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the forward pass of one Mixture-of-Experts layer
+ * on an AMD Instinct MI355X (gfx950).
+ *
+ * The layer (MoE lesson, factory.pai-world.com "Mixture of Experts", section
+ * "FFN swap"; MoE playbook, molayo1419.me, section "How it works"):
+ *
+ *   logits = x W_r^T                       router, one linear layer   (moe_route)
+ *   idx    = top-k of the selection keys    bias enters selection only (moe_route)
+ *   g      = gates over the chosen experts  unbiased scores            (moe_route)
+ *   rows   = tokens grouped by expert       dispatch                   (moe_dispatch)
+ *   h      = silu(x Wg^T) * (x Wu^T)        linear1 + SwiGLU           (moe_ffn)
+ *   o      = h Wd^T                         linear2                    (moe_ffn)
+ *   y      = sum_j g_j o_j + o_shared       gate-weighted combine      (moe_combine)
+ *
+ * moe_layer_fused runs the whole chain in one persistent launch, the one-GPU
+ * counterpart of the single mega-kernel that fuses dispatch, linear1, SwiGLU,
+ * linear2 and combine (Mega MoE wiki, aiki.softdaddy-o.com, "One-line
+ * definition"; Mega MoE blog, donniechu.com, spec table "Ops fused in 1 kernel").
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named x, y, w*, idx, gate, counts, offsets, *_row, *_slot, ws are
+ *    DEVICE pointers; moe_cfg and moe_weights structs are HOST memory read only
+ *    during the call.  The caller allocates and owns every buffer; the library
+ *    never allocates device memory and keeps no state between calls.
+ *  - Every call is asynchronous and stream-ordered on `stream`.  The return value
+ *    reports host-side validation and launch errors only.  Errors found by a
+ *    kernel (bad or duplicate expert indices, non-finite keys, an expired bounded
+ *    wait) set a sticky word at the start of the workspace; read it with
+ *    moe_read_device_error.
+ *  - All device pointers must be 16-byte aligned.
+ *  - Outputs are bitwise deterministic: identical inputs give identical bits.
+ *    No floating-point atomics are used.
+ *  - T == 0 is a valid no-op (MOE_OK, nothing launched).
+ *  - Calls that share a workspace must not overlap on the device.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,      /* a required pointer is NULL */
+    MOE_ERR_SHAPE = 2,     /* shape outside the supported limits (see moe_cfg) */
+    MOE_ERR_MODE = 3,      /* unknown mode or gating */
+    MOE_ERR_ALIGN = 4,     /* a device pointer is not 16-byte aligned */
+    MOE_ERR_WORKSPACE = 5, /* ws is NULL or smaller than moe_workspace_bytes() */
+    MOE_ERR_LAUNCH = 6,    /* a HIP launch or runtime call failed */
+    MOE_ERR_ARCH = 7,      /* the current device is not gfx950 */
+    MOE_ERR_DEVICE = 8     /* a kernel reported an error (moe_read_device_error) */
+} moe_status;
+
+/*
+ * Arithmetic modes.
+ *  MOE_MODE_F32:       x, W_r, W1, W2, y fp32; y_perm fp32; fp32 accumulation.
+ *  MOE_MODE_BF16:      x, W_r, W1, W2, y bf16; fp32 accumulation; h and y_perm bf16.
+ *  MOE_MODE_FP8_MXFP4: x, W_r, y bf16. The router runs in bf16 with fp32 sums.
+ *                      Expert inputs x and h are quantised in-layer to FP8 e4m3
+ *                      (OCP E4M3FN) with one power-of-two fp32 scale per 1x128
+ *                      block along K; W1, W2 are MXFP4 (OCP MX v1.0): e2m1 codes,
+ *                      two per byte, even K index in the low nibble, plus one e8m0
+ *                      scale byte per 32 consecutive K.  Both linears are FP8 x FP4
+ *                      (Mega MoE blog, donniechu.com, spec table), fp32
+ *                      accumulation; y_perm bf16.
+ */
+typedef enum { MOE_MODE_F32 = 0, MOE_MODE_BF16 = 1, MOE_MODE_FP8_MXFP4 = 2 } moe_mode;
+
+/*
+ * Gating (MoE lesson "Build it, Step 1: router" and "Load balancing"; the
+ * sigmoid form is the reading taken for the DeepSeek-V3-shaped workload):
+ *  MOE_GATE_SOFTMAX: key = logit + bias;          gate_j = softmax over the chosen raw logits.
+ *  MOE_GATE_SIGMOID: key = sigmoid(logit) + bias; gate_j = s_j / sum of the chosen s.
+ * Top-k orders experts by descending key; equal keys go to the lower expert index.
+ */
+typedef enum { MOE_GATE_SOFTMAX = 0, MOE_GATE_SIGMOID = 1 } moe_gating;
+
+/*
+ * Shapes.  T tokens, d model width, E routed experts, k experts per token, F
+ * expert hidden width, n_shared in {0, 1} always-on shared experts (MoE lesson,
+ * "Shared expert").  G = E + n_shared expert groups; the shared expert is group E.
+ * Limits: 0 <= T <= 2^20, 1 <= k <= min(E, 16), E <= 1024, d and F multiples of
+ * 128 (every mode), T*(k+n_shared) < 2^31.
+ * cu_limit caps the number of compute units the persistent kernels spread over
+ * (0 = all).
+ */
+typedef struct {
+    int32_t T, d, E, k, F, n_shared;
+    int32_t gating;   /* moe_gating */
+    int32_t mode;     /* moe_mode */
+    int32_t cu_limit; /* 0 = all compute units */
+    int32_t reserved; /* must be 0 */
+} moe_cfg;
+
+/*
+ * Expert weights, canonical layout (out x in, K contiguous), G groups:
+ *  w1 [G, 2F, d]: rows 0..F-1 are W_gate, rows F..2F-1 are W_up.
+ *  w2 [G, d, F]:  W_down.
+ *  fp32 / bf16 modes: values; w1_scale = w2_scale = NULL.
+ *  FP8 x MXFP4 mode:  w1 [G, 2F, d/2] and w2 [G, d, F/2] bytes of e2m1 codes;
+ *                     w1_scale [G, 2F, d/32], w2_scale [G, d, F/32] e8m0 bytes.
+ */
+typedef struct {
+    const void *w1, *w1_scale, *w2, *w2_scale;
+} moe_weights;
+
+/* Device error codes stored in the workspace's sticky word (first error wins). */
+#define MOE_DEVERR_NONE 0
+#define MOE_DEVERR_INDEX 1     /* an expert index outside [0, E) */
+#define MOE_DEVERR_DUP 2       /* a token chose the same expert twice */
+#define MOE_DEVERR_NONFINITE 3 /* a selection key is NaN or infinite */
+#define MOE_DEVERR_TIMEOUT 4   /* a bounded wait in the persistent kernel expired */
+
+/* Human-readable name of a status code (static string). */
+const char *moe_status_str(moe_status s);
+
+/* Checks that the current HIP device is gfx950. MOE_OK or MOE_ERR_ARCH / MOE_ERR_LAUNCH. */
+moe_status moe_device_check(void);
+
+/*
+ * Bytes of device workspace every call with this configuration needs (the same
+ * size serves all entry points).  0 if cfg is invalid.  The workspace holds the
+ * sticky error word, dispatch block counts, the tile plan, the intermediate h
+ * (and its FP8 scales), and the persistent kernel's counters.
+ */
+size_t moe_workspace_bytes(const moe_cfg *cfg);
+
+/*
+ * Clears the sticky error word (stream-ordered).  Call once on a new workspace.
+ */
+moe_status moe_clear_device_error(const moe_cfg *cfg, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Copies the sticky error word to *code_out (host memory) and synchronises
+ * `stream`.  Returns MOE_ERR_DEVICE if the word is non-zero.
+ */
+moe_status moe_read_device_error(const moe_cfg *cfg, const void *ws, int32_t *code_out, hipStream_t stream);
+
+/*
+ * Router, selection and gates (MoE lesson "FFN swap" and "Build it, Step 1:
+ * router"; MoE playbook "How it works", score and select).
+ *  x [T, d]        activations (fp32 in F32 mode, else bf16)
+ *  w_router [E, d] router weight (same dtype as x)
+ *  bias [E]        fp32 selection bias, or NULL for zeros (MoE lesson "Load balancing")
+ *  topk_idx [T, k]  int32 out: chosen experts, descending key, ties to the lower index
+ *  topk_gate [T, k] fp32 out: gates
+ *  logits [T, E]    fp32 out or NULL: x W_r^T
+ *  keys [T, E]      fp32 out or NULL: selection keys
+ *  ws: workspace (only the error word is used).
+ */
+moe_status moe_route(const moe_cfg *cfg, const void *x, const void *w_router, const float *bias,
+                     int32_t *topk_idx, float *topk_gate, float *logits, float *keys, void *ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Dispatch: group the T*k (token, choice) slots by expert (Mega MoE wiki,
+ * "How it works": tokens are sent to their experts before the expert MLPs).
+ * Slot s = t*k + j.  Rows of expert e are offsets[e] .. offsets[e+1]-1, in
+ * ascending token order; the shared expert (group E) owns rows T*k + t.
+ *  topk_idx [T, k]     int32 in
+ *  x [T, d]            activations (read only in FP8 x MXFP4 mode, else may be NULL)
+ *  counts [G]          int32 out: rows per group (counts[E] = T when n_shared)
+ *  offsets [G + 1]     int32 out: exclusive prefix of counts
+ *  slot_to_row [T*k]   int32 out
+ *  row_to_slot [T*k]   int32 out: inverse permutation
+ *  xq [T, d]           FP8 mode: uint8 e4m3 codes out (token order; gathered on load)
+ *  xq_scale [T, d/128] FP8 mode: fp32 power-of-two scales out
+ * Indices outside [0, E) or repeated within a token set the device error word
+ * (MOE_DEVERR_INDEX / MOE_DEVERR_DUP); the outputs are then unspecified.
+ */
+moe_status moe_dispatch(const moe_cfg *cfg, const int32_t *topk_idx, const void *x, int32_t *counts,
+                        int32_t *offsets, int32_t *slot_to_row, int32_t *row_to_slot, uint8_t *xq,
+                        float *xq_scale, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Expert FFNs over the dispatched rows: linear1 (gate+up) with SwiGLU fused in
+ * its epilogue, then linear2 (Mega MoE blog, donniechu.com, spec table).
+ * Row r of group g reads token row_to_slot[r] / k (routed) or r - T*k (shared).
+ *  w               weights (moe_weights, canonical layout)
+ *  x [T, d]        activations (F32 / BF16 modes)
+ *  xq, xq_scale    FP8 codes and scales from moe_dispatch (FP8 x MXFP4 mode)
+ *  offsets [G+1], row_to_slot [T*k]: from moe_dispatch
+ *  y_perm [T*k + n_shared*T, d] out: expert output per row (fp32 in F32 mode, else bf16)
+ */
+moe_status moe_ffn(const moe_cfg *cfg, const moe_weights *w, const void *x, const uint8_t *xq,
+                   const float *xq_scale, const int32_t *offsets, const int32_t *row_to_slot, void *y_perm,
+                   void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Gate-weighted combine (MoE playbook "How it works", combine step; MoE lesson
+ * "Shared expert"):  y[t] = (((g_0 o_0 + g_1 o_1) + ...) + g_{k-1} o_{k-1}) + o_shared
+ * in fp32 in exactly that order, then rounded to nearest even to y's dtype.
+ *  y_perm [T*k + n_shared*T, d], slot_to_row [T*k], topk_gate [T, k] in;  y [T, d] out.
+ */
+moe_status moe_combine(const moe_cfg *cfg, const void *y_perm, const int32_t *slot_to_row,
+                       const float *topk_gate, void *y, hipStream_t stream);
+
+/*
+ * The whole layer in one persistent launch: route, dispatch, linear1 + SwiGLU,
+ * linear2 and combine, chained on device with bounded waits.  Bitwise equal to
+ * moe_route -> moe_dispatch -> moe_ffn -> moe_combine on the same inputs.
+ *  x [T, d], w_router [E, d], bias [E] or NULL, w: as above; y [T, d] out.
+ *  topk_idx_out [T, k], topk_gate_out [T, k], counts_out [G]: optional copies (NULL to skip).
+ */
+moe_status moe_layer_fused(const moe_cfg *cfg, const moe_weights *w, const void *x, const void *w_router,
+                           const float *bias, void *y, int32_t *topk_idx_out, float *topk_gate_out,
+                           int32_t *counts_out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

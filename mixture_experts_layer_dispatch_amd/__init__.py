@@ -1,0 +1,257 @@
+"""Python binding for libmoe.so: the MI355X (gfx950) MoE-layer forward.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+``libmoe.so``.  PyTorch supplies device memory and the current stream.  Names
+follow the C ABI in ``include/moe.h``:
+
+    route, dispatch, ffn, combine, layer_fused, workspace_bytes, read_device_error
+
+There is no fallback: if ``libmoe.so`` is missing or cannot load, importing the
+library functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MODES = {"f32": 0, "bf16": 1, "fp8_mxfp4": 2}
+GATINGS = {"softmax": 0, "sigmoid": 1}
+DEVERR = {0: "none", 1: "expert index out of range", 2: "duplicate expert in a token",
+          3: "non-finite selection key", 4: "bounded wait expired"}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class MoeCfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("T", "d", "E", "k", "F", "n_shared", "gating", "mode", "cu_limit", "reserved")]
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [("w1", ctypes.c_void_p), ("w1_scale", ctypes.c_void_p),
+                ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmoe.so (raises OSError when it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise OSError(f"{LIB_PATH} not found: build it with mixture_experts_layer_dispatch_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        VP, SZ, I32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        CP, WP = ctypes.POINTER(MoeCfg), ctypes.POINTER(MoeWeights)
+        L.moe_status_str.argtypes = [I32]
+        L.moe_status_str.restype = ctypes.c_char_p
+        L.moe_device_check.argtypes = []
+        L.moe_workspace_bytes.argtypes = [CP]
+        L.moe_workspace_bytes.restype = SZ
+        L.moe_clear_device_error.argtypes = [CP, VP, SZ, VP]
+        L.moe_read_device_error.argtypes = [CP, VP, ctypes.POINTER(ctypes.c_int32), VP]
+        L.moe_route.argtypes = [CP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_dispatch.argtypes = [CP, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_ffn.argtypes = [CP, WP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_combine.argtypes = [CP, VP, VP, VP, VP, VP]
+        L.moe_layer_fused.argtypes = [CP, WP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        for f in ("moe_device_check", "moe_clear_device_error", "moe_read_device_error", "moe_route",
+                  "moe_dispatch", "moe_ffn", "moe_combine", "moe_layer_fused"):
+            getattr(L, f).restype = I32
+        _lib = L
+    return _lib
+
+
+EXPORTS = ("moe_status_str", "moe_device_check", "moe_workspace_bytes", "moe_clear_device_error",
+           "moe_read_device_error", "moe_route", "moe_dispatch", "moe_ffn", "moe_combine", "moe_layer_fused")
+
+
+@dataclass(frozen=True)
+class Config:
+    T: int
+    d: int
+    E: int
+    k: int
+    F: int
+    n_shared: int = 0
+    gating: str = "softmax"
+    mode: str = "bf16"
+    cu_limit: int = 0
+
+    @property
+    def G(self) -> int:
+        return self.E + self.n_shared
+
+    @property
+    def rows(self) -> int:
+        return self.T * self.k + self.n_shared * self.T
+
+    def c(self) -> MoeCfg:
+        return MoeCfg(self.T, self.d, self.E, self.k, self.F, self.n_shared, GATINGS[self.gating],
+                      MODES[self.mode], self.cu_limit, 0)
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise MoeError(status, f"{what}: {lib().moe_status_str(status).decode()}")
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _expect(t, shape, dtype, name):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name}: expected {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
+
+
+def act_dtype(cfg: Config):
+    return torch.float32 if cfg.mode == "f32" else torch.bfloat16
+
+
+def workspace_bytes(cfg: Config) -> int:
+    n = lib().moe_workspace_bytes(ctypes.byref(cfg.c()))
+    if n == 0:
+        raise MoeError(2, "invalid configuration")
+    return n
+
+
+def alloc_workspace(cfg: Config, device="cuda") -> torch.Tensor:
+    """A zero-initialised workspace (torch allocates it; the library never does)."""
+    ws = torch.zeros(workspace_bytes(cfg), dtype=torch.uint8, device=device)
+    return ws
+
+
+def clear_device_error(cfg: Config, ws: torch.Tensor, stream=None):
+    _check(lib().moe_clear_device_error(ctypes.byref(cfg.c()), _p(ws), ws.numel(), _stream(stream)),
+           "moe_clear_device_error")
+
+
+def read_device_error(cfg: Config, ws: torch.Tensor, stream=None) -> int:
+    code = ctypes.c_int32(0)
+    st = lib().moe_read_device_error(ctypes.byref(cfg.c()), _p(ws), ctypes.byref(code), _stream(stream))
+    if st not in (0, 8):
+        _check(st, "moe_read_device_error")
+    return code.value
+
+
+def route(cfg: Config, x, w_router, bias=None, *, ws, topk_idx=None, topk_gate=None, logits=None, keys=None,
+          want_logits=False, stream=None):
+    """S1-S4.  Returns (topk_idx [T,k] int32, topk_gate [T,k] f32, logits|None, keys|None)."""
+    dev = x.device
+    _expect(x, (cfg.T, cfg.d), act_dtype(cfg), "x")
+    _expect(w_router, (cfg.E, cfg.d), act_dtype(cfg), "w_router")
+    if bias is not None:
+        _expect(bias, (cfg.E,), torch.float32, "bias")
+    topk_idx = topk_idx if topk_idx is not None else torch.empty(cfg.T, cfg.k, dtype=torch.int32, device=dev)
+    topk_gate = topk_gate if topk_gate is not None else torch.empty(cfg.T, cfg.k, dtype=torch.float32, device=dev)
+    if want_logits:
+        logits = logits if logits is not None else torch.empty(cfg.T, cfg.E, dtype=torch.float32, device=dev)
+        keys = keys if keys is not None else torch.empty(cfg.T, cfg.E, dtype=torch.float32, device=dev)
+    _check(lib().moe_route(ctypes.byref(cfg.c()), _p(x), _p(w_router), _p(bias), _p(topk_idx), _p(topk_gate),
+                           _p(logits), _p(keys), _p(ws), ws.numel(), _stream(stream)), "moe_route")
+    return topk_idx, topk_gate, logits, keys
+
+
+def dispatch(cfg: Config, topk_idx, x=None, *, ws, out=None, stream=None):
+    """S5-S7.  Returns dict(counts, offsets, slot_to_row, row_to_slot, xq, xq_scale)."""
+    dev = topk_idx.device
+    _expect(topk_idx, (cfg.T, cfg.k), torch.int32, "topk_idx")
+    o = dict(out or {})
+    o.setdefault("counts", torch.empty(cfg.G, dtype=torch.int32, device=dev))
+    o.setdefault("offsets", torch.empty(cfg.G + 1, dtype=torch.int32, device=dev))
+    o.setdefault("slot_to_row", torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev))
+    o.setdefault("row_to_slot", torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev))
+    if cfg.mode == "fp8_mxfp4":
+        _expect(x, (cfg.T, cfg.d), torch.bfloat16, "x")
+        o.setdefault("xq", torch.empty(cfg.T, cfg.d, dtype=torch.uint8, device=dev))
+        o.setdefault("xq_scale", torch.empty(cfg.T, cfg.d // 128, dtype=torch.float32, device=dev))
+    else:
+        o.setdefault("xq", None)
+        o.setdefault("xq_scale", None)
+    _check(lib().moe_dispatch(ctypes.byref(cfg.c()), _p(topk_idx), _p(x), _p(o["counts"]), _p(o["offsets"]),
+                              _p(o["slot_to_row"]), _p(o["row_to_slot"]), _p(o["xq"]), _p(o["xq_scale"]),
+                              _p(ws), ws.numel(), _stream(stream)), "moe_dispatch")
+    return o
+
+
+def _weights(cfg: Config, w1, w2, w1_scale=None, w2_scale=None) -> MoeWeights:
+    G, F, d = cfg.G, cfg.F, cfg.d
+    if cfg.mode == "fp8_mxfp4":
+        _expect(w1, (G, 2 * F, d // 2), torch.uint8, "w1")
+        _expect(w2, (G, d, F // 2), torch.uint8, "w2")
+        _expect(w1_scale, (G, 2 * F, d // 32), torch.uint8, "w1_scale")
+        _expect(w2_scale, (G, d, F // 32), torch.uint8, "w2_scale")
+    else:
+        _expect(w1, (G, 2 * F, d), act_dtype(cfg), "w1")
+        _expect(w2, (G, d, F), act_dtype(cfg), "w2")
+    return MoeWeights(_p(w1), _p(w1_scale), _p(w2), _p(w2_scale))
+
+
+def ffn(cfg: Config, w1, w2, w1_scale=None, w2_scale=None, *, x=None, xq=None, xq_scale=None, offsets,
+        row_to_slot, ws, y_perm=None, stream=None):
+    """S8-S9.  Returns y_perm [T*k + n_shared*T, d] (f32 in f32 mode, else bf16)."""
+    dev = offsets.device
+    ydt = torch.float32 if cfg.mode == "f32" else torch.bfloat16
+    y_perm = y_perm if y_perm is not None else torch.empty(cfg.rows, cfg.d, dtype=ydt, device=dev)
+    W = _weights(cfg, w1, w2, w1_scale, w2_scale)
+    _check(lib().moe_ffn(ctypes.byref(cfg.c()), ctypes.byref(W), _p(x), _p(xq), _p(xq_scale), _p(offsets),
+                         _p(row_to_slot), _p(y_perm), _p(ws), ws.numel(), _stream(stream)), "moe_ffn")
+    return y_perm
+
+
+def combine(cfg: Config, y_perm, slot_to_row, topk_gate, *, y=None, stream=None):
+    """S10.  Returns y [T, d]."""
+    y = y if y is not None else torch.empty(cfg.T, cfg.d, dtype=act_dtype(cfg), device=y_perm.device)
+    _check(lib().moe_combine(ctypes.byref(cfg.c()), _p(y_perm), _p(slot_to_row), _p(topk_gate), _p(y),
+                             _stream(stream)), "moe_combine")
+    return y
+
+
+def layer_fused(cfg: Config, x, w_router, w1, w2, w1_scale=None, w2_scale=None, bias=None, *, ws, y=None,
+                topk_idx=None, topk_gate=None, counts=None, stream=None):
+    """The whole layer in one call.  Returns y [T, d]."""
+    _expect(x, (cfg.T, cfg.d), act_dtype(cfg), "x")
+    _expect(w_router, (cfg.E, cfg.d), act_dtype(cfg), "w_router")
+    y = y if y is not None else torch.empty(cfg.T, cfg.d, dtype=act_dtype(cfg), device=x.device)
+    W = _weights(cfg, w1, w2, w1_scale, w2_scale)
+    _check(lib().moe_layer_fused(ctypes.byref(cfg.c()), ctypes.byref(W), _p(x), _p(w_router), _p(bias), _p(y),
+                                 _p(topk_idx), _p(topk_gate), _p(counts), _p(ws), ws.numel(), _stream(stream)),
+           "moe_layer_fused")
+    return y
+
+
+def layer_unfused(cfg: Config, x, w_router, w1, w2, w1_scale=None, w2_scale=None, bias=None, *, ws, stream=None):
+    """route -> dispatch -> ffn -> combine as four library calls.  Returns (y, routing dict)."""
+    idx, gate, _, _ = route(cfg, x, w_router, bias, ws=ws, stream=stream)
+    dsp = dispatch(cfg, idx, x, ws=ws, stream=stream)
+    yp = ffn(cfg, w1, w2, w1_scale, w2_scale, x=x if cfg.mode != "fp8_mxfp4" else None, xq=dsp["xq"],
+             xq_scale=dsp["xq_scale"], offsets=dsp["offsets"], row_to_slot=dsp["row_to_slot"], ws=ws, stream=stream)
+    y = combine(cfg, yp, dsp["slot_to_row"], gate, stream=stream)
+    return y, dict(dsp, topk_idx=idx, topk_gate=gate, y_perm=yp)

@@ -1,0 +1,260 @@
+// C ABI of libmoe.so: validation, workspace layout and launches.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+using namespace moe;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+moe_status validate(const moe_cfg *c) {
+    if (!c) return MOE_ERR_NULL;
+    if (c->mode < MOE_MODE_F32 || c->mode > MOE_MODE_FP8_MXFP4) return MOE_ERR_MODE;
+    if (c->gating < MOE_GATE_SOFTMAX || c->gating > MOE_GATE_SIGMOID) return MOE_ERR_MODE;
+    if (c->T < 0 || c->T > (1 << 20)) return MOE_ERR_SHAPE;
+    if (c->E < 1 || c->E > 1024 || c->k < 1 || c->k > 16 || c->k > c->E) return MOE_ERR_SHAPE;
+    if (c->d < 128 || c->d % 128 || c->d > 65536 || c->F < 128 || c->F % 128 || c->F > 65536) return MOE_ERR_SHAPE;
+    if (c->n_shared != 0 && c->n_shared != 1) return MOE_ERR_SHAPE;
+    if (c->reserved != 0 || c->cu_limit < 0) return MOE_ERR_SHAPE;
+    if ((long long)c->T * (c->k + c->n_shared) >= (1LL << 31)) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+Shape shape_of(const moe_cfg *c) {
+    return Shape{c->T, c->d, c->E, c->k, c->F, c->n_shared, c->gating, c->mode};
+}
+
+// Workspace regions (byte offsets, each aligned to 256).
+struct Layout {
+    size_t err, blockcounts, tiles, h, hs;                           // every path
+    size_t idx, gate, counts, offsets, s2r, r2s, xq, xs, yperm, sync; // fused path
+    size_t total;
+};
+
+Layout layout_of(const moe_cfg *c) {
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += (bytes + 255) & ~(size_t)255;
+        return o;
+    };
+    const size_t T = c->T, k = c->k, E = c->E, G = c->E + c->n_shared, d = c->d, F = c->F;
+    const size_t rows = T * k + c->n_shared * T;
+    const bool fp8 = c->mode == MOE_MODE_FP8_MXFP4, f32 = c->mode == MOE_MODE_F32;
+    L.err = take(256);
+    L.blockcounts = take((size_t)dispatch_blocks(c->T) * E * 4);
+    L.tiles = take(2 * (G + 1) * 4);
+    L.h = take(rows * F * (f32 ? 4 : fp8 ? 1 : 2));
+    L.hs = fp8 ? take(rows * (F / 128) * 4) : 0;
+    L.idx = take(T * k * 4);
+    L.gate = take(T * k * 4);
+    L.counts = take(G * 4);
+    L.offsets = take((G + 1) * 4);
+    L.s2r = take(T * k * 4);
+    L.r2s = take(T * k * 4);
+    L.xq = fp8 ? take(T * d) : 0;
+    L.xs = fp8 ? take(T * (d / 128) * 4) : 0;
+    L.yperm = take(rows * d * (f32 ? 4 : 2));
+    L.sync = take(4096);
+    L.total = off;
+    return L;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) {
+    return (T *)((uint8_t *)ws + off);
+}
+
+moe_status check_ws(const moe_cfg *c, const void *ws, size_t ws_bytes) {
+    if (!ws) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    if (ws_bytes < layout_of(c).total) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+// gfx950 check, cached per device.
+std::mutex g_arch_mu;
+int g_arch_ok[64];  // 0 unknown, 1 ok, 2 not gfx950
+
+moe_status arch_check() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_LAUNCH;
+    if (dev < 0 || dev >= 64) return MOE_ERR_ARCH;
+    std::lock_guard<std::mutex> lk(g_arch_mu);
+    if (g_arch_ok[dev] == 0) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess) return MOE_ERR_LAUNCH;
+        g_arch_ok[dev] = std::strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    }
+    return g_arch_ok[dev] == 1 ? MOE_OK : MOE_ERR_ARCH;
+}
+
+__global__ void zero_words_kernel(int32_t *p, int n) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+}  // namespace
+
+#define MOE_TRY(expr)                    \
+    do {                                 \
+        moe_status _s = (expr);          \
+        if (_s != MOE_OK) return _s;     \
+    } while (0)
+
+extern "C" {
+
+const char *moe_status_str(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+        case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: shape outside the supported limits";
+        case MOE_ERR_MODE: return "MOE_ERR_MODE: unknown mode or gating";
+        case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: device pointer not 16-byte aligned";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+        case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH: HIP launch or runtime call failed";
+        case MOE_ERR_ARCH: return "MOE_ERR_ARCH: current device is not gfx950";
+        case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE: a kernel reported an error";
+    }
+    return "unknown moe_status";
+}
+
+moe_status moe_device_check(void) { return arch_check(); }
+
+size_t moe_workspace_bytes(const moe_cfg *cfg) {
+    if (validate(cfg) != MOE_OK) return 0;
+    return layout_of(cfg).total;
+}
+
+moe_status moe_clear_device_error(const moe_cfg *cfg, void *ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(validate(cfg));
+    MOE_TRY(check_ws(cfg, ws, ws_bytes));
+    MOE_TRY(arch_check());
+    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, stream, at<int32_t>(ws, 0), 64);
+    return launched(hipGetLastError());
+}
+
+moe_status moe_read_device_error(const moe_cfg *cfg, const void *ws, int32_t *code_out, hipStream_t stream) {
+    MOE_TRY(validate(cfg));
+    if (!ws || !code_out) return MOE_ERR_NULL;
+    int32_t v = 0;
+    if (hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, stream) != hipSuccess) return MOE_ERR_LAUNCH;
+    if (hipStreamSynchronize(stream) != hipSuccess) return MOE_ERR_LAUNCH;
+    *code_out = v;
+    return v == 0 ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+moe_status moe_route(const moe_cfg *cfg, const void *x, const void *w_router, const float *bias, int32_t *topk_idx,
+                     float *topk_gate, float *logits, float *keys, void *ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(validate(cfg));
+    if (cfg->T == 0) return MOE_OK;
+    if (!x || !w_router || !topk_idx || !topk_gate) return MOE_ERR_NULL;
+    for (const void *p : {x, w_router, (const void *)bias, (const void *)topk_idx, (const void *)topk_gate,
+                          (const void *)logits, (const void *)keys})
+        if (p && !aligned16(p)) return MOE_ERR_ALIGN;
+    MOE_TRY(check_ws(cfg, ws, ws_bytes));
+    MOE_TRY(arch_check());
+    const Layout L = layout_of(cfg);
+    return launched(launch_route(shape_of(cfg), x, w_router, bias, topk_idx, topk_gate, logits, keys,
+                                 at<int32_t>(ws, L.err), stream));
+}
+
+moe_status moe_dispatch(const moe_cfg *cfg, const int32_t *topk_idx, const void *x, int32_t *counts,
+                        int32_t *offsets, int32_t *slot_to_row, int32_t *row_to_slot, uint8_t *xq, float *xq_scale,
+                        void *ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(validate(cfg));
+    if (cfg->T == 0) return MOE_OK;
+    const bool fp8 = cfg->mode == MOE_MODE_FP8_MXFP4;
+    if (!topk_idx || !counts || !offsets || !slot_to_row || !row_to_slot) return MOE_ERR_NULL;
+    if (fp8 && (!x || !xq || !xq_scale)) return MOE_ERR_NULL;
+    for (const void *p : {(const void *)topk_idx, x, (const void *)counts, (const void *)offsets,
+                          (const void *)slot_to_row, (const void *)row_to_slot, (const void *)xq,
+                          (const void *)xq_scale})
+        if (p && !aligned16(p)) return MOE_ERR_ALIGN;
+    MOE_TRY(check_ws(cfg, ws, ws_bytes));
+    MOE_TRY(arch_check());
+    const Layout L = layout_of(cfg);
+    const Shape s = shape_of(cfg);
+    hipError_t e = launch_dispatch(s, topk_idx, at<int32_t>(ws, L.blockcounts), counts, offsets, slot_to_row,
+                                   row_to_slot, at<int32_t>(ws, L.err), stream);
+    if (e == hipSuccess && fp8) e = launch_quant_x(s, (const uint16_t *)x, xq, xq_scale, stream);
+    return launched(e);
+}
+
+moe_status moe_ffn(const moe_cfg *cfg, const moe_weights *w, const void *x, const uint8_t *xq, const float *xq_scale,
+                   const int32_t *offsets, const int32_t *row_to_slot, void *y_perm, void *ws, size_t ws_bytes,
+                   hipStream_t stream) {
+    MOE_TRY(validate(cfg));
+    if (cfg->T == 0) return MOE_OK;
+    const bool fp8 = cfg->mode == MOE_MODE_FP8_MXFP4;
+    if (!w || !w->w1 || !w->w2 || !offsets || !row_to_slot || !y_perm) return MOE_ERR_NULL;
+    if (fp8 && (!w->w1_scale || !w->w2_scale || !xq || !xq_scale)) return MOE_ERR_NULL;
+    if (!fp8 && !x) return MOE_ERR_NULL;
+    for (const void *p : {w->w1, w->w2, w->w1_scale, w->w2_scale, x, (const void *)xq, (const void *)xq_scale,
+                          (const void *)offsets, (const void *)row_to_slot, (const void *)y_perm})
+        if (p && !aligned16(p)) return MOE_ERR_ALIGN;
+    MOE_TRY(check_ws(cfg, ws, ws_bytes));
+    MOE_TRY(arch_check());
+    const Layout L = layout_of(cfg);
+    const Shape s = shape_of(cfg);
+    return launched(launch_ffn(s, ffn_plan(s), w->w1, w->w1_scale, w->w2, w->w2_scale, x, xq, xq_scale, offsets,
+                               row_to_slot, at<void>(ws, L.h), fp8 ? at<float>(ws, L.hs) : nullptr, y_perm,
+                               at<int32_t>(ws, L.tiles), stream));
+}
+
+moe_status moe_combine(const moe_cfg *cfg, const void *y_perm, const int32_t *slot_to_row, const float *topk_gate,
+                       void *y, hipStream_t stream) {
+    MOE_TRY(validate(cfg));
+    if (cfg->T == 0) return MOE_OK;
+    if (!y_perm || !slot_to_row || !topk_gate || !y) return MOE_ERR_NULL;
+    for (const void *p : {y_perm, (const void *)slot_to_row, (const void *)topk_gate, (const void *)y})
+        if (!aligned16(p)) return MOE_ERR_ALIGN;
+    MOE_TRY(arch_check());
+    return launched(launch_combine(shape_of(cfg), y_perm, slot_to_row, topk_gate, y, stream));
+}
+
+moe_status moe_layer_fused(const moe_cfg *cfg, const moe_weights *w, const void *x, const void *w_router,
+                           const float *bias, void *y, int32_t *topk_idx_out, float *topk_gate_out,
+                           int32_t *counts_out, void *ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(validate(cfg));
+    if (cfg->T == 0) return MOE_OK;
+    const bool fp8 = cfg->mode == MOE_MODE_FP8_MXFP4;
+    if (!w || !w->w1 || !w->w2 || !x || !w_router || !y) return MOE_ERR_NULL;
+    if (fp8 && (!w->w1_scale || !w->w2_scale)) return MOE_ERR_NULL;
+    for (const void *p : {w->w1, w->w2, w->w1_scale, w->w2_scale, x, w_router, (const void *)bias, (const void *)y,
+                          (const void *)topk_idx_out, (const void *)topk_gate_out, (const void *)counts_out})
+        if (p && !aligned16(p)) return MOE_ERR_ALIGN;
+    MOE_TRY(check_ws(cfg, ws, ws_bytes));
+    MOE_TRY(arch_check());
+    const Layout L = layout_of(cfg);
+    const Shape s = shape_of(cfg);
+    int32_t *err = at<int32_t>(ws, L.err);
+    int32_t *idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.idx);
+    float *gate = topk_gate_out ? topk_gate_out : at<float>(ws, L.gate);
+    int32_t *counts = counts_out ? counts_out : at<int32_t>(ws, L.counts);
+    int32_t *offsets = at<int32_t>(ws, L.offsets), *s2r = at<int32_t>(ws, L.s2r), *r2s = at<int32_t>(ws, L.r2s);
+    uint8_t *xq = fp8 ? at<uint8_t>(ws, L.xq) : nullptr;
+    float *xs = fp8 ? at<float>(ws, L.xs) : nullptr;
+    void *yperm = at<void>(ws, L.yperm);
+    hipError_t e = launch_route(s, x, w_router, bias, idx, gate, nullptr, nullptr, err, stream);
+    if (e == hipSuccess)
+        e = launch_dispatch(s, idx, at<int32_t>(ws, L.blockcounts), counts, offsets, s2r, r2s, err, stream);
+    if (e == hipSuccess && fp8) e = launch_quant_x(s, (const uint16_t *)x, xq, xs, stream);
+    if (e == hipSuccess)
+        e = launch_ffn(s, ffn_plan(s), w->w1, w->w1_scale, w->w2, w->w2_scale, x, xq, xs, offsets, r2s,
+                       at<void>(ws, L.h), fp8 ? at<float>(ws, L.hs) : nullptr, yperm, at<int32_t>(ws, L.tiles),
+                       stream);
+    if (e == hipSuccess) e = launch_combine(s, yperm, s2r, gate, y, stream);
+    return launched(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// Launchers for the gfx950 MoE kernels; called by the C ABI in api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct Shape {
+    int T, d, E, k, F, S, gating, mode;
+    int G() const { return E + S; }
+    long rows() const { return (long)T * k + (long)S * T; }
+};
+
+// router: logits, keys, top-k, gates
+hipError_t launch_route(const Shape &s, const void *x, const void *wr, const float *bias, int32_t *idx,
+                        float *gate, float *logits, float *keys, int32_t *err, hipStream_t st);
+
+// dispatch: block histogram, scan, scatter; FP8 activation quantisation
+hipError_t launch_dispatch(const Shape &s, const int32_t *idx, int32_t *blockcounts, int32_t *counts,
+                           int32_t *offsets, int32_t *slot_to_row, int32_t *row_to_slot, int32_t *err,
+                           hipStream_t st);
+hipError_t launch_quant_x(const Shape &s, const uint16_t *x, uint8_t *xq, float *xs, hipStream_t st);
+int dispatch_blocks(int T);
+
+// expert FFN
+struct FfnPlan {
+    int bm1, bn1, bm2, bn2;  // tile shapes of linear1 (N = 2F) and linear2 (N = d)
+};
+FfnPlan ffn_plan(const Shape &s);
+hipError_t launch_ffn(const Shape &s, const FfnPlan &p, const void *w1, const void *w1s, const void *w2,
+                      const void *w2s, const void *x, const uint8_t *xq, const float *xs, const int32_t *offsets,
+                      const int32_t *row_to_slot, void *h, float *hs, void *y_perm, int32_t *tile_start,
+                      hipStream_t st);
+
+// combine
+hipError_t launch_combine(const Shape &s, const void *y_perm, const int32_t *slot_to_row, const float *gate,
+                          void *y, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,257 @@
+// Router GEMM, selection keys, top-k and gates (S1-S4).
+//
+// MoE lesson (factory.pai-world.com, "Mixture of Experts"): "FFN swap" gives the
+// router as one linear layer producing an (N_tokens, E) score matrix and a top-k
+// per token; "Load balancing" and "Build it, Step 1: router" add the per-expert
+// bias to the scores for selection only, order by descending biased score with a
+// stable sort, and take the gates from the unbiased scores (softmax over the
+// chosen ones).  MoE playbook (molayo1419.me, "How it works") gives the same
+// score / select / weighted-sum steps.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int kMaxKeysPerLane = 16;  // E <= 1024 over 64 lanes
+constexpr int kMaxK = 16;
+
+__device__ __forceinline__ float sigmoidf_(float l) { return 1.0f / (1.0f + expf(-l)); }
+
+// One wave selects the top-k of one token whose E logits sit in LDS (lg[0..E)).
+// Keys for expert e live in lane e % 64, slot e / 64.
+__device__ void select_token(const float *lg, int E, int k, int gating, const float *bias, long t, int32_t *idx,
+                             float *gate, float *logits, float *keys, int32_t *err) {
+    const int lane = lane_id();
+    const int nper = (E + kWave - 1) / kWave;
+    float key[kMaxKeysPerLane];
+    uint32_t taken = 0;  // bit i: slot i unavailable
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < kMaxKeysPerLane; ++i) {
+        int e = lane + kWave * i;
+        key[i] = -INFINITY;
+        if (i < nper && e < E) {
+            float l = lg[e];
+            float s = gating == GATE_SIGMOID ? sigmoidf_(l) : l;
+            float kk = s + (bias ? bias[e] : 0.0f);
+            key[i] = kk;
+            bad |= !isfinite(kk);
+            if (logits) logits[t * E + e] = l;
+            if (keys) keys[t * E + e] = kk;
+        } else {
+            taken |= 1u << i;
+        }
+    }
+    if (__any(bad) && lane == 0) set_error(err, DEVERR_NONFINITE);
+
+    int sel[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        sel[j] = 0;
+        if (j < k) {
+            float bk = -INFINITY;
+            int bi = 0x7fffffff;
+#pragma unroll
+            for (int i = 0; i < kMaxKeysPerLane; ++i) {
+                int e = lane + kWave * i;
+                bool ok = !(taken >> i & 1u);
+                if (ok && (key[i] > bk || (key[i] == bk && e < bi))) { bk = key[i]; bi = e; }
+            }
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) {
+                float ok_ = __shfl_xor(bk, m, kWave);
+                int oi = __shfl_xor(bi, m, kWave);
+                if (ok_ > bk || (ok_ == bk && oi < bi)) { bk = ok_; bi = oi; }
+            }
+            if (bi == 0x7fffffff) bi = 0;  // only with non-finite keys (error already flagged)
+            if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+            sel[j] = bi;
+        }
+    }
+
+    // gates from the unbiased scores of the chosen experts
+    float v[kMaxK];
+    float m = -INFINITY, sum = 0.0f;
+    if (gating == GATE_SIGMOID) {
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j)
+            if (j < k) { v[j] = sigmoidf_(lg[sel[j]]); sum += v[j]; }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j)
+            if (j < k) m = fmaxf(m, lg[sel[j]]);
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j)
+            if (j < k) { v[j] = expf(lg[sel[j]] - m); sum += v[j]; }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+        if (j < k && lane == j) {
+            idx[t * k + j] = sel[j];
+            gate[t * k + j] = v[j] / sum;
+        }
+}
+
+// ---- VALU router: one wave per token (small E, or fp32 activations) ----------
+
+template <bool F32, int CH>
+__global__ __launch_bounds__(256) void route_valu_kernel(const void *__restrict__ xv, const void *__restrict__ wv,
+                                                        const float *__restrict__ bias, int T, int d, int E, int k,
+                                                        int gating, int32_t *idx, float *gate, float *logits,
+                                                        float *keys, int32_t *err) {
+    extern __shared__ float lds_logits[];  // [4][E]
+    const int wave = threadIdx.x / kWave, lane = lane_id();
+    const long t = (long)blockIdx.x * 4 + wave;
+    float *lg = lds_logits + wave * E;
+    if (t < T) {
+        constexpr int V = F32 ? 4 : 8;  // elements per 16-byte load
+        for (int e0 = 0; e0 < E; e0 += CH) {
+            float acc[CH];
+#pragma unroll
+            for (int c = 0; c < CH; ++c) acc[c] = 0.0f;
+            for (int i0 = lane * V; i0 < d; i0 += kWave * V) {
+                float xs[V];
+                if (F32) {
+                    float4 q = *(const float4 *)((const float *)xv + t * d + i0);
+                    xs[0] = q.x; xs[1] = q.y; xs[2] = q.z; xs[3] = q.w;
+                } else {
+                    uint4 q = *(const uint4 *)((const uint16_t *)xv + t * d + i0);
+                    const uint16_t *h = (const uint16_t *)&q;
+#pragma unroll
+                    for (int u = 0; u < V; ++u) xs[u] = bf16_to_f32(h[u]);
+                }
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    int e = e0 + c;
+                    if (e < E) {
+                        float ws[V];
+                        if (F32) {
+                            float4 q = *(const float4 *)((const float *)wv + (long)e * d + i0);
+                            ws[0] = q.x; ws[1] = q.y; ws[2] = q.z; ws[3] = q.w;
+                        } else {
+                            uint4 q = *(const uint4 *)((const uint16_t *)wv + (long)e * d + i0);
+                            const uint16_t *h = (const uint16_t *)&q;
+#pragma unroll
+                            for (int u = 0; u < V; ++u) ws[u] = bf16_to_f32(h[u]);
+                        }
+#pragma unroll
+                        for (int u = 0; u < V; ++u) acc[c] = fmaf(xs[u], ws[u], acc[c]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                float s = wave_sum(acc[c]);
+                if (lane == 0 && e0 + c < E) lg[e0 + c] = s;
+            }
+        }
+    }
+    __syncthreads();
+    if (t < T) select_token(lg, E, k, gating, bias, t, idx, gate, logits, keys, err);
+}
+
+// ---- MFMA router (bf16, E a multiple of 32): 32 tokens per workgroup ----------
+//
+// v_mfma_f32_32x32x16_bf16: lane l holds A[row l%32][k 8*(l/32)..+8] and
+// B[k 8*(l/32)..+8][col l%32]; result register r of lane l is
+// C[row 8*(r/4) + 4*(l/32) + r%4][col l%32].  Rows are tokens, columns experts.
+constexpr int kRouteTok = 32;
+constexpr int kRouteMaxNT = 8;  // n-tiles (32 experts) per wave: E <= 1024 over 4 waves
+
+__global__ __launch_bounds__(256) void route_mfma_kernel(const uint16_t *__restrict__ x,
+                                                        const uint16_t *__restrict__ wr,
+                                                        const float *__restrict__ bias, int T, int d, int E, int k,
+                                                        int gating, int32_t *idx, float *gate, float *logits,
+                                                        float *keys, int32_t *err) {
+    extern __shared__ float lds_logits[];  // [32][E]
+    const int wave = threadIdx.x / kWave, lane = lane_id();
+    const int ntile = E / 32;
+    const long t0 = (long)blockIdx.x * kRouteTok;
+    long trow = t0 + (lane & 31);
+    if (trow >= T) trow = T - 1;
+    const uint16_t *xa = x + trow * d + 8 * (lane >> 5);
+    const uint16_t *wb[kRouteMaxNT];
+    f32x16 acc[kRouteMaxNT];
+    int my = 0;
+#pragma unroll
+    for (int i = 0; i < kRouteMaxNT; ++i) {
+        int nt = wave + 4 * i;
+        wb[i] = wr + (long)((nt < ntile ? nt : 0) * 32 + (lane & 31)) * d + 8 * (lane >> 5);
+        acc[i] = (f32x16){};
+        if (nt < ntile) my = i + 1;
+    }
+    if (my > 0) {
+        for (int k0 = 0; k0 < d; k0 += 64) {
+            uint4 av[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) av[u] = *(const uint4 *)(xa + k0 + 16 * u);
+#pragma unroll
+            for (int i = 0; i < kRouteMaxNT; ++i) {
+                if (i < my) {
+                    uint4 bv[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) bv[u] = *(const uint4 *)(wb[i] + k0 + 16 * u);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[u]),
+                                                                         __builtin_bit_cast(bf16x8, bv[u]), acc[i],
+                                                                         0, 0, 0);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kRouteMaxNT; ++i) {
+        int nt = wave + 4 * i;
+        if (nt < ntile) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                int row = 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+                lds_logits[row * E + nt * 32 + (lane & 31)] = acc[i][r];
+            }
+        }
+    }
+    __syncthreads();
+    for (int tr = wave; tr < kRouteTok; tr += 4) {
+        long t = t0 + tr;
+        if (t < T) select_token(lds_logits + tr * E, E, k, gating, bias, t, idx, gate, logits, keys, err);
+    }
+}
+
+hipError_t launch_route(const Shape &s, const void *x, const void *wr, const float *bias, int32_t *idx,
+                        float *gate, float *logits, float *keys, int32_t *err, hipStream_t st) {
+    if (s.T == 0) return hipSuccess;
+    if (s.mode != MODE_F32 && s.E % 32 == 0) {
+        dim3 grid((s.T + kRouteTok - 1) / kRouteTok);
+        size_t lds = (size_t)kRouteTok * s.E * sizeof(float);
+        if (lds > 65536) {
+            hipError_t e = hipFuncSetAttribute((const void *)route_mfma_kernel,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(route_mfma_kernel, grid, dim3(256), lds, st, (const uint16_t *)x, (const uint16_t *)wr,
+                           bias, s.T, s.d, s.E, s.k, s.gating, idx, gate, logits, keys, err);
+    } else {
+        dim3 grid((s.T + 3) / 4);
+        size_t lds = (size_t)4 * s.E * sizeof(float);
+        bool f32 = s.mode == MODE_F32;
+        if (s.E <= 8) {
+            if (f32)
+                hipLaunchKernelGGL((route_valu_kernel<true, 8>), grid, dim3(256), lds, st, x, wr, bias, s.T, s.d,
+                                   s.E, s.k, s.gating, idx, gate, logits, keys, err);
+            else
+                hipLaunchKernelGGL((route_valu_kernel<false, 8>), grid, dim3(256), lds, st, x, wr, bias, s.T, s.d,
+                                   s.E, s.k, s.gating, idx, gate, logits, keys, err);
+        } else {
+            if (f32)
+                hipLaunchKernelGGL((route_valu_kernel<true, 32>), grid, dim3(256), lds, st, x, wr, bias, s.T, s.d,
+                                   s.E, s.k, s.gating, idx, gate, logits, keys, err);
+            else
+                hipLaunchKernelGGL((route_valu_kernel<false, 32>), grid, dim3(256), lds, st, x, wr, bias, s.T,
+                                   s.d, s.E, s.k, s.gating, idx, gate, logits, keys, err);
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

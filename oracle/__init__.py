@@ -73,6 +73,8 @@ def lib():
         L.oracle_layer.restype = I32
         L.oracle_expert_rows.argtypes = [CP, VP, VP, VP, VP, I32, VP, I64, VP, VP]
         L.oracle_expert_rows.restype = None
+        L.oracle_keys_from.argtypes = [CP, VP, VP, VP]
+        L.oracle_keys_from.restype = None
         L.oracle_input_row.argtypes = [CP, VP, I64, VP]
         L.oracle_input_row.restype = None
         _lib = L
@@ -154,6 +156,15 @@ def topk_gates_from(w, logits: np.ndarray, keys: np.ndarray):
     gates = np.empty((T, w.k), dtype=np.float32)
     _check(lib().oracle_topk_gates_from(ctypes.byref(c), _p(logits), _p(keys), _p(idx), _p(gates)))
     return idx, gates
+
+
+def keys_from_logits(w, logits: np.ndarray, bias=None) -> np.ndarray:
+    """Selection keys [T,E] from given fp32 logits (softmax: l + b; sigmoid: sigmoid(l) + b)."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    c = _cfg(w, logits.shape[0])
+    keys = np.empty_like(logits)
+    lib().oracle_keys_from(ctypes.byref(c), _p(logits), _p(bias), _p(keys))
+    return keys
 
 
 def dispatch(w, idx: np.ndarray):

@@ -473,3 +473,8 @@ void oracle_expert_rows(const oracle_cfg *c, const void *w1, const void *w1s, co
     for (int64_t r = 0; r < nrows; ++r)
         oracle_expert_row(c, &w, g, xin + r * c->d, out + r * c->d, h_out ? h_out + r * c->F : NULL);
 }
+
+/* Selection keys for all T tokens from given logits [T,E] (e.g. another implementation's). */
+void oracle_keys_from(const oracle_cfg *c, const float *logits, const float *bias, float *keys) {
+    for (int64_t t = 0; t < c->T; ++t) oracle_keys_token(c, logits + t * c->E, bias, keys + t * c->E);
+}

@@ -1,0 +1,75 @@
+"""The C ABI library loads, exports every symbol include/moe.h declares, and
+validates arguments on the host (no GPU work is started by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_dispatch_amd as moe
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    names = declared()
+    assert len(names) >= 10
+    L = moe.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(moe.EXPORTS)
+
+
+def test_status_strings():
+    L = moe.lib()
+    for s in range(9):
+        assert L.moe_status_str(s).startswith(b"MOE_")
+
+
+def test_workspace_bytes_and_validation():
+    ok = moe.Config(T=64, d=128, E=8, k=2, F=256, mode="f32")
+    assert moe.workspace_bytes(ok) > 0
+    bad = [
+        moe.Config(T=64, d=100, E=8, k=2, F=256),          # d not a multiple of 128
+        moe.Config(T=64, d=128, E=8, k=9, F=256),          # k > E
+        moe.Config(T=64, d=128, E=2000, k=2, F=256),       # E too large
+        moe.Config(T=64, d=128, E=8, k=2, F=200),          # F not a multiple of 128
+        moe.Config(T=64, d=128, E=8, k=2, F=256, n_shared=2),
+        moe.Config(T=-1, d=128, E=8, k=2, F=256),
+        moe.Config(T=64, d=128, E=32, k=17, F=256),        # k > 16
+    ]
+    for c in bad:
+        assert moe.lib().moe_workspace_bytes(ctypes.byref(c.c())) == 0, c
+
+
+def test_host_validation_status_codes():
+    L = moe.lib()
+    c = moe.Config(T=64, d=128, E=8, k=2, F=256, mode="bf16").c()
+    # NULL pointers are rejected before any device work
+    assert L.moe_route(ctypes.byref(c), None, None, None, None, None, None, None, None, 0, None) == 1
+    assert L.moe_combine(ctypes.byref(c), None, None, None, None, None) == 1
+    # a bad shape is reported as such
+    b = moe.Config(T=64, d=100, E=8, k=2, F=256).c()
+    assert L.moe_route(ctypes.byref(b), None, None, None, None, None, None, None, None, 0, None) == 2
+    # unknown mode
+    m = moe.MoeCfg(64, 128, 8, 2, 256, 0, 0, 7, 0, 0)
+    assert L.moe_route(ctypes.byref(m), None, None, None, None, None, None, None, None, 0, None) == 3
+    # misaligned pointers
+    assert L.moe_combine(ctypes.byref(c), ctypes.c_void_p(0x1001), ctypes.c_void_p(0x2000),
+                         ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000), None) == 4
+    # T == 0 is a no-op
+    z = moe.Config(T=0, d=128, E=8, k=2, F=256).c()
+    assert L.moe_route(ctypes.byref(z), None, None, None, None, None, None, None, None, 0, None) == 0
+
+
+def test_workspace_too_small_rejected():
+    L = moe.lib()
+    c = moe.Config(T=64, d=128, E=8, k=2, F=256, mode="bf16").c()
+    p = ctypes.c_void_p(0x10000)
+    assert L.moe_route(ctypes.byref(c), p, p, None, p, p, None, None, p, 16, None) == 5
