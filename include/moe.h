@@ -212,6 +212,22 @@ moe_status moe_layer_fused(const moe_cfg *cfg, const moe_weights *w, const void 
                            const float *bias, void *y, int32_t *topk_idx_out, float *topk_gate_out,
                            int32_t *counts_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Kernel timing for measurement tools (not needed to run the layer).  While
+ * enabled (on != 0), every kernel the library launches is bracketed by two HIP
+ * events recorded on that launch's own stream, so timings include no host gaps.
+ * Returns MOE_OK.
+ */
+moe_status moe_profile_enable(int on);
+
+/*
+ * Synchronises on the recorded events, writes one line "name launches total_ms\n"
+ * per kernel name (in first-launch order) into the host buffer buf (NUL-terminated,
+ * truncated to n bytes), clears the records and returns the full length of the
+ * report in bytes.  buf may be NULL to clear the records only.
+ */
+int moe_profile_report(char *buf, size_t n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -66,7 +66,10 @@ def lib():
         L.moe_ffn.argtypes = [CP, WP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_combine.argtypes = [CP, VP, VP, VP, VP, VP]
         L.moe_layer_fused.argtypes = [CP, WP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
-        for f in ("moe_device_check", "moe_clear_device_error", "moe_read_device_error", "moe_route",
+        L.moe_profile_enable.argtypes = [I32]
+        L.moe_profile_report.argtypes = [ctypes.c_char_p, SZ]
+        L.moe_profile_report.restype = I32
+        for f in ("moe_profile_enable", "moe_device_check", "moe_clear_device_error", "moe_read_device_error", "moe_route",
                   "moe_dispatch", "moe_ffn", "moe_combine", "moe_layer_fused"):
             getattr(L, f).restype = I32
         _lib = L
@@ -74,7 +77,8 @@ def lib():
 
 
 EXPORTS = ("moe_status_str", "moe_device_check", "moe_workspace_bytes", "moe_clear_device_error",
-           "moe_read_device_error", "moe_route", "moe_dispatch", "moe_ffn", "moe_combine", "moe_layer_fused")
+           "moe_read_device_error", "moe_route", "moe_dispatch", "moe_ffn", "moe_combine", "moe_layer_fused",
+           "moe_profile_enable", "moe_profile_report")
 
 
 @dataclass(frozen=True)
@@ -133,6 +137,22 @@ def _expect(t, shape, dtype, name):
 
 def act_dtype(cfg: Config):
     return torch.float32 if cfg.mode == "f32" else torch.bfloat16
+
+
+def profile_enable(on: bool = True):
+    """Bracket every library kernel launch with HIP events on its own stream."""
+    lib().moe_profile_enable(1 if on else 0)
+
+
+def profile_report() -> dict:
+    """{kernel name: (launches, total ms)} since the last report; synchronises."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    lib().moe_profile_report(buf, len(buf))
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, cnt, ms = line.split()
+        out[name] = (int(cnt), float(ms))
+    return out
 
 
 def workspace_bytes(cfg: Config) -> int:

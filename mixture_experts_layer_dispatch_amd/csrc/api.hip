@@ -130,6 +130,13 @@ const char *moe_status_str(moe_status s) {
 
 moe_status moe_device_check(void) { return arch_check(); }
 
+moe_status moe_profile_enable(int on) {
+    g_prof_on.store(on ? 1 : 0);
+    return MOE_OK;
+}
+
+int moe_profile_report(char *buf, size_t n) { return prof_report(buf, n); }
+
 size_t moe_workspace_bytes(const moe_cfg *cfg) {
     if (validate(cfg) != MOE_OK) return 0;
     return layout_of(cfg).total;
@@ -139,7 +146,7 @@ moe_status moe_clear_device_error(const moe_cfg *cfg, void *ws, size_t ws_bytes,
     MOE_TRY(validate(cfg));
     MOE_TRY(check_ws(cfg, ws, ws_bytes));
     MOE_TRY(arch_check());
-    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, stream, at<int32_t>(ws, 0), 64);
+    MOE_LAUNCH("clear_error", zero_words_kernel, dim3(1), dim3(64), 0, stream, at<int32_t>(ws, 0), 64);
     return launched(hipGetLastError());
 }
 

@@ -66,9 +66,9 @@ hipError_t launch_combine(const Shape &s, const void *y_perm, const int32_t *slo
     const long threads = (long)s.T * (s.d / V);
     dim3 grid((unsigned)((threads + 255) / 256));
     if (s.mode == MODE_F32)
-        hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, st, y_perm, slot_to_row, gate, y, s.T, s.k, s.d, s.S);
+        MOE_LAUNCH("combine", combine_kernel<true>, grid, dim3(256), 0, st, y_perm, slot_to_row, gate, y, s.T, s.k, s.d, s.S);
     else
-        hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, st, y_perm, slot_to_row, gate, y, s.T, s.k, s.d, s.S);
+        MOE_LAUNCH("combine", combine_kernel<false>, grid, dim3(256), 0, st, y_perm, slot_to_row, gate, y, s.T, s.k, s.d, s.S);
     return hipGetLastError();
 }
 

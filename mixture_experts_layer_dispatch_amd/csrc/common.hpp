@@ -11,6 +11,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 enum Mode { MODE_F32 = 0, MODE_BF16 = 1, MODE_FP8 = 2 };
 enum Gating { GATE_SOFTMAX = 0, GATE_SIGMOID = 1 };

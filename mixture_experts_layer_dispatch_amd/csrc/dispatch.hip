@@ -120,10 +120,10 @@ hipError_t launch_dispatch(const Shape &s, const int32_t *idx, int32_t *blockcou
     if (s.T == 0) return hipSuccess;
     const int nblk = dispatch_blocks(s.T);
     const size_t lds = (size_t)4 * s.E * sizeof(unsigned long long);
-    hipLaunchKernelGGL(dispatch_count_kernel, dim3(nblk), dim3(256), lds, st, idx, s.T, s.k, s.E, blockcounts, err);
-    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, blockcounts, nblk, s.T, s.k, s.E, s.S,
+    MOE_LAUNCH("dispatch_count", dispatch_count_kernel, dim3(nblk), dim3(256), lds, st, idx, s.T, s.k, s.E, blockcounts, err);
+    MOE_LAUNCH("dispatch_scan", dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, blockcounts, nblk, s.T, s.k, s.E, s.S,
                        counts, offsets);
-    hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(nblk), dim3(256), lds, st, idx, s.T, s.k, s.E,
+    MOE_LAUNCH("dispatch_scatter", dispatch_scatter_kernel, dim3(nblk), dim3(256), lds, st, idx, s.T, s.k, s.E,
                        (const int32_t *)blockcounts, slot_to_row, row_to_slot, err);
     return hipGetLastError();
 }
@@ -161,7 +161,7 @@ hipError_t launch_quant_x(const Shape &s, const uint16_t *x, uint8_t *xq, float 
     const long nblocks = (long)s.T * s.d / 128;
     if (nblocks == 0) return hipSuccess;
     const long threads = nblocks * 16;
-    hipLaunchKernelGGL(quant_x_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, x, nblocks, xq, xs);
+    MOE_LAUNCH("quant_x", quant_x_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, x, nblocks, xq, xs);
     return hipGetLastError();
 }
 

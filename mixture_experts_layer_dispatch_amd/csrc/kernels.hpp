@@ -4,7 +4,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace moe {
+
+// per-kernel timing hooks (prof.hip)
+void prof_begin(hipStream_t st);
+void prof_end(const char *name, hipStream_t st);
+int prof_report(char *buf, size_t n);
+extern std::atomic<int> g_prof_on;
+
+// hipLaunchKernelGGL bracketed by the timing hooks
+#define MOE_LAUNCH(name, kernel, grid, block, lds, stream, ...)                  \
+    do {                                                                        \
+        ::moe::prof_begin(stream);                                              \
+        hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);      \
+        ::moe::prof_end(name, stream);                                          \
+    } while (0)
 
 struct Shape {
     int T, d, E, k, F, S, gating, mode;

@@ -229,7 +229,7 @@ hipError_t launch_route(const Shape &s, const void *x, const void *wr, const flo
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess) return e;
         }
-        hipLaunchKernelGGL(route_mfma_kernel, grid, dim3(256), lds, st, (const uint16_t *)x, (const uint16_t *)wr,
+        MOE_LAUNCH("route", route_mfma_kernel, grid, dim3(256), lds, st, (const uint16_t *)x, (const uint16_t *)wr,
                            bias, s.T, s.d, s.E, s.k, s.gating, idx, gate, logits, keys, err);
     } else {
         dim3 grid((s.T + 3) / 4);
@@ -237,17 +237,17 @@ hipError_t launch_route(const Shape &s, const void *x, const void *wr, const flo
         bool f32 = s.mode == MODE_F32;
         if (s.E <= 8) {
             if (f32)
-                hipLaunchKernelGGL((route_valu_kernel<true, 8>), grid, dim3(256), lds, st, x, wr, bias, s.T, s.d,
+                MOE_LAUNCH("route", (route_valu_kernel<true, 8>), grid, dim3(256), lds, st, x, wr, bias, s.T, s.d,
                                    s.E, s.k, s.gating, idx, gate, logits, keys, err);
             else
-                hipLaunchKernelGGL((route_valu_kernel<false, 8>), grid, dim3(256), lds, st, x, wr, bias, s.T, s.d,
+                MOE_LAUNCH("route", (route_valu_kernel<false, 8>), grid, dim3(256), lds, st, x, wr, bias, s.T, s.d,
                                    s.E, s.k, s.gating, idx, gate, logits, keys, err);
         } else {
             if (f32)
-                hipLaunchKernelGGL((route_valu_kernel<true, 32>), grid, dim3(256), lds, st, x, wr, bias, s.T, s.d,
+                MOE_LAUNCH("route", (route_valu_kernel<true, 32>), grid, dim3(256), lds, st, x, wr, bias, s.T, s.d,
                                    s.E, s.k, s.gating, idx, gate, logits, keys, err);
             else
-                hipLaunchKernelGGL((route_valu_kernel<false, 32>), grid, dim3(256), lds, st, x, wr, bias, s.T,
+                MOE_LAUNCH("route", (route_valu_kernel<false, 32>), grid, dim3(256), lds, st, x, wr, bias, s.T,
                                    s.d, s.E, s.k, s.gating, idx, gate, logits, keys, err);
         }
     }
