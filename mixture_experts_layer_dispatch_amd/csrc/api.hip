@@ -32,7 +32,7 @@ Shape shape_of(const moe_cfg *c) {
 
 // Workspace regions (byte offsets, each aligned to 256).
 struct Layout {
-    size_t err, blockcounts, tiles, h, hs;                           // every path
+    size_t err, blockcounts, tiles, h, hs, rpart, upart;             // every path
     size_t idx, gate, counts, offsets, s2r, r2s, xq, xs, yperm, sync; // fused path
     size_t total;
 };
@@ -53,6 +53,11 @@ Layout layout_of(const moe_cfg *c) {
     L.tiles = take(2 * (G + 1) * 4);
     L.h = take(rows * F * (f32 ? 4 : fp8 ? 1 : 2));
     L.hs = fp8 ? take(rows * (F / 128) * 4) : 0;
+    {
+        const Shape s = Shape{c->T, c->d, c->E, c->k, c->F, c->n_shared, c->gating, c->mode};
+        L.rpart = take((size_t)route_splitk_slices(s) * T * E * 4);
+        L.upart = take(ffn_partial_bytes(s));
+    }
     L.idx = take(T * k * 4);
     L.gate = take(T * k * 4);
     L.counts = take(G * 4);
@@ -172,7 +177,7 @@ moe_status moe_route(const moe_cfg *cfg, const void *x, const void *w_router, co
     MOE_TRY(arch_check());
     const Layout L = layout_of(cfg);
     return launched(launch_route(shape_of(cfg), x, w_router, bias, topk_idx, topk_gate, logits, keys,
-                                 at<int32_t>(ws, L.err), stream));
+                                 at<int32_t>(ws, L.err), at<float>(ws, L.rpart), stream));
 }
 
 moe_status moe_dispatch(const moe_cfg *cfg, const int32_t *topk_idx, const void *x, int32_t *counts,
@@ -215,7 +220,7 @@ moe_status moe_ffn(const moe_cfg *cfg, const moe_weights *w, const void *x, cons
     const Shape s = shape_of(cfg);
     return launched(launch_ffn(s, ffn_plan(s), w->w1, w->w1_scale, w->w2, w->w2_scale, x, xq, xq_scale, offsets,
                                row_to_slot, at<void>(ws, L.h), fp8 ? at<float>(ws, L.hs) : nullptr, y_perm,
-                               at<int32_t>(ws, L.tiles), stream));
+                               at<int32_t>(ws, L.tiles), at<float>(ws, L.upart), stream));
 }
 
 moe_status moe_combine(const moe_cfg *cfg, const void *y_perm, const int32_t *slot_to_row, const float *topk_gate,
@@ -252,14 +257,14 @@ moe_status moe_layer_fused(const moe_cfg *cfg, const moe_weights *w, const void 
     uint8_t *xq = fp8 ? at<uint8_t>(ws, L.xq) : nullptr;
     float *xs = fp8 ? at<float>(ws, L.xs) : nullptr;
     void *yperm = at<void>(ws, L.yperm);
-    hipError_t e = launch_route(s, x, w_router, bias, idx, gate, nullptr, nullptr, err, stream);
+    hipError_t e = launch_route(s, x, w_router, bias, idx, gate, nullptr, nullptr, err, at<float>(ws, L.rpart), stream);
     if (e == hipSuccess)
         e = launch_dispatch(s, idx, at<int32_t>(ws, L.blockcounts), counts, offsets, s2r, r2s, err, stream);
     if (e == hipSuccess && fp8) e = launch_quant_x(s, (const uint16_t *)x, xq, xs, stream);
     if (e == hipSuccess)
         e = launch_ffn(s, ffn_plan(s), w->w1, w->w1_scale, w->w2, w->w2_scale, x, xq, xs, offsets, r2s,
                        at<void>(ws, L.h), fp8 ? at<float>(ws, L.hs) : nullptr, yperm, at<int32_t>(ws, L.tiles),
-                       stream);
+                       at<float>(ws, L.upart), stream);
     if (e == hipSuccess) e = launch_combine(s, yperm, s2r, gate, y, stream);
     return launched(e);
 }

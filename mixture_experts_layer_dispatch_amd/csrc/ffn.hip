@@ -685,10 +685,28 @@ FfnPlan ffn_plan(const Shape &s) {
     FfnPlan p;
     const long rows = s.rows();
     const double per_group = (double)rows / s.G();
+    p.decode = s.mode == MODE_FP8 && per_group <= 48.0;
+    if (p.decode) {
+        // one 64-lane wave per (group, 32-row tile, 32 output columns, K slice)
+        p.ks = rows <= 32 && (s.d / 128) % 4 == 0 ? 4 : 1;
+        p.bm1 = p.bm2 = 32;
+        p.bn1 = p.bn2 = 32;
+        p.ntn1 = (2 * s.F / 32) * p.ks;
+        p.ntn2 = s.d / 32;
+        return p;
+    }
+    p.ks = 1;
     p.bm1 = p.bm2 = per_group >= 160 ? 256 : 128;
     p.bn1 = 256;
     p.bn2 = s.d % 256 == 0 ? 256 : 128;
+    p.ntn1 = s.F / (p.bn1 / 2);
+    p.ntn2 = s.d / p.bn2;
     return p;
+}
+
+size_t ffn_partial_bytes(const Shape &s) {
+    const FfnPlan p = ffn_plan(s);
+    return p.decode ? (size_t)p.ks * s.rows() * 2 * s.F * sizeof(float) : 0;
 }
 
 static int gemm_variant() {
@@ -733,12 +751,12 @@ static hipError_t launch_gemm(const char *name, dim3 grid, const GemmArgs &a, hi
 hipError_t launch_fp8_ffn(const Shape &s, const FfnPlan &p, const uint8_t *w1, const uint8_t *w1s,
                           const uint8_t *w2, const uint8_t *w2s, const uint8_t *xq, const float *xs,
                           const int32_t *offsets, const int32_t *row_to_slot, uint8_t *h, float *hs, void *y_perm,
-                          const int32_t *ts1, const int32_t *ts2, hipStream_t st);
+                          const int32_t *ts1, const int32_t *ts2, float *upart, hipStream_t st);
 
 hipError_t launch_ffn(const Shape &s, const FfnPlan &p, const void *w1, const void *w1s, const void *w2,
                       const void *w2s, const void *x, const uint8_t *xq, const float *xs, const int32_t *offsets,
                       const int32_t *row_to_slot, void *h, float *hs, void *y_perm, int32_t *tile_start,
-                      hipStream_t st) {
+                      float *upart, hipStream_t st) {
     if (s.T == 0) return hipSuccess;
     const long rows = s.rows();
     const int G = s.G();
@@ -751,12 +769,12 @@ hipError_t launch_ffn(const Shape &s, const FfnPlan &p, const void *w1, const vo
         return hipGetLastError();
     }
     int32_t *ts1 = tile_start, *ts2 = tile_start + (G + 1);
-    const int ntn1 = s.F / (p.bn1 / 2), ntn2 = s.d / p.bn2;
+    const int ntn1 = p.ntn1, ntn2 = p.ntn2;
     MOE_LAUNCH("tile_plan", tile_plan_kernel, dim3(1), dim3(1024), 0, st, offsets, G, p.bm1, ntn1, p.bm2, ntn2, ts1, ts2);
     if (s.mode == MODE_FP8)
         return launch_fp8_ffn(s, p, (const uint8_t *)w1, (const uint8_t *)w1s, (const uint8_t *)w2,
                               (const uint8_t *)w2s, xq, xs, offsets, row_to_slot, (uint8_t *)h, hs, y_perm, ts1, ts2,
-                              st);
+                              upart, st);
     auto grid_for = [&](int bm, int ntn) {
         long ub = (rows / bm + G) * (long)ntn;
         return dim3((unsigned)((ub + 7) / 8 * 8));

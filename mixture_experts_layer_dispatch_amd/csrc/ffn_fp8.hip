@@ -376,13 +376,159 @@ static hipError_t launch_fp8(const char *name, dim3 grid, const Fp8Args &a, hipS
     return hipGetLastError();
 }
 
+// ---- decode path: few rows per group ----------------------------------------------------
+//
+// With a handful of rows per expert the layer is weight streaming (HBM bound).  Each
+// 64-lane wave owns one (group, 32-row tile, 32 output columns, K slice) and streams its
+// 32 weight rows straight from HBM into the MFMA operands (no LDS), so thousands of
+// independent waves keep enough loads in flight.  linear1 writes fp32 partial sums per K
+// slice; a second pass adds the slices in order, applies SwiGLU and requantises h to e4m3
+// per 128 columns; linear2 then streams W2 the same way and writes bf16 rows.
+
+constexpr long kDecodeWaves = 256 * 16;  // resident 64-lane waves: 256 CUs x 16
+
+struct DecArgs {
+    const uint8_t *A;            // linear1: xq [T, K] gathered by row; linear2: hq [rows, K]
+    const float *As;             // [*, K/128]
+    const int32_t *row_to_slot;  // linear1 only
+    const int32_t *offsets, *tile_start;
+    const uint8_t *B, *Bs;       // MXFP4 codes [G, N, K/2], e8m0 [G, N, K/32]
+    float *part;                 // linear1: partials [ks][rows][N]
+    uint16_t *Y;                 // linear2: y_perm [rows, N]
+    long rows;
+    int T, k, K, N, G, ks;
+};
+
+template <bool LIN1>
+__device__ __forceinline__ void fp8_decode_tile(const DecArgs &a, int tile) {
+    int g, lo = 0, hi = a.G - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (a.tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+    const int rb = a.offsets[g], cnt = a.offsets[g + 1] - rb;
+    const int mtiles = (cnt + 31) / 32, local = tile - a.tile_start[g];
+    const int mt = local % mtiles, rest = local / mtiles;
+    const int nt = LIN1 ? rest / a.ks : rest, ksl = LIN1 ? rest % a.ks : 0;
+    const int row0 = rb + mt * 32, nrows = min(32, cnt - mt * 32);
+
+    const int lane = lane_id(), kh = lane >> 5;
+    const int r = lane & 31;
+    const long grow = row0 + (r < nrows ? r : 0);
+    const long src = LIN1 ? row_token8(grow, a.row_to_slot, a.T, a.k) : grow;
+    const int KB = a.K / 128;
+    const uint8_t *pa = a.A + src * a.K;
+    const float *psa = a.As + src * KB;
+    const long n = (long)nt * 32 + r;
+    const uint8_t *pb = a.B + ((long)g * a.N + n) * (a.K / 2);
+    const uint8_t *psb = a.Bs + ((long)g * a.N + n) * (a.K / 32);
+    const int kc = a.K / a.ks, kbeg = ksl * kc;
+
+    f32x16 acc = (f32x16){};
+    const int kend = kbeg + kc;  // kc is a multiple of 64
+#define DEC_STEPS(U, k0)                                                                               \
+    do {                                                                                               \
+        i32x4 alo[U], ahi[U], bq[U];                                                                   \
+        int sa[U], sb[U];                                                                              \
+        _Pragma("unroll") for (int u = 0; u < U; ++u) {                                                \
+            const int kk = (k0) + 64 * u;                                                              \
+            /* fp8 A operand: K {16 kh..+15} and {32 + 16 kh..+15} of the 64-wide step */             \
+            alo[u] = *(const i32x4 *)(pa + kk + 16 * kh);                                              \
+            ahi[u] = *(const i32x4 *)(pa + kk + 32 + 16 * kh);                                         \
+            /* fp4 B operand: 32 consecutive K from 32 kh, one e8m0 block */                           \
+            bq[u] = *(const i32x4 *)(pb + (kk + 32 * kh) / 2);                                         \
+            sb[u] = psb[(kk + 32 * kh) / 32];                                                          \
+            sa[u] = (int)((__float_as_uint(psa[kk / 128]) >> 23) & 0xFF);                              \
+        }                                                                                              \
+        _Pragma("unroll") for (int u = 0; u < U; ++u) {                                                \
+            i32x8 av = {alo[u][0], alo[u][1], alo[u][2], alo[u][3], ahi[u][0], ahi[u][1], ahi[u][2], ahi[u][3]}; \
+            i32x8 bv = {bq[u][0], bq[u][1], bq[u][2], bq[u][3], 0, 0, 0, 0};                           \
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 4, 0, sa[u], 0, sb[u]); \
+        }                                                                                              \
+    } while (0)
+    int k0 = kbeg;
+    for (; k0 + 256 <= kend; k0 += 256) DEC_STEPS(4, k0);
+    for (; k0 < kend; k0 += 64) DEC_STEPS(1, k0);
+#undef DEC_STEPS
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int row = 8 * (q >> 2) + 4 * kh + (q & 3);
+        if (row >= nrows) continue;
+        const long orow = row0 + row;
+        if (LIN1) a.part[((long)ksl * a.rows + orow) * a.N + n] = acc[q];
+        else a.Y[orow * a.N + n] = f32_to_bf16(acc[q]);
+    }
+}
+
+// Grid-stride over the tiles: the grid is sized by the device, not by an upper bound of
+// empty tiles (which, with a few hundred mostly empty groups, is mostly launch overhead).
+template <bool LIN1>
+__global__ __launch_bounds__(64) void fp8_decode_kernel(DecArgs a) {
+    const int total = a.tile_start[a.G];
+    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) fp8_decode_tile<LIN1>(a, tile);
+}
+
+// Sums the K slices of linear1 in order, applies SwiGLU and quantises h to e4m3 with one
+// power-of-two scale per 128 columns.  One wave per (row, 128-column block).
+__global__ __launch_bounds__(256) void fp8_decode_swiglu_kernel(const float *__restrict__ part, long rows, int F,
+                                                               int ks, uint8_t *__restrict__ hq,
+                                                               float *__restrict__ hs) {
+    const int lane = lane_id();
+    const long wid = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int nfb = F / 128;
+    if (wid >= rows * nfb) return;
+    const long r = wid / nfb;
+    const int fb = (int)(wid % nfb), f = fb * 128 + 2 * lane;
+    float gsum[2] = {0.0f, 0.0f}, usum[2] = {0.0f, 0.0f};
+    for (int q = 0; q < ks; ++q) {
+        const float *p = part + ((long)q * rows + r) * (2L * F);
+        gsum[0] += p[f]; gsum[1] += p[f + 1];
+        usum[0] += p[F + f]; usum[1] += p[F + f + 1];
+    }
+    float h[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) h[i] = gsum[i] / (1.0f + __expf(-gsum[i])) * usum[i];
+    float amax = fmaxf(fabsf(h[0]), fabsf(h[1]));
+    amax = wave_max(amax);
+    const int e = e4m3_block_exponent(amax);
+    const float inv = ldexpf(1.0f, -e);
+    const uint32_t c = cvt_e4m3x2(h[0] * inv, h[1] * inv);
+    *(uint16_t *)(hq + r * F + f) = (uint16_t)c;
+    if (lane == 0) hs[r * nfb + fb] = ldexpf(1.0f, e);
+}
+
+static hipError_t launch_fp8_decode(const Shape &s, const FfnPlan &p, const uint8_t *w1, const uint8_t *w1s,
+                                    const uint8_t *w2, const uint8_t *w2s, const uint8_t *xq, const float *xs,
+                                    const int32_t *offsets, const int32_t *row_to_slot, uint8_t *h, float *hs,
+                                    void *y_perm, const int32_t *ts1, const int32_t *ts2, float *upart,
+                                    hipStream_t st) {
+    const long rows = s.rows();
+    const int G = s.G();
+    auto grid_for = [&](int ntn) {
+        long ub = (rows / 32 + G) * (long)ntn;
+        return dim3((unsigned)(ub < kDecodeWaves ? ub : kDecodeWaves));
+    };
+    DecArgs a1 = {xq, xs, row_to_slot, offsets, ts1, w1, w1s, upart, nullptr, rows, s.T, s.k, s.d, 2 * s.F, G, p.ks};
+    MOE_LAUNCH("linear1", fp8_decode_kernel<true>, grid_for(p.ntn1), dim3(64), 0, st, a1);
+    const long waves = rows * (s.F / 128);
+    MOE_LAUNCH("swiglu_quant", fp8_decode_swiglu_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st,
+               (const float *)upart, rows, s.F, p.ks, h, hs);
+    DecArgs a2 = {h, hs, nullptr, offsets, ts2, w2, w2s, nullptr, (uint16_t *)y_perm, rows, s.T, s.k, s.F, s.d, G, 1};
+    MOE_LAUNCH("linear2", fp8_decode_kernel<false>, grid_for(p.ntn2), dim3(64), 0, st, a2);
+    return hipGetLastError();
+}
+
 hipError_t launch_fp8_ffn(const Shape &s, const FfnPlan &p, const uint8_t *w1, const uint8_t *w1s,
                           const uint8_t *w2, const uint8_t *w2s, const uint8_t *xq, const float *xs,
                           const int32_t *offsets, const int32_t *row_to_slot, uint8_t *h, float *hs, void *y_perm,
-                          const int32_t *ts1, const int32_t *ts2, hipStream_t st) {
+                          const int32_t *ts1, const int32_t *ts2, float *upart, hipStream_t st) {
+    if (p.decode)
+        return launch_fp8_decode(s, p, w1, w1s, w2, w2s, xq, xs, offsets, row_to_slot, h, hs, y_perm, ts1, ts2,
+                                 upart, st);
     const long rows = s.rows();
     const int G = s.G();
-    const int ntn1 = s.F / (p.bn1 / 2), ntn2 = s.d / p.bn2;
+    const int ntn1 = p.ntn1, ntn2 = p.ntn2;
     auto grid_for = [&](int bm, int ntn) {
         long ub = (rows / bm + G) * (long)ntn;
         return dim3((unsigned)((ub + 7) / 8 * 8));

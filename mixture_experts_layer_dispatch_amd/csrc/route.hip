@@ -218,9 +218,88 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const uint16_t *__restr
     }
 }
 
+// ---- split-K router for few tokens: every wave owns 32 tokens x 32 experts x a K slice ----
+//
+// With few tokens the router is a GEMV over W_r; spreading it over (expert tile, K slice,
+// token tile) waves streams W_r once across the whole chip.  Partial logits land in
+// part[ks][t][e] and route_select_kernel sums them in ks order (fixed, so deterministic).
+__global__ __launch_bounds__(64) void route_splitk_kernel(const uint16_t *__restrict__ x,
+                                                         const uint16_t *__restrict__ wr, int T, int d, int E,
+                                                         int kchunk, float *__restrict__ part) {
+    const int lane = lane_id();
+    const int et = blockIdx.x, ks = blockIdx.y, tt = blockIdx.z;
+    long trow = (long)tt * 32 + (lane & 31);
+    const bool tvalid = trow < T;
+    if (!tvalid) trow = T - 1;
+    const int k0 = ks * kchunk;
+    const uint16_t *xa = x + trow * d + k0 + 8 * (lane >> 5);
+    const uint16_t *wb = wr + (long)(et * 32 + (lane & 31)) * d + k0 + 8 * (lane >> 5);
+    f32x16 acc = (f32x16){};
+    for (int kk = 0; kk < kchunk; kk += 64) {
+        u32x4 av[4], bv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            av[u] = *(const u32x4 *)(xa + kk + 16 * u);
+            bv[u] = *(const u32x4 *)(wb + kk + 16 * u);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[u]),
+                                                          __builtin_bit_cast(bf16x8, bv[u]), acc, 0, 0, 0);
+    }
+    // acc[r] = logit partial of token 8(r/4) + 4(lane/32) + r%4 of the tile, expert lane%32
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        long t = (long)tt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (t < T) part[((long)ks * T + t) * E + et * 32 + (lane & 31)] = acc[r];
+    }
+}
+
+// One workgroup per token: thread e sums expert e's K slices in slice order (its loads are
+// independent, so they are all in flight together), then wave 0 selects.
+__global__ __launch_bounds__(256) void route_select_kernel(const float *__restrict__ part, int nks, int T, int E,
+                                                          int k, int gating, const float *__restrict__ bias,
+                                                          int32_t *idx, float *gate, float *logits, float *keys,
+                                                          int32_t *err) {
+    extern __shared__ float lg[];  // [E]
+    const long t = blockIdx.x;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        float v[64];
+#pragma unroll
+        for (int q = 0; q < 64; ++q)
+            if (q < nks) v[q] = part[((long)q * T + t) * E + e];
+        float s = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 64; ++q)
+            if (q < nks) s += v[q];
+        lg[e] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) select_token(lg, E, k, gating, bias, t, idx, gate, logits, keys, err);
+}
+
+// Router work layout: the split-K path is used for few tokens (bf16, E a multiple of 32).
+int route_splitk_slices(const Shape &s) {
+    if (s.mode == MODE_F32 || s.E % 32 != 0 || s.T > kRouteSplitMaxT || s.T == 0) return 0;
+    const int tiles = (s.E / 32) * ((s.T + 31) / 32);
+    int best = 1;
+    for (int q = 1; q <= 64; ++q)  // slices of K: a multiple of 64 each, ~512 waves in all
+        if (s.d % (64 * q) == 0 && tiles * q <= 512) best = q;
+    return best;
+}
+
 hipError_t launch_route(const Shape &s, const void *x, const void *wr, const float *bias, int32_t *idx,
-                        float *gate, float *logits, float *keys, int32_t *err, hipStream_t st) {
+                        float *gate, float *logits, float *keys, int32_t *err, float *part, hipStream_t st) {
     if (s.T == 0) return hipSuccess;
+    const int nks = part ? route_splitk_slices(s) : 0;
+    if (nks > 0) {
+        dim3 grid(s.E / 32, nks, (s.T + 31) / 32);
+        MOE_LAUNCH("route", route_splitk_kernel, grid, dim3(64), 0, st, (const uint16_t *)x, (const uint16_t *)wr,
+                   s.T, s.d, s.E, s.d / nks, part);
+        MOE_LAUNCH("route_select", route_select_kernel, dim3(s.T), dim3(256), (size_t)s.E * sizeof(float),
+                   st, (const float *)part, nks, s.T, s.E, s.k, s.gating, bias, idx, gate, logits, keys, err);
+        return hipGetLastError();
+    }
     if (s.mode != MODE_F32 && s.E % 32 == 0) {
         dim3 grid((s.T + kRouteTok - 1) / kRouteTok);
         size_t lds = (size_t)kRouteTok * s.E * sizeof(float);
