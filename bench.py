@@ -137,11 +137,11 @@ def main():
     log(f"inputs resident in HBM ({time.time() - t0:.1f}s)")
 
     flush_mb = args.flush_mb if args.flush_mb is not None else (512 if w.T <= 64 else 0)
-    flush_buf = torch.ones(flush_mb * (1 << 18), dtype=torch.int32, device="cuda") if flush_mb else None
+    flush_buf = torch.ones(flush_mb * (1 << 18), dtype=torch.float32, device="cuda") if flush_mb else None
 
     def flush():
         # a read-only sweep: evicts cached weights without leaving dirty lines to write back
-        flush_buf.sum()
+        flush_buf.amax()  # fp32 max: one read pass, no widening copy
 
     def step_fused():
         moe.layer_fused(cfg, x, wr, w1, w2, w1s, w2s, bias, ws=ws, y=y, topk_idx=idx, topk_gate=gate,

@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["api.hip", "route.hip", "dispatch.hip", "ffn.hip", "ffn_fp8.hip", "combine.hip", "prof.hip"]
+SOURCES = ["api.hip", "route.hip", "dispatch.hip", "ffn.hip", "ffn_fp8.hip", "combine.hip", "prof.hip", "fused.hip",
+           "fused_bf16.hip", "fused_fp8.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -33,7 +33,7 @@ Shape shape_of(const moe_cfg *c) {
 // Workspace regions (byte offsets, each aligned to 256).
 struct Layout {
     size_t err, blockcounts, tiles, h, hs, rpart, upart;             // every path
-    size_t idx, gate, counts, offsets, s2r, r2s, xq, xs, yperm, sync; // fused path
+    size_t idx, gate, counts, offsets, s2r, r2s, xq, xs, yperm, done1; // fused path
     size_t total;
 };
 
@@ -48,7 +48,7 @@ Layout layout_of(const moe_cfg *c) {
     const size_t T = c->T, k = c->k, E = c->E, G = c->E + c->n_shared, d = c->d, F = c->F;
     const size_t rows = T * k + c->n_shared * T;
     const bool fp8 = c->mode == MOE_MODE_FP8_MXFP4, f32 = c->mode == MOE_MODE_F32;
-    L.err = take(256);
+    L.err = take(256);  // error word at 0, persistent-kernel counters at 64 words
     L.blockcounts = take((size_t)dispatch_blocks(c->T) * E * 4);
     L.tiles = take(2 * (G + 1) * 4);
     L.h = take(rows * F * (f32 ? 4 : fp8 ? 1 : 2));
@@ -67,7 +67,10 @@ Layout layout_of(const moe_cfg *c) {
     L.xq = fp8 ? take(T * d) : 0;
     L.xs = fp8 ? take(T * (d / 128) * 4) : 0;
     L.yperm = take(rows * d * (f32 ? 4 : 2));
-    L.sync = take(4096);
+    {
+        const Shape s = Shape{c->T, c->d, c->E, c->k, c->F, c->n_shared, c->gating, c->mode};
+        L.done1 = take((size_t)fused_row_tiles(s, ffn_plan(s)) * 4);
+    }
     L.total = off;
     return L;
 }
@@ -151,6 +154,7 @@ moe_status moe_clear_device_error(const moe_cfg *cfg, void *ws, size_t ws_bytes,
     MOE_TRY(validate(cfg));
     MOE_TRY(check_ws(cfg, ws, ws_bytes));
     MOE_TRY(arch_check());
+    // the error word and the persistent kernel's counters (the first 256 bytes)
     MOE_LAUNCH("clear_error", zero_words_kernel, dim3(1), dim3(64), 0, stream, at<int32_t>(ws, 0), 64);
     return launched(hipGetLastError());
 }
@@ -253,20 +257,35 @@ moe_status moe_layer_fused(const moe_cfg *cfg, const moe_weights *w, const void 
     int32_t *idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.idx);
     float *gate = topk_gate_out ? topk_gate_out : at<float>(ws, L.gate);
     int32_t *counts = counts_out ? counts_out : at<int32_t>(ws, L.counts);
-    int32_t *offsets = at<int32_t>(ws, L.offsets), *s2r = at<int32_t>(ws, L.s2r), *r2s = at<int32_t>(ws, L.r2s);
-    uint8_t *xq = fp8 ? at<uint8_t>(ws, L.xq) : nullptr;
-    float *xs = fp8 ? at<float>(ws, L.xs) : nullptr;
-    void *yperm = at<void>(ws, L.yperm);
-    hipError_t e = launch_route(s, x, w_router, bias, idx, gate, nullptr, nullptr, err, at<float>(ws, L.rpart), stream);
-    if (e == hipSuccess)
-        e = launch_dispatch(s, idx, at<int32_t>(ws, L.blockcounts), counts, offsets, s2r, r2s, err, stream);
-    if (e == hipSuccess && fp8) e = launch_quant_x(s, (const uint16_t *)x, xq, xs, stream);
-    if (e == hipSuccess)
-        e = launch_ffn(s, ffn_plan(s), w->w1, w->w1_scale, w->w2, w->w2_scale, x, xq, xs, offsets, r2s,
-                       at<void>(ws, L.h), fp8 ? at<float>(ws, L.hs) : nullptr, yperm, at<int32_t>(ws, L.tiles),
-                       at<float>(ws, L.upart), stream);
-    if (e == hipSuccess) e = launch_combine(s, yperm, s2r, gate, y, stream);
-    return launched(e);
+    FusedArgs a{};
+    a.x = x;
+    a.wr = w_router;
+    a.bias = bias;
+    a.w1 = w->w1;
+    a.w1s = w->w1_scale;
+    a.w2 = w->w2;
+    a.w2s = w->w2_scale;
+    a.y = y;
+    a.idx = idx;
+    a.gate = gate;
+    a.counts = counts;
+    a.err = err;
+    a.sync = err + 16;  // counters: words 16 .. 16 + SYNC_WORDS of the first 256 bytes
+    a.done1 = at<int32_t>(ws, L.done1);
+    a.blockcounts = at<int32_t>(ws, L.blockcounts);
+    a.offsets = at<int32_t>(ws, L.offsets);
+    a.s2r = at<int32_t>(ws, L.s2r);
+    a.r2s = at<int32_t>(ws, L.r2s);
+    a.ts1 = at<int32_t>(ws, L.tiles);
+    a.ts2 = a.ts1 + (s.G() + 1);
+    a.xq = fp8 ? at<uint8_t>(ws, L.xq) : nullptr;
+    a.xs = fp8 ? at<float>(ws, L.xs) : nullptr;
+    a.h = at<void>(ws, L.h);
+    a.hs = fp8 ? at<float>(ws, L.hs) : nullptr;
+    a.yperm = at<void>(ws, L.yperm);
+    a.rpart = at<float>(ws, L.rpart);
+    a.upart = at<float>(ws, L.upart);
+    return launched(launch_layer_fused(s, ffn_plan(s), a, cfg->cu_limit, stream));
 }
 
 }  // extern "C"

@@ -1,11 +1,5 @@
-// Gate-weighted combine (S10).
-//
-// MoE playbook (molayo1419.me, "How it works", combine step) and MoE lesson
-// (factory.pai-world.com, "Mixture of Experts", "FFN swap"): the layer output is
-// the gate-weighted sum of the chosen experts' outputs; the lesson's "Shared
-// expert" section adds the always-on shared expert.  The sum is taken in fp32 in a
-// fixed order -- routed experts in selection order, then the shared expert -- so
-// results are bitwise reproducible, then rounded once to the output dtype.
+// Combine kernel (S10) and its launcher; the work item lives in combine_dev.hpp.
+#include "combine_dev.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -15,48 +9,7 @@ template <bool F32>
 __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ yp, const int32_t *__restrict__ s2r,
                                                      const float *__restrict__ gate, void *__restrict__ y, int T,
                                                      int k, int d, int S) {
-    constexpr int V = F32 ? 4 : 8;  // elements per 16-byte access
-    const int per = d / V;
-    const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    const long t = gid / per;
-    if (t >= T) return;
-    const int c = (int)(gid % per) * V;
-    const long tk = (long)T * k;
-    float acc[V];
-#pragma unroll
-    for (int u = 0; u < V; ++u) acc[u] = 0.0f;
-    auto add_row = [&](long r, float g, bool scale) {
-        if (F32) {
-            float4 q = *(const float4 *)((const float *)yp + r * d + c);
-            float v[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) acc[u] = scale ? acc[u] + g * v[u] : acc[u] + v[u];
-        } else {
-            uint4 q = *(const uint4 *)((const uint16_t *)yp + r * d + c);
-            const uint16_t *h = (const uint16_t *)&q;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                float v = bf16_to_f32(h[u]);
-                acc[u] = scale ? acc[u] + g * v : acc[u] + v;
-            }
-        }
-    };
-    for (int j = 0; j < k; ++j) {
-        long r = s2r[t * k + j];
-        r = r < 0 ? 0 : (r >= tk ? tk - 1 : r);
-        add_row(r, gate[t * k + j], true);
-    }
-    if (S) add_row(tk + t, 1.0f, false);
-    if (F32) {
-        *(float4 *)((float *)y + t * d + c) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    } else {
-        uint4 o;
-        o.x = pack_bf16x2(acc[0], acc[1]);
-        o.y = pack_bf16x2(acc[2], acc[3]);
-        o.z = pack_bf16x2(acc[4], acc[5]);
-        o.w = pack_bf16x2(acc[6], acc[7]);
-        *(uint4 *)((uint16_t *)y + t * d + c) = o;
-    }
+    combine_lane<F32>(yp, s2r, gate, y, T, k, d, S, (long)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 hipError_t launch_combine(const Shape &s, const void *y_perm, const int32_t *slot_to_row, const float *gate,
@@ -66,9 +19,11 @@ hipError_t launch_combine(const Shape &s, const void *y_perm, const int32_t *slo
     const long threads = (long)s.T * (s.d / V);
     dim3 grid((unsigned)((threads + 255) / 256));
     if (s.mode == MODE_F32)
-        MOE_LAUNCH("combine", combine_kernel<true>, grid, dim3(256), 0, st, y_perm, slot_to_row, gate, y, s.T, s.k, s.d, s.S);
+        MOE_LAUNCH("combine", combine_kernel<true>, grid, dim3(256), 0, st, y_perm, slot_to_row, gate, y, s.T, s.k,
+                   s.d, s.S);
     else
-        MOE_LAUNCH("combine", combine_kernel<false>, grid, dim3(256), 0, st, y_perm, slot_to_row, gate, y, s.T, s.k, s.d, s.S);
+        MOE_LAUNCH("combine", combine_kernel<false>, grid, dim3(256), 0, st, y_perm, slot_to_row, gate, y, s.T, s.k,
+                   s.d, s.S);
     return hipGetLastError();
 }
 

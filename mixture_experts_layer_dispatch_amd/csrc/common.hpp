@@ -88,11 +88,96 @@ __device__ __forceinline__ uint32_t cvt_e4m3x4(float a, float b, float c, float 
     return (uint32_t)w;
 }
 
-// Map a linear workgroup id so that ids landing on one XCD (ids are dealt to the
-// 8 XCDs round-robin) become a contiguous range.  n must be a multiple of 8.
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
-    if (n % 8) return bid;
-    return (bid % 8) * (n / 8) + bid / 8;
+// ---- LDS DMA, counted waits and LDS swizzles (shared by the GEMM tiles) ----------
+
+// global_load_lds_dwordx4 / _dword (gfx950): lane L's bytes land in LDS at (M0 base +
+// size * L), with no staging registers.
+__device__ __forceinline__ void lds_dma16(const void *g, uint8_t *lds_block) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                     (__attribute__((address_space(3))) void *)lds_block, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void *g, uint8_t *lds_block) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                     (__attribute__((address_space(3))) void *)lds_block, 4, 0, 0);
+}
+
+// s_waitcnt lgkmcnt(0) with vmcnt and expcnt left at their maxima.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// s_waitcnt vmcnt(n) (n < 64) with expcnt and lgkmcnt left at their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// LDS tile rows of BK bf16 (BK * 2 bytes: 128 or 64) as 16-byte chunks.  Physical chunk
+// = logical chunk XOR a key of the row, chosen so that the 16 lanes of one ds_read_b128
+// phase (rows r..r+15 at one logical chunk) hit 16 distinct 16-byte slots of the
+// 256-byte window of gfx950's 64 LDS banks: (row >> 1) & 7 for 128-byte rows,
+// (row >> 2) & 3 for 64-byte rows.  (Measured: 0 bank-conflict cycles; keyed on the
+// low row bits instead, half of the LDS cycles are conflicts.)
+template <int BK>
+__device__ __forceinline__ int swz_key(int row) {
+    return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+}
+template <int BK>
+__device__ __forceinline__ int swz_off(int row, int chunk) {
+    return row * (BK * 2) + ((chunk ^ swz_key<BK>(row)) << 4);
+}
+
+// Token feeding dispatched row r: routed rows carry slot = t*k + j, the shared
+// expert's rows are T*k + t.  Clamped so that corrupt inputs cannot read outside x.
+__device__ __forceinline__ long row_token(long r, const int32_t *__restrict__ row_to_slot, int T, int k) {
+    long tk = (long)T * k;
+    long t;
+    if (r < tk) {
+        long s = row_to_slot[r];
+        s = s < 0 ? 0 : (s >= tk ? tk - 1 : s);
+        t = s / k;
+    } else {
+        t = r - tk;
+    }
+    return t < 0 ? 0 : (t >= T ? T - 1 : t);
+}
+
+// ---- tiles over ragged expert groups ------------------------------------------------
+//
+// A group g of n_g rows is cut into ceil(n_g / BM) row tiles times the N tiles; ts[g] is
+// the exclusive prefix of tiles per group (ts[G] the total).  Within a group, row tiles
+// vary fastest so that the tiles sharing one weight tile are neighbours.
+
+// Tile of workgroup slot b (of a multiple of 8 slots), or -1.  Slot b runs on XCD b % 8;
+// the tiles are split into 8 contiguous ranges, range x going to the slots of XCD x.
+__device__ __forceinline__ int pick_tile(int b, int total) {
+    const int xcd = b & 7, j = b >> 3;
+    const int per = (total + 7) >> 3;
+    const int t = xcd * per + j;
+    return (j < per && t < total) ? t : -1;
+}
+
+struct TileInfo {
+    int g, row0, nrows, nt, mt;  // group, first row, valid rows, N tile, row tile within the group
+};
+
+__device__ __forceinline__ TileInfo decode_tile(int tile, const int32_t *__restrict__ ts, const int32_t *__restrict__ offsets,
+                                                int G, int BM) {
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (ts[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    TileInfo ti;
+    ti.g = lo;
+    const int rb = offsets[lo], cnt = offsets[lo + 1] - rb;
+    const int mtiles = (cnt + BM - 1) / BM;
+    const int local = tile - ts[lo];
+    const int mt = local % mtiles;
+    ti.mt = mt;
+    ti.nt = local / mtiles;
+    ti.row0 = rb + mt * BM;
+    ti.nrows = min(BM, cnt - mt * BM);
+    return ti;
 }
 
 }  // namespace moe

@@ -1,0 +1,94 @@
+// Host planning of the persistent layer kernel: router kind, item ranges, LDS size, and
+// the launch of the matching instantiation (fp32 here; bf16 and FP8 in their own files).
+#include "dispatch_dev.hpp"
+#include "fused_dev.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+hipError_t launch_fused_bf16(FusedArgs &a, int bm, int bn2, size_t lds, int cu_limit, hipStream_t st);
+hipError_t launch_fused_fp8(FusedArgs &a, bool decode, int bm, int bn2, size_t lds, int cu_limit, hipStream_t st);
+
+namespace {
+
+int router_kind(const Shape &s, int nks) {
+    if (nks > 0) return ROUTER_SPLITK;
+    if (s.mode != MODE_F32 && s.E % 32 == 0) return ROUTER_MFMA;
+    return s.E <= 8 ? ROUTER_VALU8 : ROUTER_VALU32;
+}
+
+size_t router_lds(const Shape &s, int kind) {
+    switch (kind) {
+        case ROUTER_SPLITK: return (size_t)s.E * 4;
+        case ROUTER_MFMA: return (size_t)kRouteTok * s.E * 4;
+        default: return (size_t)4 * s.E * 4;
+    }
+}
+
+size_t gemm_lds(const Shape &s, const FfnPlan &p) {
+    if (s.mode == MODE_F32 || p.decode) return 0;
+    const bool b256 = p.bm1 == 256, n256 = p.bn2 == 256;
+    if (s.mode == MODE_BF16) {
+        const size_t l1 = b256 ? bf16_tile_lds<256, 256>() : bf16_tile_lds<128, 256>();
+        const size_t l2 = b256 ? (n256 ? bf16_tile_lds<256, 256>() : bf16_tile_lds<256, 128>())
+                               : (n256 ? bf16_tile_lds<128, 256>() : bf16_tile_lds<128, 128>());
+        return l1 > l2 ? l1 : l2;
+    }
+    const size_t l1 = b256 ? fp8_tile_lds<256, 256>() : fp8_tile_lds<128, 256>();
+    const size_t l2 = b256 ? (n256 ? fp8_tile_lds<256, 256>() : fp8_tile_lds<256, 128>())
+                           : (n256 ? fp8_tile_lds<128, 256>() : fp8_tile_lds<128, 128>());
+    return l1 > l2 ? l1 : l2;
+}
+
+}  // namespace
+
+int fused_row_tiles(const Shape &s, const FfnPlan &p) {
+    const long rows = s.rows(), G = s.G();
+    return (int)((rows + p.bm1 - 1) / p.bm1 + (G < rows ? G : rows));
+}
+
+size_t fused_lds_bytes(const Shape &s, const FfnPlan &p) {
+    const int kind = router_kind(s, route_splitk_slices(s));
+    size_t b = gemm_lds(s, p);
+    const size_t r = router_lds(s, kind), m = (size_t)4 * s.E * 8, plan = (2 * 1032 + 256) * 4;
+    for (size_t v : {r, m, plan}) b = v > b ? v : b;
+    return b;
+}
+
+hipError_t launch_layer_fused(const Shape &s, const FfnPlan &p, FusedArgs &a, int cu_limit, hipStream_t st) {
+    a.T = s.T; a.d = s.d; a.E = s.E; a.k = s.k; a.F = s.F; a.S = s.S; a.G = s.G(); a.gating = s.gating;
+    a.nks = route_splitk_slices(s);
+    a.router = router_kind(s, a.nks);
+    a.nblk = dispatch_blocks(s.T);
+    a.bm = p.bm1;
+    a.ntn1 = p.ntn1;
+    a.ntn2 = p.ntn2;
+    a.ks = p.ks;
+    a.rows = s.rows();
+    a.nm = fused_row_tiles(s, p);
+    const long lanes_q = s.mode == MODE_FP8 ? (long)s.T * (s.d / 128) * 16 : 0;
+    const long nq = (lanes_q + 1023) / 1024;
+    long nr;
+    switch (a.router) {
+        case ROUTER_SPLITK: nr = (route_splitk_waves(s, a.nks) + 3) / 4; break;
+        case ROUTER_MFMA: nr = (s.T + kRouteTok - 1) / kRouteTok; break;
+        default: nr = (s.T + 3) / 4; break;
+    }
+    const long nsel = a.router == ROUTER_SPLITK ? s.T : 0;
+    a.b_r = nq;
+    a.b_sel = a.b_r + nr;
+    a.b_cnt = a.b_sel + nsel;
+    a.b_plan = a.b_cnt + a.nblk;
+    a.b_end = (a.b_plan + 1 + a.nblk + 7) / 8 * 8;
+    a.n1 = (a.rows * s.F + 255) / 256;
+    a.n2 = (a.rows * s.d + 255) / 256;
+    const int V = s.mode == MODE_F32 ? 4 : 8;
+    const long lanes_c = (long)s.T * (s.d / V);
+    a.ncb = p.decode ? (lanes_c + kWave - 1) / kWave : (lanes_c + 255) / 256;
+    const size_t lds = fused_lds_bytes(s, p);
+    if (s.mode == MODE_F32) return launch_fused_kernel<MODE_F32, 128, 128, false>(a, lds, cu_limit, st);
+    if (s.mode == MODE_BF16) return launch_fused_bf16(a, p.bm1, p.bn2, lds, cu_limit, st);
+    return launch_fused_fp8(a, p.decode, p.bm1, p.bn2, lds, cu_limit, st);
+}
+
+}  // namespace moe

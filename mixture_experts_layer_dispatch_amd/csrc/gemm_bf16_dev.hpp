@@ -1,0 +1,269 @@
+// Expert FFN work items over dispatched rows (S8-S9), bf16 and fp32: linear1 (gate+up)
+// with SwiGLU in the epilogue, then linear2, as grouped GEMMs over ragged expert groups.
+//
+// MoE lesson (factory.pai-world.com, "Mixture of Experts", "FFN swap"): each expert
+// is an independent FFN, usually SwiGLU.  Mega MoE blog (donniechu.com, spec table)
+// and Mega MoE wiki ("One-line definition"): linear1, SwiGLU and linear2 are the
+// middle of the fused chain.  SwiGLU is read as silu(x Wg^T) * (x Wu^T), with
+// W1 = [Wg; Wu] stacked along its output rows.
+//
+// Tiles: a group g of n_g rows is cut into ceil(n_g / BM) row tiles times the N
+// tiles; a planning step writes the exclusive prefix of tiles per group, and each
+// tile finds its (group, row tile, N tile) by binary search.  Within a group, row
+// tiles vary fastest so that the tiles sharing one weight tile are neighbours, and
+// neighbouring tiles are dealt to the same XCD (and its L2).
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+// ---- bf16 grouped GEMM ----------------------------------------------------------
+//
+// C[rows, N] = A[rows, K] * B_g[N, K]^T per group, bf16 inputs, fp32 accumulation on
+// v_mfma_f32_32x32x16_bf16.  256 threads = 2 x 2 waves, each owning a (BM/2) x (BN/2)
+// block of 32x32 MFMA tiles.
+//
+// SWIGLU (linear1): the BN columns of a tile are BN/2 gate rows f0.. of W1 followed
+// by the BN/2 up rows F+f0..; each wave holds matching gate and up accumulators,
+// and the epilogue writes h = silu(gate) * up as bf16 [rows, F].
+// Otherwise (linear2): the epilogue writes C as bf16 [rows, ldc].
+
+struct GemmArgs {
+    const uint16_t *A;           // linear1: x [T, K] (gathered by row); linear2: h [rows, K]
+    const int32_t *row_to_slot;  // linear1 only
+    const uint16_t *B;           // [G, Ntot, K]
+    uint16_t *C;                 // linear1: h [rows, F]; linear2: y_perm [rows, ldc]
+    const int32_t *offsets;      // [G+1]
+    const int32_t *tile_start;   // [G+1]
+    int T, k, K, Ntot, ldc, G, F;
+};
+
+template <int BM, int BN>
+constexpr size_t bf16_tile_lds() { return 4 * (size_t)(BM + BN) * 64; }  // 4 stages of BK = 32
+
+// ---- bf16 grouped GEMM, LDS DMA with a mid-stage barrier -----------------------------
+//
+// BK = 32 (two k16 MFMA steps per stage), NS = 4 LDS stages, DMA issued PD = 3 stages
+// ahead.  Fragments are double-buffered in registers.  The one barrier per stage sits
+// between the two k16 steps and publishes stage kt+1 (every wave has waited for its own
+// DMA of it), so the first fragments of stage kt+1 are read while the second half of
+// stage kt runs on the MFMAs.  Buffer (kt+3) % 4 held stage kt-1, whose last fragments
+// were read before the barrier of iteration kt-1, which every wave has passed when it
+// issues the DMA at the start of iteration kt.
+//
+// The wave is the only one on its SIMD and issues in order, so a burst of LDS reads or
+// DMA instructions would leave the MFMA pipe idle.  Each k16 step is therefore issued
+// as groups {one DMA instruction, one fragment read, TM*TN/(TM+TN) MFMAs}, pinned with
+// scheduling barriers.  The loop body has no branches: past the last stage the DMA
+// re-reads the last stage into the free buffer, which is never read again.
+//
+// One tile per call; lds holds bf16_tile_lds<BM, BN>() bytes.  Every wave has waited for
+// its own DMAs when it returns, but other waves may still read fragments: callers that
+// reuse lds must pass a workgroup barrier first.
+template <int BM, int BN, bool SWIGLU, bool GATHER>
+__device__ __forceinline__ void bf16_tile(const GemmArgs &a, int tile, uint8_t *lds) {
+    constexpr int BK = 32, PD = 3, NS = PD + 1;
+    constexpr int TM = BM / 64, TN = BN / 64;
+    constexpr int CPR = BK / 8, RPI = 64 / CPR;
+    constexpr int IA = BM / (4 * RPI), IB = BN / (4 * RPI);
+    constexpr int PER = IA + IB;
+    constexpr int ROWB = BK * 2;
+    constexpr int STAGE = (BM + BN) * ROWB;
+    static_assert(IA >= 1 && IB >= 1 && (BN / 2) % (RPI * IB) == 0, "tile shape");
+
+    const TileInfo ti = decode_tile(tile, a.tile_start, a.offsets, a.G, BM);
+
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lrow = lane / CPR, lphys = lane % CPR;
+
+    const uint16_t *pa[IA];
+#pragma unroll
+    for (int q = 0; q < IA; ++q) {
+        int r = RPI * (wave * IA + q) + lrow;
+        long grow = ti.row0 + (r < ti.nrows ? r : 0);
+        long src = GATHER ? row_token(grow, a.row_to_slot, a.T, a.k) : grow;
+        pa[q] = a.A + src * a.K + ((lphys ^ swz_key<BK>(r)) * 8);
+    }
+    const int f0 = ti.nt * (BN / 2), n0 = ti.nt * BN;
+    const uint16_t *pb[IB];
+#pragma unroll
+    for (int q = 0; q < IB; ++q) {
+        int r = RPI * (wave * IB + q) + lrow;
+        long wrow = SWIGLU ? (r < BN / 2 ? f0 + r : a.F + f0 + r - BN / 2) : n0 + r;
+        pb[q] = a.B + ((long)ti.g * a.Ntot + wrow) * a.K + ((lphys ^ swz_key<BK>(r)) * 8);
+    }
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){};
+
+    // LDS byte offsets of this lane's fragment rows, for both k16 halves of a stage
+    int aoff[2][TM], boff[2][TN];
+    const int khalf = lane >> 5;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) aoff[h][i] = swz_off<BK>(wm * (BM / 2) + i * 32 + (lane & 31), h * 2 + khalf);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            int base;
+            if (SWIGLU) {
+                constexpr int TNh = TN / 2;
+                base = j < TNh ? wn * (BN / 4) + j * 32 : BN / 2 + wn * (BN / 4) + (j - TNh) * 32;
+            } else {
+                base = wn * (BN / 2) + j * 32;
+            }
+            boff[h][j] = BM * ROWB + swz_off<BK>(base + (lane & 31), h * 2 + khalf);
+        }
+    }
+    const int nk = a.K / BK;
+
+#define MOE_BARRIER()                          \
+    do {                                       \
+        asm volatile("" ::: "memory");         \
+        __builtin_amdgcn_s_barrier();          \
+        asm volatile("" ::: "memory");         \
+    } while (0)
+
+    bf16x8 fr0[TM + TN], fr1[TM + TN];  // A fragments then B fragments
+    // one DMA instruction q (< PER) of stage kt_ into buffer stg
+#define MOE_DMA1(q, stg, kt_)                                                                    \
+    do {                                                                                         \
+        uint8_t *s_ = lds + (stg) * STAGE;                                                       \
+        const int ko_ = (kt_) * BK;                                                              \
+        if ((q) < IA) lds_dma16(pa[(q) < IA ? (q) : 0] + ko_, s_ + (wave * IA + (q)) * 1024);    \
+        else lds_dma16(pb[(q) >= IA ? (q) - IA : 0] + ko_, s_ + BM * ROWB + (wave * IB + (q) - IA) * 1024); \
+    } while (0)
+#define MOE_FRAG1(F, u, stg, h)                                                                  \
+    do {                                                                                         \
+        const uint8_t *s_ = lds + (stg) * STAGE;                                                 \
+        F[u] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(s_ + ((u) < TM ? aoff[h][(u) < TM ? (u) : 0] \
+                                                                  : boff[h][(u) >= TM ? (u) - TM : 0]))); \
+    } while (0)
+#define MOE_MFMA1(F, m)                                                                          \
+    acc[(m) / TN][(m) % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[(m) / TN], F[TM + (m) % TN], \
+                                                                      acc[(m) / TN][(m) % TN], 0, 0, 0)
+
+    constexpr int NF = TM + TN;          // fragments per k16 step
+    constexpr int NM = TM * TN;          // MFMAs per k16 step
+    static_assert(NF == PER, "one DMA and one fragment read per MFMA group");
+
+    // prologue: stages 0 and 1 in flight, stage 0 published, its first fragments read
+#pragma unroll
+    for (int s0 = 0; s0 < PD; ++s0)
+#pragma unroll
+        for (int q = 0; q < PER; ++q) MOE_DMA1(q, s0, s0 < nk ? s0 : nk - 1);
+    wait_vmcnt<(PD - 1) * PER>();
+    MOE_BARRIER();
+#pragma unroll
+    for (int u = 0; u < NF; ++u) MOE_FRAG1(fr0, u, 0, 0);
+
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt % NS, nxt = (kt + 1) % NS, pre = (kt + PD) % NS;
+        const int kpre = kt + PD < nk ? kt + PD : nk - 1;  // past the end: a harmless copy into the free buffer
+        wait_lgkmcnt0();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < NF; ++u) {
+            MOE_DMA1(u, pre, kpre);
+            MOE_FRAG1(fr1, u, cur, 1);
+#pragma unroll
+            for (int m = u * NM / NF; m < (u + 1) * NM / NF; ++m) MOE_MFMA1(fr0, m);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wait_lgkmcnt0();
+        wait_vmcnt<(PD - 1) * PER>();
+        MOE_BARRIER();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < NF; ++u) {
+            MOE_FRAG1(fr0, u, nxt, 0);
+#pragma unroll
+            for (int m = u * NM / NF; m < (u + 1) * NM / NF; ++m) MOE_MFMA1(fr1, m);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    wait_vmcnt<0>();
+#undef MOE_DMA1
+#undef MOE_FRAG1
+#undef MOE_MFMA1
+#undef MOE_BARRIER
+
+    // epilogue
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = wm * (BM / 2) + i * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+            if (row >= ti.nrows) continue;
+            const long grow = ti.row0 + row;
+            if (SWIGLU) {
+                constexpr int TNh = TN / 2;
+#pragma unroll
+                for (int j = 0; j < TNh; ++j) {
+                    float gv = acc[i][j][r], uv = acc[i][j + TNh][r];
+                    float h = gv / (1.0f + __expf(-gv)) * uv;
+                    int f = f0 + wn * (BN / 4) + j * 32 + (lane & 31);
+                    a.C[grow * a.F + f] = f32_to_bf16(h);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    int col = n0 + wn * (BN / 2) + j * 32 + (lane & 31);
+                    a.C[grow * a.ldc + col] = f32_to_bf16(acc[i][j][r]);
+                }
+            }
+        }
+    }
+}
+
+// ---- fp32 path: one lane per output element ------------------------------------
+
+__device__ __forceinline__ int group_of_row(long r, const int32_t *__restrict__ offsets, int G) {
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (offsets[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// linear1 + SwiGLU, one output element h[r, f] per lane; gid = r * F + f
+__device__ __forceinline__ void ffn1_f32_lane(const float *__restrict__ x, const int32_t *__restrict__ r2s,
+                                              const float *__restrict__ w1, const int32_t *__restrict__ offsets,
+                                              int G, int T, int k, int d, int F, long rows, float *__restrict__ h,
+                                              long gid) {
+    if (gid >= rows * F) return;
+    const long r = gid / F;
+    const int f = (int)(gid % F);
+    const int g = group_of_row(r, offsets, G);
+    const long t = row_token(r, r2s, T, k);
+    const float *xr = x + t * d;
+    const float *wg = w1 + ((long)g * 2 * F + f) * d, *wu = w1 + ((long)g * 2 * F + F + f) * d;
+    float ug = 0.0f, uu = 0.0f;
+    for (int i = 0; i < d; ++i) {
+        ug = fmaf(xr[i], wg[i], ug);
+        uu = fmaf(xr[i], wu[i], uu);
+    }
+    h[r * F + f] = ug / (1.0f + expf(-ug)) * uu;
+}
+
+// linear2, one output element y[r, c] per lane; gid = r * d + c
+__device__ __forceinline__ void ffn2_f32_lane(const float *__restrict__ h, const float *__restrict__ w2,
+                                              const int32_t *__restrict__ offsets, int G, int d, int F, long rows,
+                                              float *__restrict__ y, long gid) {
+    if (gid >= rows * d) return;
+    const long r = gid / d;
+    const int c = (int)(gid % d);
+    const int g = group_of_row(r, offsets, G);
+    const float *hr = h + r * F, *wr = w2 + ((long)g * d + c) * F;
+    float s = 0.0f;
+    for (int f = 0; f < F; ++f) s = fmaf(hr[f], wr[f], s);
+    y[r * d + c] = s;
+}
+
+}  // namespace moe

@@ -1,0 +1,433 @@
+// FP8 e4m3 x MXFP4 grouped GEMM work items (S8-S9 in the FP8 x FP4 mode, S12).
+//
+// Mega MoE blog (donniechu.com, spec table) and Mega MoE wiki ("One-line definition"):
+// both expert linears run as FP8 x FP4.  Activations are e4m3 with one power-of-two
+// fp32 scale per 1x128 block along K; weights are MXFP4 (e2m1 pairs per byte, one
+// e8m0 scale per 32 along K).  Because the activation scales are powers of two they
+// are exactly e8m0 values, so v_mfma_scale_f32_32x32x64_f8f6f4 applies both scales in
+// hardware (A: fp8 e4m3, B: fp4 e2m1) and the fp32 accumulators need no per-block
+// promotion step.
+//
+// Tiling follows the bf16 kernel: BM x BN tiles over ragged expert groups, K advancing
+// 128 per stage, stages moved by LDS DMA three buffers deep (two stages in flight), a
+// mid-stage barrier, register double-buffered fragments and an issue order pinned to
+// small {DMA, LDS read, MFMA} groups.  Per stage the DMA moves, for each tile row, 128
+// bytes of A codes, 64 bytes of B codes, the row's fp32 A scale and the 4 e8m0 B scale
+// bytes of this K range.
+//
+// linear1 (SWIGLU): waves are stacked along M (4 x 1), so one wave holds all 128 gate
+// columns and the matching 128 up columns of its rows; the epilogue forms
+// h = silu(gate) * up, takes the row's amax over those 128 columns (one quantisation
+// block of h), and writes e4m3 codes plus the power-of-two scale.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+struct Fp8Args {
+    const uint8_t *A;            // codes: linear1 xq [T, K] (gathered by row); linear2 hq [rows, K]
+    const float *As;             // scales [*, K/128]
+    const int32_t *row_to_slot;  // linear1 only
+    const uint8_t *B;            // MXFP4 codes [G, Ntot, K/2]
+    const uint8_t *Bs;           // e8m0 [G, Ntot, K/32]
+    void *C;                     // linear1: hq codes [rows, F]; linear2: y_perm bf16 [rows, ldc]
+    float *Cs;                   // linear1: h scales [rows, F/128]
+    const int32_t *offsets, *tile_start;
+    int T, k, K, Ntot, ldc, G, F;
+};
+
+// 16-byte-chunk swizzles of 128-byte (A codes) and 64-byte (B codes) LDS rows.
+__device__ __forceinline__ int sw128(int row, int c) { return swz_off<64>(row, c); }
+__device__ __forceinline__ int sw64(int row, int c) { return swz_off<32>(row, c); }
+
+template <int BM, int BN>
+constexpr size_t fp8_tile_lds() { return 3 * ((size_t)BM * 128 + BN * 64 + BM * 4 + BN * 4 + 256); }
+
+// One tile per call; lds holds fp8_tile_lds<BM, BN>() bytes.  Every wave has waited for
+// its own DMAs when it returns, but other waves may still read fragments: callers that
+// reuse lds must pass a workgroup barrier first.
+template <int BM, int BN, int WM, bool SWIGLU, bool GATHER>
+__device__ __forceinline__ void fp8_tile(const Fp8Args &a, int tile, uint8_t *lds) {
+    constexpr int WN = 4 / WM;
+    constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+    constexpr int PD = 2, NS = PD + 1;
+    // DMA instructions per wave per stage: A codes (8 rows x 128 B each), B codes (16 rows
+    // x 64 B each), one dword each for the A and B scales (64 rows per instruction)
+    constexpr int PA = BM / 32, PB = BN / 64;
+    static_assert(BM % 64 == 0 && BN % 64 == 0 && BM <= 256 && BN <= 256, "tile shape");
+    constexpr int OFF_B = BM * 128, OFF_SA = OFF_B + BN * 64, OFF_SB = OFF_SA + BM * 4;
+    constexpr int OFF_SPARE = OFF_SB + BN * 4;  // 256 B sink for the scale DMAs of idle waves
+    constexpr int STAGE = OFF_SPARE + 256;
+    static_assert(!SWIGLU || WN == 1, "the SwiGLU epilogue needs whole 128-column blocks per wave");
+    int g, row0, nrows, nt;
+    {
+        int lo = 0, hi = a.G - 1;
+        while (lo < hi) {
+            int mid = (lo + hi + 1) >> 1;
+            if (a.tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
+        }
+        g = lo;
+        const int rb = a.offsets[g], cnt = a.offsets[g + 1] - rb;
+        const int mtiles = (cnt + BM - 1) / BM, local = tile - a.tile_start[g];
+        const int mt = local % mtiles;
+        nt = local / mtiles;
+        row0 = rb + mt * BM;
+        nrows = min(BM, cnt - mt * BM);
+    }
+
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int wm = WN == 1 ? wave : wave >> 1, wn = WN == 1 ? 0 : wave & 1;
+    const int KB = a.K / 128;  // stages
+
+    // ---- DMA sources ------------------------------------------------------------------
+    // A codes: instruction q (of this wave's PA) fills rows 8 (wave PA + q) + 0..7;
+    // lane L owns row L/8, physical chunk L%8.
+    const uint8_t *pa[PA];
+#pragma unroll
+    for (int q = 0; q < PA; ++q) {
+        int r = 8 * (wave * PA + q) + (lane >> 3);
+        long grow = row0 + (r < nrows ? r : 0);
+        long src = GATHER ? row_token(grow, a.row_to_slot, a.T, a.k) : grow;
+        pa[q] = a.A + src * a.K + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+    }
+    // A scales: wave w < ISA * 4 covers rows 64 w' .. (one dword per lane)
+    const float *psa = nullptr;
+    {
+        int r = 64 * wave + lane;
+        if (r < BM) {
+            long grow = row0 + (r < nrows ? r : 0);
+            long src = GATHER ? row_token(grow, a.row_to_slot, a.T, a.k) : grow;
+            psa = a.As + src * KB;
+        }
+    }
+    // B codes: instruction q fills rows 16 (wave PB + q) + 0..15; lane L owns row L/4, chunk L%4
+    const int f0 = nt * (BN / 2), n0 = nt * BN;
+    auto wrow_of = [&](int r) -> long {
+        return SWIGLU ? (r < BN / 2 ? f0 + r : a.F + f0 + r - BN / 2) : n0 + r;
+    };
+    const uint8_t *pb[PB];
+#pragma unroll
+    for (int q = 0; q < PB; ++q) {
+        int r = 16 * (wave * PB + q) + (lane >> 2);
+        pb[q] = a.B + ((long)g * a.Ntot + wrow_of(r)) * (a.K / 2) + (((lane & 3) ^ ((r >> 2) & 3)) << 4);
+    }
+    const uint8_t *psb = nullptr;
+    {
+        int r = 64 * wave + lane;
+        if (r < BN) psb = a.Bs + ((long)g * a.Ntot + wrow_of(r)) * (a.K / 32);
+    }
+    // Every wave issues exactly PER DMA instructions per stage, so the counted vmcnt waits
+    // hold for all of them: a wave with no scale rows of its own re-loads row 0's scale
+    // into the spare slot.
+    const bool has_sa = 64 * wave < BM, has_sb = 64 * wave < BN;
+    constexpr int PER = PA + PB + 2;
+    if (!has_sa) psa = a.As + (GATHER ? row_token(row0, a.row_to_slot, a.T, a.k) : (long)row0) * KB;
+    if (!has_sb) psb = a.Bs + ((long)g * a.Ntot + wrow_of(0)) * (a.K / 32);
+    const int sa_dst = has_sa ? OFF_SA + wave * 256 : OFF_SPARE;
+    const int sb_dst = has_sb ? OFF_SB + wave * 256 : OFF_SPARE;
+
+    // ---- fragment offsets -------------------------------------------------------------
+    const int khalf = lane >> 5;
+    int aoff[2][TM][2], boff[2][TN], arow[TM], brow[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) arow[i] = wm * (BM / WM) + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        int base;
+        if (SWIGLU) base = j < TN / 2 ? j * 32 : BN / 2 + (j - TN / 2) * 32;
+        else base = wn * (BN / WN) + j * 32;
+        brow[j] = base + (lane & 31);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            // For the fp8 A operand of v_mfma_scale_f32_32x32x64_f8f6f4, lane half kh holds
+            // K {16 kh .. 16 kh + 15} and {32 + 16 kh .. 32 + 16 kh + 15} of the 64-wide step
+            // (while the fp4 B operand holds 32 consecutive K, its e8m0 block): chunks
+            // 4 h + kh and 4 h + 2 + kh of the 128-byte row.  Verified against a CPU model
+            // of the instruction, scales included.
+            aoff[h][i][0] = sw128(arow[i], h * 4 + khalf);
+            aoff[h][i][1] = sw128(arow[i], h * 4 + 2 + khalf);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) boff[h][j] = OFF_B + sw64(brow[j], h * 2 + khalf);
+    }
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){};
+
+#define FP8_DMA(q, stg, kt_)                                                                        \
+    do {                                                                                            \
+        uint8_t *s_ = lds + (stg) * STAGE;                                                          \
+        const int kt2_ = (kt_);                                                                     \
+        if ((q) < PA) lds_dma16(pa[(q) < PA ? (q) : 0] + kt2_ * 128, s_ + (wave * PA + (q)) * 1024);    \
+        else if ((q) < PA + PB)                                                                     \
+            lds_dma16(pb[(q) >= PA && (q) < PA + PB ? (q) - PA : 0] + kt2_ * 64,                        \
+                  s_ + OFF_B + (wave * PB + (q) - PA) * 1024);                                      \
+        else if ((q) == PA + PB)                                                                    \
+            lds_dma4(psa + kt2_, s_ + sa_dst);                                                          \
+        else                                                                                        \
+            lds_dma4(psb + kt2_ * 4, s_ + sb_dst);                                                      \
+    } while (0)
+
+    // fragments: A (two 16-byte reads), B (one read), for k64 step h of a stage
+    i32x4 fa0[TM][2], fb0[TN], fa1[TM][2], fb1[TN];
+    int sa0[TM], sb0[TN];  // e8m0 of the stage (A per row; B dword of 4 blocks per column)
+#define FP8_FRAG(FA, FB, u, stg, h)                                                                 \
+    do {                                                                                            \
+        const uint8_t *s_ = lds + (stg) * STAGE;                                                    \
+        if ((u) < 2 * TM) {                                                                         \
+            const int i_ = (u) >> 1, c_ = (u) & 1;                                                  \
+            FA[i_ < TM ? i_ : 0][c_] = *(const i32x4 *)(s_ + aoff[h][i_ < TM ? i_ : 0][c_]);        \
+        } else {                                                                                    \
+            const int j_ = (u) - 2 * TM;                                                            \
+            FB[j_ < TN ? j_ : 0] = *(const i32x4 *)(s_ + boff[h][j_ < TN ? j_ : 0]);                \
+        }                                                                                           \
+    } while (0)
+#define FP8_SCALES(SA, SB, stg)                                                                     \
+    do {                                                                                            \
+        const uint8_t *s_ = lds + (stg) * STAGE;                                                    \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i)                                              \
+            SA[i] = (int)((*(const uint32_t *)(s_ + OFF_SA + arow[i] * 4) >> 23) & 0xFF);           \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j)                                              \
+            SB[j] = *(const int *)(s_ + OFF_SB + brow[j] * 4);                                      \
+    } while (0)
+#define FP8_MFMA(FA, FB, m, h)                                                                      \
+    do {                                                                                            \
+        const int i_ = (m) / TN, j_ = (m) % TN;                                                     \
+        i32x8 av_ = {FA[i_][0][0], FA[i_][0][1], FA[i_][0][2], FA[i_][0][3],                        \
+                     FA[i_][1][0], FA[i_][1][1], FA[i_][1][2], FA[i_][1][3]};                       \
+        i32x8 bv_ = {FB[j_][0], FB[j_][1], FB[j_][2], FB[j_][3], 0, 0, 0, 0};                       \
+        const int sb_ = (sb0[j_] >> (8 * ((h) * 2 + khalf))) & 0xFF;                                \
+        acc[i_][j_] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av_, bv_, acc[i_][j_], 0, 4, 0, \
+                                                                      sa0[i_], 0, sb_);             \
+    } while (0)
+#define FP8_BARRIER()                          \
+    do {                                       \
+        asm volatile("" ::: "memory");         \
+        __builtin_amdgcn_s_barrier();          \
+        asm volatile("" ::: "memory");         \
+    } while (0)
+
+    constexpr int NR = 2 * TM + TN;  // fragment reads per k64 step
+    constexpr int NM = TM * TN;      // MFMAs per k64 step
+    constexpr int NG = NM;           // issue groups per k64 step (one MFMA each)
+
+    // prologue
+#pragma unroll
+    for (int s0 = 0; s0 < PD; ++s0)
+#pragma unroll
+        for (int q = 0; q < PER; ++q) FP8_DMA(q, s0, s0 < KB ? s0 : KB - 1);
+    wait_vmcnt<(PD - 1) * PER>();
+    FP8_BARRIER();
+#pragma unroll
+    for (int u = 0; u < NR; ++u) FP8_FRAG(fa0, fb0, u, 0, 0);
+    FP8_SCALES(sa0, sb0, 0);
+
+    for (int kt = 0; kt < KB; ++kt) {
+        const int cur = kt % NS, nxt = (kt + 1) % NS, pre = (kt + PD) % NS;
+        const int kpre = kt + PD < KB ? kt + PD : KB - 1;
+        wait_lgkmcnt0();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+            for (int q = gi * PER / NG; q < (gi + 1) * PER / NG; ++q) FP8_DMA(q, pre, kpre);
+#pragma unroll
+            for (int u = gi * NR / NG; u < (gi + 1) * NR / NG; ++u) FP8_FRAG(fa1, fb1, u, cur, 1);
+            FP8_MFMA(fa0, fb0, gi, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wait_lgkmcnt0();
+        wait_vmcnt<(PD - 1) * PER>();
+        FP8_BARRIER();
+        __builtin_amdgcn_sched_barrier(0);
+        int sa1[TM], sb1[TN];
+        FP8_SCALES(sa1, sb1, nxt);
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+            for (int u = gi * NR / NG; u < (gi + 1) * NR / NG; ++u) FP8_FRAG(fa0, fb0, u, nxt, 0);
+            FP8_MFMA(fa1, fb1, gi, 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) sa0[i] = sa1[i];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) sb0[j] = sb1[j];
+    }
+    wait_vmcnt<0>();
+#undef FP8_DMA
+#undef FP8_FRAG
+#undef FP8_SCALES
+#undef FP8_MFMA
+#undef FP8_BARRIER
+
+    // ---- epilogue -----------------------------------------------------------------------
+    if (SWIGLU) {
+        uint8_t *hq = (uint8_t *)a.C;
+        constexpr int TNh = TN / 2;  // 4 column tiles of 32 = the 128-column block
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * (BM / WM) + i * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+                float hv[TNh];
+                float amax = 0.0f;
+#pragma unroll
+                for (int j = 0; j < TNh; ++j) {
+                    float gv = acc[i][j][r], uv = acc[i][j + TNh][r];
+                    hv[j] = gv / (1.0f + __expf(-gv)) * uv;
+                    amax = fmaxf(amax, fabsf(hv[j]));
+                }
+                // the 32 lanes of this half-wave hold the 128 columns of the row
+#pragma unroll
+                for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+                if (row < nrows) {
+                    const int e = e4m3_block_exponent(amax);
+                    const float inv = ldexpf(1.0f, -e);
+                    const long grow = row0 + row;
+#pragma unroll
+                    for (int j = 0; j < TNh; ++j) {
+                        uint32_t c = cvt_e4m3x2(hv[j] * inv, 0.0f) & 0xFFu;
+                        hq[grow * a.F + f0 + j * 32 + (lane & 31)] = (uint8_t)c;
+                    }
+                    if ((lane & 31) == 0) a.Cs[grow * (a.F / 128) + f0 / 128] = ldexpf(1.0f, e);
+                }
+            }
+        }
+    } else {
+        uint16_t *y = (uint16_t *)a.C;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * (BM / WM) + i * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+                if (row >= nrows) continue;
+                const long grow = row0 + row;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    int col = n0 + wn * (BN / WN) + j * 32 + (lane & 31);
+                    y[grow * a.ldc + col] = f32_to_bf16(acc[i][j][r]);
+                }
+            }
+        }
+    }
+}
+
+// ---- decode path: few rows per group ----------------------------------------------------
+//
+// With a handful of rows per expert the layer is weight streaming (HBM bound).  Each
+// 64-lane wave owns one (group, 32-row tile, 32 output columns, K slice) and streams its
+// 32 weight rows straight from HBM into the MFMA operands (no LDS), so thousands of
+// independent waves keep enough loads in flight.  linear1 writes fp32 partial sums per K
+// slice; a second pass adds the slices in order, applies SwiGLU and requantises h to e4m3
+// per 128 columns; linear2 then streams W2 the same way and writes bf16 rows.
+
+struct DecArgs {
+    const uint8_t *A;            // linear1: xq [T, K] gathered by row; linear2: hq [rows, K]
+    const float *As;             // [*, K/128]
+    const int32_t *row_to_slot;  // linear1 only
+    const int32_t *offsets, *tile_start;
+    const uint8_t *B, *Bs;       // MXFP4 codes [G, N, K/2], e8m0 [G, N, K/32]
+    float *part;                 // linear1: partials [ks][rows][N]
+    uint16_t *Y;                 // linear2: y_perm [rows, N]
+    long rows;
+    int T, k, K, N, G, ks;
+};
+
+template <bool LIN1>
+__device__ __forceinline__ void fp8_decode_tile(const DecArgs &a, int tile) {
+    int g, lo = 0, hi = a.G - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (a.tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+    const int rb = a.offsets[g], cnt = a.offsets[g + 1] - rb;
+    const int mtiles = (cnt + 31) / 32, local = tile - a.tile_start[g];
+    const int mt = local % mtiles, rest = local / mtiles;
+    const int nt = LIN1 ? rest / a.ks : rest, ksl = LIN1 ? rest % a.ks : 0;
+    const int row0 = rb + mt * 32, nrows = min(32, cnt - mt * 32);
+
+    const int lane = lane_id(), kh = lane >> 5;
+    const int r = lane & 31;
+    const long grow = row0 + (r < nrows ? r : 0);
+    const long src = LIN1 ? row_token(grow, a.row_to_slot, a.T, a.k) : grow;
+    const int KB = a.K / 128;
+    const uint8_t *pa = a.A + src * a.K;
+    const float *psa = a.As + src * KB;
+    const long n = (long)nt * 32 + r;
+    const uint8_t *pb = a.B + ((long)g * a.N + n) * (a.K / 2);
+    const uint8_t *psb = a.Bs + ((long)g * a.N + n) * (a.K / 32);
+    const int kc = a.K / a.ks, kbeg = ksl * kc;
+
+    f32x16 acc = (f32x16){};
+    const int kend = kbeg + kc;  // kc is a multiple of 64
+#define DEC_STEPS(U, k0)                                                                               \
+    do {                                                                                               \
+        i32x4 alo[U], ahi[U], bq[U];                                                                   \
+        int sa[U], sb[U];                                                                              \
+        _Pragma("unroll") for (int u = 0; u < U; ++u) {                                                \
+            const int kk = (k0) + 64 * u;                                                              \
+            /* fp8 A operand: K {16 kh..+15} and {32 + 16 kh..+15} of the 64-wide step */             \
+            alo[u] = *(const i32x4 *)(pa + kk + 16 * kh);                                              \
+            ahi[u] = *(const i32x4 *)(pa + kk + 32 + 16 * kh);                                         \
+            /* fp4 B operand: 32 consecutive K from 32 kh, one e8m0 block */                           \
+            bq[u] = *(const i32x4 *)(pb + (kk + 32 * kh) / 2);                                         \
+            sb[u] = psb[(kk + 32 * kh) / 32];                                                          \
+            sa[u] = (int)((__float_as_uint(psa[kk / 128]) >> 23) & 0xFF);                              \
+        }                                                                                              \
+        _Pragma("unroll") for (int u = 0; u < U; ++u) {                                                \
+            i32x8 av = {alo[u][0], alo[u][1], alo[u][2], alo[u][3], ahi[u][0], ahi[u][1], ahi[u][2], ahi[u][3]}; \
+            i32x8 bv = {bq[u][0], bq[u][1], bq[u][2], bq[u][3], 0, 0, 0, 0};                           \
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 4, 0, sa[u], 0, sb[u]); \
+        }                                                                                              \
+    } while (0)
+    int k0 = kbeg;
+    for (; k0 + 256 <= kend; k0 += 256) DEC_STEPS(4, k0);
+    for (; k0 < kend; k0 += 64) DEC_STEPS(1, k0);
+#undef DEC_STEPS
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int row = 8 * (q >> 2) + 4 * kh + (q & 3);
+        if (row >= nrows) continue;
+        const long orow = row0 + row;
+        if (LIN1) a.part[((long)ksl * a.rows + orow) * a.N + n] = acc[q];
+        else a.Y[orow * a.N + n] = f32_to_bf16(acc[q]);
+    }
+}
+
+// Sums the K slices of linear1 in order, applies SwiGLU and quantises h to e4m3 with one
+// power-of-two scale per 128 columns.  One wave per (row, 128-column block): wid = row *
+// (F / 128) + block.
+__device__ __forceinline__ void decode_swiglu_wave(const float *__restrict__ part, long rows, int F, int ks,
+                                                  uint8_t *__restrict__ hq, float *__restrict__ hs, long wid) {
+    const int lane = lane_id();
+    const int nfb = F / 128;
+    const long r = wid / nfb;
+    const int fb = (int)(wid % nfb), f = fb * 128 + 2 * lane;
+    float gsum[2] = {0.0f, 0.0f}, usum[2] = {0.0f, 0.0f};
+    for (int q = 0; q < ks; ++q) {
+        const float *p = part + ((long)q * rows + r) * (2L * F);
+        gsum[0] += p[f]; gsum[1] += p[f + 1];
+        usum[0] += p[F + f]; usum[1] += p[F + f + 1];
+    }
+    float h[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) h[i] = gsum[i] / (1.0f + __expf(-gsum[i])) * usum[i];
+    float amax = fmaxf(fabsf(h[0]), fabsf(h[1]));
+    amax = wave_max(amax);
+    const int e = e4m3_block_exponent(amax);
+    const float inv = ldexpf(1.0f, -e);
+    const uint32_t c = cvt_e4m3x2(h[0] * inv, h[1] * inv);
+    *(uint16_t *)(hq + r * F + f) = (uint16_t)c;
+    if (lane == 0) hs[r * nfb + fb] = ldexpf(1.0f, e);
+}
+
+}  // namespace moe

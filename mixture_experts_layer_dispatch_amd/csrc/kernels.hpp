@@ -32,6 +32,7 @@ struct Shape {
 // partial logits (few-token split-K path), or nullptr to always use the one-pass kernels.
 constexpr int kRouteSplitMaxT = 128;
 int route_splitk_slices(const Shape &s);
+long route_splitk_waves(const Shape &s, int nks);
 hipError_t launch_route(const Shape &s, const void *x, const void *wr, const float *bias, int32_t *idx,
                         float *gate, float *logits, float *keys, int32_t *err, float *part, hipStream_t st);
 
@@ -59,5 +60,60 @@ hipError_t launch_ffn(const Shape &s, const FfnPlan &p, const void *w1, const vo
 // combine
 hipError_t launch_combine(const Shape &s, const void *y_perm, const int32_t *slot_to_row, const float *gate,
                           void *y, hipStream_t st);
+
+// ---- persistent layer kernel -------------------------------------------------------
+//
+// One launch runs every step of the layer.  Work items are numbered in step order and
+// dealt round-robin to co-resident workgroups (waves, on the decode path); an item waits
+// only on items with smaller numbers, through counters in the workspace, so every wait
+// ends once the grid is resident.
+
+enum SyncWord {
+    SYNC_QUANT = 0,  // FP8 activation items done
+    SYNC_ROUTE,      // router items done
+    SYNC_SELECT,     // split-K router: tokens selected
+    SYNC_COUNT,      // dispatch histogram blocks done
+    SYNC_PLAN,       // scan and tile plans published
+    SYNC_SCATTER,    // dispatch scatter blocks done
+    SYNC_LIN1,       // linear1 items done (fp32 path)
+    SYNC_LIN2,       // linear2 items done
+    SYNC_EXIT,       // workgroups finished (the last one clears every word)
+    SYNC_WORDS = 16
+};
+
+enum RouterKind { ROUTER_SPLITK = 0, ROUTER_MFMA = 1, ROUTER_VALU8 = 2, ROUTER_VALU32 = 3 };
+
+struct FusedArgs {
+    int T, d, E, k, F, S, G, gating;
+    const void *x, *wr;
+    const float *bias;
+    const void *w1, *w1s, *w2, *w2s;
+    void *y;
+    int32_t *idx;
+    float *gate;
+    int32_t *counts;
+    // workspace
+    int32_t *err, *sync, *done1, *blockcounts, *offsets, *s2r, *r2s, *ts1, *ts2;
+    uint8_t *xq;
+    float *xs;
+    void *h;
+    float *hs;
+    void *yperm;
+    float *rpart, *upart;
+    // plan
+    int router, nks, nblk;
+    int bm, ntn1, ntn2, ks;
+    long rows;
+    int nm;   // row tiles bound (counters in done1)
+    // workgroup item ranges: [0, b_r) quant, [b_r, b_sel) router, [b_sel, b_cnt) select,
+    // [b_cnt, b_plan) histogram, b_plan plan, [b_plan + 1, b_end) scatter, then the GEMMs
+    long b_r, b_sel, b_cnt, b_plan, b_end;
+    long n1, n2;  // fp32 path: linear1 and linear2 items
+    long ncb;     // combine items (workgroups of 256 lanes; waves of 64 on the decode path)
+};
+
+size_t fused_lds_bytes(const Shape &s, const FfnPlan &p);
+int fused_row_tiles(const Shape &s, const FfnPlan &p);  // bound of row tiles (counters needed)
+hipError_t launch_layer_fused(const Shape &s, const FfnPlan &p, FusedArgs &a, int cu_limit, hipStream_t st);
 
 }  // namespace moe

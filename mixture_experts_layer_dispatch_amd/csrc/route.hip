@@ -1,162 +1,19 @@
-// Router GEMM, selection keys, top-k and gates (S1-S4).
-//
-// MoE lesson (factory.pai-world.com, "Mixture of Experts"): "FFN swap" gives the
-// router as one linear layer producing an (N_tokens, E) score matrix and a top-k
-// per token; "Load balancing" and "Build it, Step 1: router" add the per-expert
-// bias to the scores for selection only, order by descending biased score with a
-// stable sort, and take the gates from the unbiased scores (softmax over the
-// chosen ones).  MoE playbook (molayo1419.me, "How it works") gives the same
-// score / select / weighted-sum steps.
+// Router kernels (S1-S4) and their launcher; the work items live in route_dev.hpp.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "route_dev.hpp"
 
 namespace moe {
 
-constexpr int kMaxKeysPerLane = 16;  // E <= 1024 over 64 lanes
-constexpr int kMaxK = 16;
-
-__device__ __forceinline__ float sigmoidf_(float l) { return 1.0f / (1.0f + expf(-l)); }
-
-// One wave selects the top-k of one token whose E logits sit in LDS (lg[0..E)).
-// Keys for expert e live in lane e % 64, slot e / 64.
-__device__ void select_token(const float *lg, int E, int k, int gating, const float *bias, long t, int32_t *idx,
-                             float *gate, float *logits, float *keys, int32_t *err) {
-    const int lane = lane_id();
-    const int nper = (E + kWave - 1) / kWave;
-    float key[kMaxKeysPerLane];
-    uint32_t taken = 0;  // bit i: slot i unavailable
-    bool bad = false;
-#pragma unroll
-    for (int i = 0; i < kMaxKeysPerLane; ++i) {
-        int e = lane + kWave * i;
-        key[i] = -INFINITY;
-        if (i < nper && e < E) {
-            float l = lg[e];
-            float s = gating == GATE_SIGMOID ? sigmoidf_(l) : l;
-            float kk = s + (bias ? bias[e] : 0.0f);
-            key[i] = kk;
-            bad |= !isfinite(kk);
-            if (logits) logits[t * E + e] = l;
-            if (keys) keys[t * E + e] = kk;
-        } else {
-            taken |= 1u << i;
-        }
-    }
-    if (__any(bad) && lane == 0) set_error(err, DEVERR_NONFINITE);
-
-    int sel[kMaxK];
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-        sel[j] = 0;
-        if (j < k) {
-            float bk = -INFINITY;
-            int bi = 0x7fffffff;
-#pragma unroll
-            for (int i = 0; i < kMaxKeysPerLane; ++i) {
-                int e = lane + kWave * i;
-                bool ok = !(taken >> i & 1u);
-                if (ok && (key[i] > bk || (key[i] == bk && e < bi))) { bk = key[i]; bi = e; }
-            }
-#pragma unroll
-            for (int m = 32; m >= 1; m >>= 1) {
-                float ok_ = __shfl_xor(bk, m, kWave);
-                int oi = __shfl_xor(bi, m, kWave);
-                if (ok_ > bk || (ok_ == bk && oi < bi)) { bk = ok_; bi = oi; }
-            }
-            if (bi == 0x7fffffff) bi = 0;  // only with non-finite keys (error already flagged)
-            if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
-            sel[j] = bi;
-        }
-    }
-
-    // gates from the unbiased scores of the chosen experts
-    float v[kMaxK];
-    float m = -INFINITY, sum = 0.0f;
-    if (gating == GATE_SIGMOID) {
-#pragma unroll
-        for (int j = 0; j < kMaxK; ++j)
-            if (j < k) { v[j] = sigmoidf_(lg[sel[j]]); sum += v[j]; }
-    } else {
-#pragma unroll
-        for (int j = 0; j < kMaxK; ++j)
-            if (j < k) m = fmaxf(m, lg[sel[j]]);
-#pragma unroll
-        for (int j = 0; j < kMaxK; ++j)
-            if (j < k) { v[j] = expf(lg[sel[j]] - m); sum += v[j]; }
-    }
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-        if (j < k && lane == j) {
-            idx[t * k + j] = sel[j];
-            gate[t * k + j] = v[j] / sum;
-        }
-}
-
-// ---- VALU router: one wave per token (small E, or fp32 activations) ----------
-
 template <bool F32, int CH>
-__global__ __launch_bounds__(256) void route_valu_kernel(const void *__restrict__ xv, const void *__restrict__ wv,
+__global__ __launch_bounds__(256) void route_valu_kernel(const void *__restrict__ x, const void *__restrict__ wr,
                                                         const float *__restrict__ bias, int T, int d, int E, int k,
                                                         int gating, int32_t *idx, float *gate, float *logits,
                                                         float *keys, int32_t *err) {
     extern __shared__ float lds_logits[];  // [4][E]
-    const int wave = threadIdx.x / kWave, lane = lane_id();
-    const long t = (long)blockIdx.x * 4 + wave;
-    float *lg = lds_logits + wave * E;
-    if (t < T) {
-        constexpr int V = F32 ? 4 : 8;  // elements per 16-byte load
-        for (int e0 = 0; e0 < E; e0 += CH) {
-            float acc[CH];
-#pragma unroll
-            for (int c = 0; c < CH; ++c) acc[c] = 0.0f;
-            for (int i0 = lane * V; i0 < d; i0 += kWave * V) {
-                float xs[V];
-                if (F32) {
-                    float4 q = *(const float4 *)((const float *)xv + t * d + i0);
-                    xs[0] = q.x; xs[1] = q.y; xs[2] = q.z; xs[3] = q.w;
-                } else {
-                    uint4 q = *(const uint4 *)((const uint16_t *)xv + t * d + i0);
-                    const uint16_t *h = (const uint16_t *)&q;
-#pragma unroll
-                    for (int u = 0; u < V; ++u) xs[u] = bf16_to_f32(h[u]);
-                }
-#pragma unroll
-                for (int c = 0; c < CH; ++c) {
-                    int e = e0 + c;
-                    if (e < E) {
-                        float ws[V];
-                        if (F32) {
-                            float4 q = *(const float4 *)((const float *)wv + (long)e * d + i0);
-                            ws[0] = q.x; ws[1] = q.y; ws[2] = q.z; ws[3] = q.w;
-                        } else {
-                            uint4 q = *(const uint4 *)((const uint16_t *)wv + (long)e * d + i0);
-                            const uint16_t *h = (const uint16_t *)&q;
-#pragma unroll
-                            for (int u = 0; u < V; ++u) ws[u] = bf16_to_f32(h[u]);
-                        }
-#pragma unroll
-                        for (int u = 0; u < V; ++u) acc[c] = fmaf(xs[u], ws[u], acc[c]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < CH; ++c) {
-                float s = wave_sum(acc[c]);
-                if (lane == 0 && e0 + c < E) lg[e0 + c] = s;
-            }
-        }
-    }
-    __syncthreads();
-    if (t < T) select_token(lg, E, k, gating, bias, t, idx, gate, logits, keys, err);
+    route_valu_block<F32, CH>(x, wr, bias, T, d, E, k, gating, blockIdx.x, lds_logits, idx, gate, logits, keys,
+                              err);
 }
-
-// ---- MFMA router (bf16, E a multiple of 32): 32 tokens per workgroup ----------
-//
-// v_mfma_f32_32x32x16_bf16: lane l holds A[row l%32][k 8*(l/32)..+8] and
-// B[k 8*(l/32)..+8][col l%32]; result register r of lane l is
-// C[row 8*(r/4) + 4*(l/32) + r%4][col l%32].  Rows are tokens, columns experts.
-constexpr int kRouteTok = 32;
-constexpr int kRouteMaxNT = 8;  // n-tiles (32 experts) per wave: E <= 1024 over 4 waves
 
 __global__ __launch_bounds__(256) void route_mfma_kernel(const uint16_t *__restrict__ x,
                                                         const uint16_t *__restrict__ wr,
@@ -164,118 +21,23 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const uint16_t *__restr
                                                         int gating, int32_t *idx, float *gate, float *logits,
                                                         float *keys, int32_t *err) {
     extern __shared__ float lds_logits[];  // [32][E]
-    const int wave = threadIdx.x / kWave, lane = lane_id();
-    const int ntile = E / 32;
-    const long t0 = (long)blockIdx.x * kRouteTok;
-    long trow = t0 + (lane & 31);
-    if (trow >= T) trow = T - 1;
-    const uint16_t *xa = x + trow * d + 8 * (lane >> 5);
-    const uint16_t *wb[kRouteMaxNT];
-    f32x16 acc[kRouteMaxNT];
-    int my = 0;
-#pragma unroll
-    for (int i = 0; i < kRouteMaxNT; ++i) {
-        int nt = wave + 4 * i;
-        wb[i] = wr + (long)((nt < ntile ? nt : 0) * 32 + (lane & 31)) * d + 8 * (lane >> 5);
-        acc[i] = (f32x16){};
-        if (nt < ntile) my = i + 1;
-    }
-    if (my > 0) {
-        for (int k0 = 0; k0 < d; k0 += 64) {
-            uint4 av[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) av[u] = *(const uint4 *)(xa + k0 + 16 * u);
-#pragma unroll
-            for (int i = 0; i < kRouteMaxNT; ++i) {
-                if (i < my) {
-                    uint4 bv[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) bv[u] = *(const uint4 *)(wb[i] + k0 + 16 * u);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[u]),
-                                                                         __builtin_bit_cast(bf16x8, bv[u]), acc[i],
-                                                                         0, 0, 0);
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < kRouteMaxNT; ++i) {
-        int nt = wave + 4 * i;
-        if (nt < ntile) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                int row = 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-                lds_logits[row * E + nt * 32 + (lane & 31)] = acc[i][r];
-            }
-        }
-    }
-    __syncthreads();
-    for (int tr = wave; tr < kRouteTok; tr += 4) {
-        long t = t0 + tr;
-        if (t < T) select_token(lds_logits + tr * E, E, k, gating, bias, t, idx, gate, logits, keys, err);
-    }
+    route_mfma_block(x, wr, bias, T, d, E, k, gating, blockIdx.x, lds_logits, idx, gate, logits, keys, err);
 }
 
-// ---- split-K router for few tokens: every wave owns 32 tokens x 32 experts x a K slice ----
-//
-// With few tokens the router is a GEMV over W_r; spreading it over (expert tile, K slice,
-// token tile) waves streams W_r once across the whole chip.  Partial logits land in
-// part[ks][t][e] and route_select_kernel sums them in ks order (fixed, so deterministic).
+// one wave per (expert tile, K slice, token tile)
 __global__ __launch_bounds__(64) void route_splitk_kernel(const uint16_t *__restrict__ x,
                                                          const uint16_t *__restrict__ wr, int T, int d, int E,
-                                                         int kchunk, float *__restrict__ part) {
-    const int lane = lane_id();
-    const int et = blockIdx.x, ks = blockIdx.y, tt = blockIdx.z;
-    long trow = (long)tt * 32 + (lane & 31);
-    const bool tvalid = trow < T;
-    if (!tvalid) trow = T - 1;
-    const int k0 = ks * kchunk;
-    const uint16_t *xa = x + trow * d + k0 + 8 * (lane >> 5);
-    const uint16_t *wb = wr + (long)(et * 32 + (lane & 31)) * d + k0 + 8 * (lane >> 5);
-    f32x16 acc = (f32x16){};
-    for (int kk = 0; kk < kchunk; kk += 64) {
-        u32x4 av[4], bv[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            av[u] = *(const u32x4 *)(xa + kk + 16 * u);
-            bv[u] = *(const u32x4 *)(wb + kk + 16 * u);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[u]),
-                                                          __builtin_bit_cast(bf16x8, bv[u]), acc, 0, 0, 0);
-    }
-    // acc[r] = logit partial of token 8(r/4) + 4(lane/32) + r%4 of the tile, expert lane%32
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        long t = (long)tt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (t < T) part[((long)ks * T + t) * E + et * 32 + (lane & 31)] = acc[r];
-    }
+                                                         int nks, float *__restrict__ part) {
+    route_splitk_wave(x, wr, T, d, E, nks, blockIdx.x, part);
 }
 
-// One workgroup per token: thread e sums expert e's K slices in slice order (its loads are
-// independent, so they are all in flight together), then wave 0 selects.
+// one workgroup per token
 __global__ __launch_bounds__(256) void route_select_kernel(const float *__restrict__ part, int nks, int T, int E,
                                                           int k, int gating, const float *__restrict__ bias,
                                                           int32_t *idx, float *gate, float *logits, float *keys,
                                                           int32_t *err) {
     extern __shared__ float lg[];  // [E]
-    const long t = blockIdx.x;
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        float v[64];
-#pragma unroll
-        for (int q = 0; q < 64; ++q)
-            if (q < nks) v[q] = part[((long)q * T + t) * E + e];
-        float s = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 64; ++q)
-            if (q < nks) s += v[q];
-        lg[e] = s;
-    }
-    __syncthreads();
-    if (threadIdx.x < kWave) select_token(lg, E, k, gating, bias, t, idx, gate, logits, keys, err);
+    route_sum_select(part, nks, T, E, k, gating, bias, blockIdx.x, lg, idx, gate, logits, keys, err);
 }
 
 // Router work layout: the split-K path is used for few tokens (bf16, E a multiple of 32).
@@ -288,14 +50,16 @@ int route_splitk_slices(const Shape &s) {
     return best;
 }
 
+long route_splitk_waves(const Shape &s, int nks) { return (long)(s.E / 32) * nks * ((s.T + 31) / 32); }
+
 hipError_t launch_route(const Shape &s, const void *x, const void *wr, const float *bias, int32_t *idx,
                         float *gate, float *logits, float *keys, int32_t *err, float *part, hipStream_t st) {
     if (s.T == 0) return hipSuccess;
     const int nks = part ? route_splitk_slices(s) : 0;
     if (nks > 0) {
-        dim3 grid(s.E / 32, nks, (s.T + 31) / 32);
+        dim3 grid((unsigned)(route_splitk_waves(s, nks)));
         MOE_LAUNCH("route", route_splitk_kernel, grid, dim3(64), 0, st, (const uint16_t *)x, (const uint16_t *)wr,
-                   s.T, s.d, s.E, s.d / nks, part);
+                   s.T, s.d, s.E, nks, part);
         MOE_LAUNCH("route_select", route_select_kernel, dim3(s.T), dim3(256), (size_t)s.E * sizeof(float),
                    st, (const float *)part, nks, s.T, s.E, s.k, s.gating, bias, idx, gate, logits, keys, err);
         return hipGetLastError();

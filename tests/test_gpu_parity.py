@@ -5,6 +5,8 @@ the full-size workloads are checked on routing and dispatch for every token and
 on outputs for a seeded sample of tokens (each token's output depends only on
 its own row and the weights, so a sample is an exact sub-result).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -83,6 +85,24 @@ def test_small_layer_parity(name):
     _, _, r2 = run_unfused(w, d)
     assert torch.equal(r2["y"], r["y"]) and torch.equal(r2["dsp"]["row_to_slot"], r["dsp"]["row_to_slot"])
     log(f"case {name}: rel L2 {err:.2e} (tol {TOL[w.mode]:.0e}), near-tie tokens {near}")
+
+
+@pytest.mark.parametrize("name", ["bf16_sigmoid_shared", "f32_sigmoid_shared", "fp8_softmax_shared", "fp8_decode_5"])
+def test_fused_grid_sizes_and_repeats(name):
+    """The persistent kernel gives the unfused bits on a full grid, on 8 CUs and on 3 CUs
+    (many items per workgroup), and its counters are clean for the next call."""
+    w = SMALL[name]
+    log(f"case {name}: fused at several grid sizes")
+    d = upload(synth.make_inputs(w))
+    cfg, ws, r = run_unfused(w, d)
+    view = torch.int16 if w.mode != "f32" else torch.int32
+    for cu_limit in (0, 8, 3, 0):
+        cfg_l = dataclasses.replace(cfg_of(w), cu_limit=cu_limit)
+        y2, idx2, gate2, _ = run_fused(w, d, cfg_l, ws)
+        assert torch.equal(idx2, r["idx"]) and torch.equal(gate2, r["gate"])
+        assert torch.equal(y2.view(view), r["y"].view(view)), f"fused != unfused at cu_limit {cu_limit}"
+    sync = ws[64:128].view(torch.int32).cpu().numpy()
+    assert not sync.any(), f"counters left set: {sync}"
 
 
 def test_zero_tokens_is_noop():
