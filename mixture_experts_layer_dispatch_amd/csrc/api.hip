@@ -33,7 +33,7 @@ Shape shape_of(const moe_cfg *c) {
 // Workspace regions (byte offsets, each aligned to 256).
 struct Layout {
     size_t err, blockcounts, tiles, h, hs, rpart, upart;             // every path
-    size_t idx, gate, counts, offsets, s2r, r2s, xq, xs, yperm, done1; // fused path
+    size_t idx, gate, counts, offsets, s2r, r2s, xq, xs, yperm, sync, done1;  // fused path
     size_t total;
 };
 
@@ -48,7 +48,7 @@ Layout layout_of(const moe_cfg *c) {
     const size_t T = c->T, k = c->k, E = c->E, G = c->E + c->n_shared, d = c->d, F = c->F;
     const size_t rows = T * k + c->n_shared * T;
     const bool fp8 = c->mode == MOE_MODE_FP8_MXFP4, f32 = c->mode == MOE_MODE_F32;
-    L.err = take(256);  // error word at 0, persistent-kernel counters at 64 words
+    L.err = take(256);  // sticky error word
     L.blockcounts = take((size_t)dispatch_blocks(c->T) * E * 4);
     L.tiles = take(2 * (G + 1) * 4);
     L.h = take(rows * F * (f32 ? 4 : fp8 ? 1 : 2));
@@ -69,7 +69,8 @@ Layout layout_of(const moe_cfg *c) {
     L.yperm = take(rows * d * (f32 ? 4 : 2));
     {
         const Shape s = Shape{c->T, c->d, c->E, c->k, c->F, c->n_shared, c->gating, c->mode};
-        L.done1 = take((size_t)fused_row_tiles(s, ffn_plan(s)) * 4);
+        L.sync = take(kSyncInts * 4);
+        L.done1 = take((size_t)fused_row_tiles(s, ffn_plan(s)) * kRowTileSlots * kSlot * 4);
     }
     L.total = off;
     return L;
@@ -154,8 +155,11 @@ moe_status moe_clear_device_error(const moe_cfg *cfg, void *ws, size_t ws_bytes,
     MOE_TRY(validate(cfg));
     MOE_TRY(check_ws(cfg, ws, ws_bytes));
     MOE_TRY(arch_check());
-    // the error word and the persistent kernel's counters (the first 256 bytes)
-    MOE_LAUNCH("clear_error", zero_words_kernel, dim3(1), dim3(64), 0, stream, at<int32_t>(ws, 0), 64);
+    // the error word and the persistent kernel's synchronisation words
+    const Layout L = layout_of(cfg);
+    MOE_LAUNCH("clear_error", zero_words_kernel, dim3(1), dim3(64), 0, stream, at<int32_t>(ws, L.err), 64);
+    MOE_LAUNCH("clear_error", zero_words_kernel, dim3((unsigned)((kSyncInts + 255) / 256)), dim3(256), 0, stream,
+               at<int32_t>(ws, L.sync), (int)kSyncInts);
     return launched(hipGetLastError());
 }
 
@@ -270,7 +274,7 @@ moe_status moe_layer_fused(const moe_cfg *cfg, const moe_weights *w, const void 
     a.gate = gate;
     a.counts = counts;
     a.err = err;
-    a.sync = err + 16;  // counters: words 16 .. 16 + SYNC_WORDS of the first 256 bytes
+    a.sync = at<int32_t>(ws, L.sync);
     a.done1 = at<int32_t>(ws, L.done1);
     a.blockcounts = at<int32_t>(ws, L.blockcounts);
     a.offsets = at<int32_t>(ws, L.offsets);

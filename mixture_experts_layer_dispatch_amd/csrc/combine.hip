@@ -9,7 +9,7 @@ template <bool F32>
 __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ yp, const int32_t *__restrict__ s2r,
                                                      const float *__restrict__ gate, void *__restrict__ y, int T,
                                                      int k, int d, int S) {
-    combine_lane<F32>(yp, s2r, gate, y, T, k, d, S, (long)blockIdx.x * blockDim.x + threadIdx.x);
+    combine_lane<F32, false>(yp, s2r, gate, y, T, k, d, S, (long)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 hipError_t launch_combine(const Shape &s, const void *y_perm, const int32_t *slot_to_row, const float *gate,

@@ -13,7 +13,7 @@
 namespace moe {
 
 // One lane: 16 bytes of output columns of one token; gid = t * (d / V) + column chunk.
-template <bool F32>
+template <bool F32, bool COH>
 __device__ __forceinline__ void combine_lane(const void *__restrict__ yp, const int32_t *__restrict__ s2r,
                                              const float *__restrict__ gate, void *__restrict__ y, int T, int k,
                                              int d, int S, long gid) {
@@ -27,25 +27,23 @@ __device__ __forceinline__ void combine_lane(const void *__restrict__ yp, const 
 #pragma unroll
     for (int u = 0; u < V; ++u) acc[u] = 0.0f;
     auto add_row = [&](long r, float g, bool scale) {
+        const i32x4 q = ldc16<COH>(yp, (size_t)(r * d + c) * (F32 ? 4 : 2));
         if constexpr (F32) {
-            float4 q = *(const float4 *)((const float *)yp + r * d + c);
-            float v[4] = {q.x, q.y, q.z, q.w};
+            float v[4] = {__int_as_float(q[0]), __int_as_float(q[1]), __int_as_float(q[2]), __int_as_float(q[3])};
 #pragma unroll
             for (int u = 0; u < 4; ++u) acc[u] = scale ? acc[u] + g * v[u] : acc[u] + v[u];
         } else {
-            uint4 q = *(const uint4 *)((const uint16_t *)yp + r * d + c);
-            const uint16_t *h = (const uint16_t *)&q;
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                float v = bf16_to_f32(h[u]);
+                float v = bf16_to_f32((uint16_t)((uint32_t)q[u >> 1] >> (16 * (u & 1))));
                 acc[u] = scale ? acc[u] + g * v : acc[u] + v;
             }
         }
     };
     for (int j = 0; j < k; ++j) {
-        long r = s2r[t * k + j];
+        long r = ldc<COH>(s2r + t * k + j);
         r = r < 0 ? 0 : (r >= tk ? tk - 1 : r);
-        add_row(r, gate[t * k + j], true);
+        add_row(r, ldc<COH>(gate + t * k + j), true);
     }
     if (S) add_row(tk + t, 1.0f, false);
     if constexpr (F32) {

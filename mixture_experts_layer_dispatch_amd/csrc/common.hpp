@@ -126,13 +126,70 @@ __device__ __forceinline__ int swz_off(int row, int chunk) {
     return row * (BK * 2) + ((chunk ^ swz_key<BK>(row)) << 4);
 }
 
+// ---- device-coherent accesses ----------------------------------------------------------
+//
+// Data that one workgroup writes and another reads inside the persistent layer kernel
+// moves through device-scope (sc1) loads and stores: on gfx950 these are coherent across
+// the XCDs' L2 caches, so they need no cache write-back or invalidation (an agent-scope
+// fence costs microseconds per wave and invalidates the whole L2).  The hand-off is then
+// s_waitcnt vmcnt(0) on the producer (its sc1 stores have reached the device coherence
+// point) followed by a relaxed device-scope counter update, and a spin on that counter on
+// the consumer, whose later sc1 loads are issued in order after the spin.  COH = false
+// gives plain accesses: the stand-alone kernels, where launches order everything.
+
+template <bool COH>
+__device__ __forceinline__ int32_t ldc(const int32_t *p) {
+    if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else return *p;
+}
+template <bool COH>
+__device__ __forceinline__ float ldc(const float *p) {
+    if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else return *p;
+}
+template <bool COH>
+__device__ __forceinline__ void stc(int32_t *p, int32_t v) {
+    if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+}
+template <bool COH>
+__device__ __forceinline__ void stc(float *p, float v) {
+    if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+}
+template <bool COH>
+__device__ __forceinline__ void stc(uint64_t *p, uint64_t v) {
+    if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+}
+
+// Raw buffer resource over [base, base + 2 GiB): base must be wave-uniform.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+constexpr int kCpolSc1 = 16;  // cache policy: device scope
+
+// 16 bytes at base + off (the coherent form needs off < 2^31).
+template <bool COH>
+__device__ __forceinline__ i32x4 ldc16(const void *base, size_t off) {
+    if constexpr (COH) return __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(base), (uint32_t)off, 0, kCpolSc1);
+    else return *(const i32x4 *)((const uint8_t *)base + off);
+}
+// 2 bytes at base + 2 i (the coherent form needs 2 i < 2^31).
+template <bool COH>
+__device__ __forceinline__ void stc16(uint16_t *base, size_t i, uint16_t v) {
+    if constexpr (COH) __builtin_amdgcn_raw_buffer_store_b16(v, buffer_rsrc(base), (uint32_t)(2 * i), 0, kCpolSc1);
+    else base[i] = v;
+}
+
 // Token feeding dispatched row r: routed rows carry slot = t*k + j, the shared
 // expert's rows are T*k + t.  Clamped so that corrupt inputs cannot read outside x.
+template <bool COH = false>
 __device__ __forceinline__ long row_token(long r, const int32_t *__restrict__ row_to_slot, int T, int k) {
     long tk = (long)T * k;
     long t;
     if (r < tk) {
-        long s = row_to_slot[r];
+        long s = ldc<COH>(row_to_slot + r);
         s = s < 0 ? 0 : (s >= tk ? tk - 1 : s);
         t = s / k;
     } else {

@@ -10,14 +10,14 @@ int dispatch_blocks(int T) { return (T + kDispTok - 1) / kDispTok; }
 __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t *__restrict__ idx, int T, int k, int E,
                                                             int32_t *__restrict__ blockcounts, int32_t *err) {
     extern __shared__ unsigned long long masks[];  // [4][E]
-    count_block(idx, T, k, E, blockIdx.x, masks, blockcounts, err);
+    count_block<false>(idx, T, k, E, blockIdx.x, masks, blockcounts, err);
 }
 
 __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t *__restrict__ blockcounts, int nblk, int T,
                                                            int E, int S, int32_t *__restrict__ counts,
                                                            int32_t *__restrict__ offsets) {
     __shared__ int32_t sh[1024 + 256];
-    dispatch_scan_block(blockcounts, nblk, T, E, S, counts, offsets, sh);
+    dispatch_scan_block<false>(blockcounts, nblk, T, E, S, counts, offsets, sh);
 }
 
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t *__restrict__ idx, int T, int k, int E,
@@ -25,7 +25,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t *__
                                                               int32_t *__restrict__ slot_to_row,
                                                               int32_t *__restrict__ row_to_slot) {
     extern __shared__ unsigned long long masks[];  // [4][E]
-    scatter_block(idx, T, k, E, blockIdx.x, bases, slot_to_row, row_to_slot, masks);
+    scatter_block<false>(idx, T, k, E, blockIdx.x, bases, slot_to_row, row_to_slot, masks);
 }
 
 hipError_t launch_dispatch(const Shape &s, const int32_t *idx, int32_t *blockcounts, int32_t *counts,
@@ -45,7 +45,7 @@ hipError_t launch_dispatch(const Shape &s, const int32_t *idx, int32_t *blockcou
 
 __global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t *__restrict__ x, long nblocks,
                                                      uint8_t *__restrict__ xq, float *__restrict__ xs) {
-    quant_x_lane(x, nblocks, xq, xs, (long)blockIdx.x * blockDim.x + threadIdx.x);
+    quant_x_lane<false>(x, nblocks, xq, xs, (long)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 hipError_t launch_quant_x(const Shape &s, const uint16_t *x, uint8_t *xq, float *xs, hipStream_t st) {

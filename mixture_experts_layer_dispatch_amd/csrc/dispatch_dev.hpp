@@ -22,10 +22,11 @@ constexpr int kMaxChoices = 16;
 // Token t's k choices, loaded together (clamped, unconditional loads: a load under a
 // branch would be waited for before the branch joins), with a bit per usable choice:
 // in range and not a repeat of an earlier choice of the same token.
+template <bool COH>
 __device__ __forceinline__ uint32_t load_choices(const int32_t *__restrict__ idx, long t, int k, int E,
                                                  int ids[kMaxChoices], bool &bad_index, bool &dup) {
 #pragma unroll
-    for (int j = 0; j < kMaxChoices; ++j) ids[j] = idx[t * k + (j < k ? j : k - 1)];
+    for (int j = 0; j < kMaxChoices; ++j) ids[j] = ldc<COH>(idx + t * k + (j < k ? j : k - 1));
     uint32_t ok = 0;
     bad_index = dup = false;
 #pragma unroll
@@ -46,6 +47,7 @@ __device__ __forceinline__ uint32_t load_choices(const int32_t *__restrict__ idx
 
 // Builds masks[w][e] for dispatch block blk: bit `lane` set when token
 // (blk*256 + w*64 + lane) chose e.  Invalid choices are reported (when err) and skipped.
+template <bool COH>
 __device__ __forceinline__ void build_masks(const int32_t *__restrict__ idx, int T, int k, int E, int blk,
                                             unsigned long long *masks, int32_t *err) {
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
@@ -55,7 +57,7 @@ __device__ __forceinline__ void build_masks(const int32_t *__restrict__ idx, int
     if (t < T) {
         int ids[kMaxChoices];
         bool bad, dup;
-        const uint32_t ok = load_choices(idx, t, k, E, ids, bad, dup);
+        const uint32_t ok = load_choices<COH>(idx, t, k, E, ids, bad, dup);
         if (bad) set_error(err, DEVERR_INDEX);
         if (dup) set_error(err, DEVERR_DUP);
 #pragma unroll
@@ -66,13 +68,14 @@ __device__ __forceinline__ void build_masks(const int32_t *__restrict__ idx, int
 }
 
 // Per-expert histogram of block blk: blockcounts[blk][e].  masks: 4*E words of LDS.
+template <bool COH>
 __device__ __forceinline__ void count_block(const int32_t *__restrict__ idx, int T, int k, int E, int blk,
                                             unsigned long long *masks, int32_t *__restrict__ blockcounts,
                                             int32_t *err) {
-    build_masks(idx, T, k, E, blk, masks, err);
+    build_masks<COH>(idx, T, k, E, blk, masks, err);
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         int c = __popcll(masks[e]) + __popcll(masks[E + e]) + __popcll(masks[2 * E + e]) + __popcll(masks[3 * E + e]);
-        blockcounts[(long)blk * E + e] = c;
+        stc<COH>(blockcounts + (long)blk * E + e, c);
     }
 }
 
@@ -107,6 +110,7 @@ __device__ __forceinline__ int block_exclusive_scan(int32_t *v, int n, int32_t *
 // One workgroup: per-expert totals, the exclusive scan over experts (counts, offsets),
 // and each block's base row per expert, written over the block counts.  sh: 1024 + 256
 // ints of LDS.  Column loads go 16 blocks at a time, all in flight together.
+template <bool COH>
 __device__ __forceinline__ void dispatch_scan_block(int32_t *__restrict__ blockcounts, int nblk, int T, int E,
                                                     int S, int32_t *__restrict__ counts,
                                                     int32_t *__restrict__ offsets, int32_t *sh) {
@@ -117,36 +121,36 @@ __device__ __forceinline__ void dispatch_scan_block(int32_t *__restrict__ blockc
         for (int b0 = 0; b0 < nblk; b0 += CH) {
             int c[CH];
 #pragma unroll
-            for (int u = 0; u < CH; ++u) c[u] = blockcounts[(long)min(b0 + u, nblk - 1) * E + e];
+            for (int u = 0; u < CH; ++u) c[u] = ldc<COH>(blockcounts + (long)min(b0 + u, nblk - 1) * E + e);
 #pragma unroll
             for (int u = 0; u < CH; ++u)
                 if (b0 + u < nblk) s += c[u];
         }
         tot[e] = s;
-        counts[e] = s;
+        stc<COH>(counts + e, s);
     }
     __syncthreads();
     const int routed = block_exclusive_scan(tot, E, tmp);  // tot[e] = offsets[e] now
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         int s = tot[e];
-        offsets[e] = s;
+        stc<COH>(offsets + e, s);
         for (int b0 = 0; b0 < nblk; b0 += CH) {
             int c[CH];
 #pragma unroll
-            for (int u = 0; u < CH; ++u) c[u] = blockcounts[(long)min(b0 + u, nblk - 1) * E + e];
+            for (int u = 0; u < CH; ++u) c[u] = ldc<COH>(blockcounts + (long)min(b0 + u, nblk - 1) * E + e);
 #pragma unroll
             for (int u = 0; u < CH; ++u)
                 if (b0 + u < nblk) {
-                    blockcounts[(long)(b0 + u) * E + e] = s;
+                    stc<COH>(blockcounts + (long)(b0 + u) * E + e, s);
                     s += c[u];
                 }
         }
     }
     if (threadIdx.x == 0) {
-        offsets[E] = routed;
+        stc<COH>(offsets + E, routed);
         if (S) {
-            counts[E] = T;
-            offsets[E + 1] = routed + T;
+            stc<COH>(counts + E, T);
+            stc<COH>(offsets + E + 1, routed + T);
         }
     }
     __syncthreads();
@@ -154,12 +158,13 @@ __device__ __forceinline__ void dispatch_scan_block(int32_t *__restrict__ blockc
 
 // One workgroup: tile_start prefixes of both GEMMs over the G groups (ragged row tiles
 // times N tiles per group).  sh: 2 * 1032 + 256 ints of LDS.
+template <bool COH>
 __device__ __forceinline__ void tile_plan_block(const int32_t *__restrict__ offsets, int G, int bm1, int ntn1,
                                                 int bm2, int ntn2, int32_t *__restrict__ ts1,
                                                 int32_t *__restrict__ ts2, int32_t *sh) {
     int32_t *v1 = sh, *v2 = sh + 1032, *tmp = sh + 2064;
     for (int g = threadIdx.x; g < G; g += blockDim.x) {
-        const int c = offsets[g + 1] - offsets[g];
+        const int c = ldc<COH>(offsets + g + 1) - ldc<COH>(offsets + g);
         v1[g] = (c + bm1 - 1) / bm1 * ntn1;
         v2[g] = (c + bm2 - 1) / bm2 * ntn2;
     }
@@ -167,37 +172,38 @@ __device__ __forceinline__ void tile_plan_block(const int32_t *__restrict__ offs
     const int n1 = block_exclusive_scan(v1, G, tmp);
     const int n2 = block_exclusive_scan(v2, G, tmp);
     for (int g = threadIdx.x; g < G; g += blockDim.x) {
-        ts1[g] = v1[g];
-        ts2[g] = v2[g];
+        stc<COH>(ts1 + g, v1[g]);
+        stc<COH>(ts2 + g, v2[g]);
     }
     if (threadIdx.x == 0) {
-        ts1[G] = n1;
-        ts2[G] = n2;
+        stc<COH>(ts1 + G, n1);
+        stc<COH>(ts2 + G, n2);
     }
     __syncthreads();
 }
 
 // Rows of block blk: slot_to_row and row_to_slot from the block bases.
+template <bool COH>
 __device__ __forceinline__ void scatter_block(const int32_t *__restrict__ idx, int T, int k, int E, int blk,
                                               const int32_t *__restrict__ bases, int32_t *__restrict__ slot_to_row,
                                               int32_t *__restrict__ row_to_slot, unsigned long long *masks) {
-    build_masks(idx, T, k, E, blk, masks, nullptr);  // errors were reported by the count pass
+    build_masks<COH>(idx, T, k, E, blk, masks, nullptr);  // errors were reported by the count pass
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
     const long t = (long)blk * kDispTok + tid;
     if (t >= T) return;
     const unsigned long long below = (1ull << lane) - 1ull;
     int ids[kMaxChoices];
     bool bad, dup;
-    const uint32_t ok = load_choices(idx, t, k, E, ids, bad, dup);
+    const uint32_t ok = load_choices<COH>(idx, t, k, E, ids, bad, dup);
 #pragma unroll
     for (int j = 0; j < kMaxChoices; ++j) {
         if (!(ok >> j & 1u)) continue;
         const int e = ids[j];
         int rank = __popcll(masks[wave * E + e] & below);
         for (int w = 0; w < wave; ++w) rank += __popcll(masks[w * E + e]);
-        int row = bases[(long)blk * E + e] + rank;
-        slot_to_row[t * k + j] = row;
-        row_to_slot[row] = (int32_t)(t * k + j);
+        int row = ldc<COH>(bases + (long)blk * E + e) + rank;
+        stc<COH>(slot_to_row + t * k + j, row);
+        stc<COH>(row_to_slot + row, (int32_t)(t * k + j));
     }
 }
 
@@ -205,6 +211,7 @@ __device__ __forceinline__ void scatter_block(const int32_t *__restrict__ idx, i
 //
 // 16 lanes own one 128-value block (8 values each, one 16-byte load); gid is the global
 // lane index, block gid / 16.
+template <bool COH>
 __device__ __forceinline__ void quant_x_lane(const uint16_t *__restrict__ x, long nblocks, uint8_t *__restrict__ xq,
                                              float *__restrict__ xs, long gid) {
     const long blk = gid >> 4;
@@ -227,8 +234,8 @@ __device__ __forceinline__ void quant_x_lane(const uint16_t *__restrict__ x, lon
     uint2 out;
     out.x = cvt_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
     out.y = cvt_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
-    *(uint2 *)(xq + blk * 128 + sub * 8) = out;
-    if (sub == 0) xs[blk] = ldexpf(1.0f, e);
+    stc<COH>((uint64_t *)(xq + blk * 128 + sub * 8), (uint64_t)out.x | ((uint64_t)out.y << 32));
+    if (sub == 0) stc<COH>(xs + blk, ldexpf(1.0f, e));
 }
 
 }  // namespace moe

@@ -11,7 +11,7 @@ __global__ __launch_bounds__(256) void tile_plan_kernel(const int32_t *__restric
                                                        int ntn1, int bm2, int ntn2, int32_t *__restrict__ ts1,
                                                        int32_t *__restrict__ ts2) {
     __shared__ int32_t sh[2 * 1032 + 256];
-    tile_plan_block(offsets, G, bm1, ntn1, bm2, ntn2, ts1, ts2, sh);
+    tile_plan_block<false>(offsets, G, bm1, ntn1, bm2, ntn2, ts1, ts2, sh);
 }
 
 template <int BM, int BN, bool SWIGLU, bool GATHER>
@@ -40,10 +40,24 @@ FfnPlan ffn_plan(const Shape &s) {
     FfnPlan p;
     const long rows = s.rows();
     const double per_group = (double)rows / s.G();
-    p.decode = s.mode == MODE_FP8 && per_group <= 48.0;
+    const long G = s.G();
+    p.decode = s.mode == MODE_FP8 && per_group <= 48.0 && rows * (s.d > 2 * s.F ? s.d : 2 * s.F) < (1L << 31);
     if (p.decode) {
-        // one 64-lane wave per (group, 32-row tile, 32 output columns, K slice)
-        p.ks = rows <= 32 && (s.d / 128) % 4 == 0 ? 4 : 1;
+        // One 64-lane wave per (group, 32-row tile, 32 output columns, K slice).  linear1's
+        // K slices (whole 256-wide chunks) minimise rounds over the resident waves (256 CUs
+        // x 16) times the K per wave plus a fixed cost per tile worth 1024 of K, counting
+        // the row tiles one per touched group.
+        constexpr long kWaves = 4096;
+        const long mt = rows <= G ? rows : rows / 32 + G;
+        const long per_ks = mt * (2L * s.F / 32);
+        const int chunks = s.d % 256 == 0 ? s.d / 256 : 1;
+        long best_cost = -1;
+        p.ks = 1;
+        for (int q = 1; q <= chunks && q <= 32; ++q) {
+            if (chunks % q) continue;
+            const long cost = (per_ks * q + kWaves - 1) / kWaves * (s.d / q + 1024);
+            if (best_cost < 0 || cost < best_cost) { best_cost = cost; p.ks = q; }
+        }
         p.bm1 = p.bm2 = 32;
         p.bn1 = p.bn2 = 32;
         p.ntn1 = (2 * s.F / 32) * p.ks;

@@ -34,14 +34,14 @@ constexpr long kDecodeMaxWaves = 1L << 20;  // grid cap; the kernels stride over
 template <bool LIN1>
 __global__ __launch_bounds__(64) void fp8_decode_kernel(DecArgs a) {
     const int total = a.tile_start[a.G];
-    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) fp8_decode_tile<LIN1>(a, tile);
+    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) fp8_decode_tile<LIN1, false>(a, tile, a.tile_start, a.offsets);
 }
 
 __global__ __launch_bounds__(256) void fp8_decode_swiglu_kernel(const float *__restrict__ part, long rows, int F,
                                                                int ks, uint8_t *__restrict__ hq,
                                                                float *__restrict__ hs) {
     const long wid = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wid < rows * (F / 128)) decode_swiglu_wave(part, rows, F, ks, hq, hs, wid);
+    if (wid < rows * (F / 128)) decode_swiglu_wave<false>(part, rows, F, ks, hq, hs, wid);
 }
 
 static hipError_t launch_fp8_decode(const Shape &s, const FfnPlan &p, const uint8_t *w1, const uint8_t *w1s,

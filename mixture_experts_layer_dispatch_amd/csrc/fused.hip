@@ -51,7 +51,8 @@ size_t fused_lds_bytes(const Shape &s, const FfnPlan &p) {
     const int kind = router_kind(s, route_splitk_slices(s));
     size_t b = gemm_lds(s, p);
     const size_t r = router_lds(s, kind), m = (size_t)4 * s.E * 8, plan = (2 * 1032 + 256) * 4;
-    for (size_t v : {r, m, plan}) b = v > b ? v : b;
+    const size_t cached = p.decode ? (size_t)3 * (s.G() + 1) * 4 : 0;  // the plan, kept in LDS
+    for (size_t v : {r, m, plan, cached}) b = v > b ? v : b;
     return b;
 }
 
@@ -78,15 +79,17 @@ hipError_t launch_layer_fused(const Shape &s, const FfnPlan &p, FusedArgs &a, in
     a.b_r = nq;
     a.b_sel = a.b_r + nr;
     a.b_cnt = a.b_sel + nsel;
-    a.b_plan = a.b_cnt + a.nblk;
-    a.b_end = (a.b_plan + 1 + a.nblk + 7) / 8 * 8;
+    // with a single dispatch block the plan item also counts and scatters it
+    const long nsplit = a.nblk == 1 ? 0 : a.nblk;
+    a.b_plan = a.b_cnt + nsplit;
+    a.b_end = (a.b_plan + 1 + nsplit + 7) / 8 * 8;
     a.n1 = (a.rows * s.F + 255) / 256;
     a.n2 = (a.rows * s.d + 255) / 256;
     const int V = s.mode == MODE_F32 ? 4 : 8;
     const long lanes_c = (long)s.T * (s.d / V);
     a.ncb = p.decode ? (lanes_c + kWave - 1) / kWave : (lanes_c + 255) / 256;
     const size_t lds = fused_lds_bytes(s, p);
-    if (s.mode == MODE_F32) return launch_fused_kernel<MODE_F32, 128, 128, false>(a, lds, cu_limit, st);
+    if (s.mode == MODE_F32) return launch_fused_kernel<MODE_F32, 128, 128>(a, lds, cu_limit, st);
     if (s.mode == MODE_BF16) return launch_fused_bf16(a, p.bm1, p.bn2, lds, cu_limit, st);
     return launch_fused_fp8(a, p.decode, p.bm1, p.bn2, lds, cu_limit, st);
 }

@@ -19,15 +19,20 @@
 // resident (a cooperative launch) every wait ends.  Waits are still bounded in time:
 // after 2 s a wait sets the timeout error and gives up, and so does every later wait.
 //
-// Decode (FP8 x FP4, few rows per group): after the plan, items are single waves --
-// weight-streaming tiles of linear1 (K slices), then of linear2, then combine chunks.
-// The wave that completes the last linear1 slice of a 32-row tile adds the slices,
-// applies SwiGLU and quantises h for those rows, and then opens the tile to linear2.
+// Hand-offs.  An agent-scope fence costs microseconds per wave on MI355X and its acquire
+// half invalidates the XCD's whole L2, so fences are kept off the per-item path.  The
+// small data of the steps before the GEMMs (routing, histograms, plan, permutation, FP8
+// activations) moves through device-coherent (sc1) loads and stores, handed over by
+// counters alone.  The GEMM phases read it, and the GEMM outputs, with ordinary cached
+// loads; there each workgroup makes one acquire before linear1, one release after its
+// last linear1 tile, one acquire before its first linear2 tile, and the same again around
+// the combine.
 //
-// Memory ordering.  A producer makes its writes visible with an agent-scope release
-// fence (every wave) before one lane bumps the counter; a consumer spins on the counter
-// with relaxed agent-scope atomic loads and then issues an agent-scope acquire fence.
-// Each wait is made once per workgroup or wave and remembered.
+// Decode (FP8 x FP4, few rows per group): after the plan, items are single waves --
+// weight-streaming tiles of linear1 (K slices), then of linear2, then combine chunks --
+// and every hand-off is coherent: the wave that completes the last linear1 slice of a
+// 32-row tile adds the slices, applies SwiGLU and quantises h for those rows, and then
+// opens the tile to linear2.  The plan is cached in LDS once per workgroup.
 #pragma once
 
 #include "combine_dev.hpp"
@@ -45,122 +50,226 @@ constexpr uint64_t kSpinTicks = 200000000ull;  // 2 s of the 100 MHz real-time c
 __device__ __forceinline__ int atomic_ld(const int32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ int atomic_add(int32_t *p, int v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-// Lane 0 spins until *p >= target, or until a timeout is (or was) reported.
+// Lane 0 spins until *p >= target, or until a timeout is (or was) reported.  The sleep
+// between polls doubles up to MAXSLEEP x 8 x 64 cycles: a thousand workgroups polling
+// one word at full rate would starve the memory channel that serves it, and with it the
+// very producers they wait for.
+template <int MAXSLEEP>
 __device__ __forceinline__ void spin_until(const int32_t *p, int target, int32_t *err) {
     if (lane_id() == 0 && atomic_ld(p) < target) {
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        while (atomic_ld(p) < target) {
-            if (atomic_ld(err) == DEVERR_TIMEOUT) break;
-            if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
-                set_error(err, DEVERR_TIMEOUT);
-                break;
+        int backoff = 1;
+        for (unsigned n = 1; atomic_ld(p) < target; ++n) {
+            if ((n & 15) == 0) {
+                if (atomic_ld(err) == DEVERR_TIMEOUT) break;
+                if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
+                    set_error(err, DEVERR_TIMEOUT);
+                    break;
+                }
             }
-            __builtin_amdgcn_s_sleep(2);
+            for (int z = 0; z < backoff; ++z) __builtin_amdgcn_s_sleep(8);
+            backoff = backoff < MAXSLEEP ? 2 * backoff : MAXSLEEP;
         }
     }
+    compiler_fence();
 }
 
-// Workgroup-wide wait: wave 0 spins, then every wave acquires.
-__device__ __forceinline__ void wg_wait(const int32_t *p, int target, int32_t *err) {
-    if (threadIdx.x < kWave) spin_until(p, target, err);
+// ---- spread counters and replicated flags ----------------------------------------------
+
+__device__ __forceinline__ int32_t *counter_sub(int32_t *sync, int c, long id) {
+    return sync + ((long)c * kSpread + id % kSpread) * kSlot;
+}
+__device__ __forceinline__ int32_t *flag_replica(int32_t *sync, int f, long id) {
+    return sync + ((long)(NUM_COUNTERS + f) * kSpread + id % kSpread) * kSlot;
+}
+
+// Sum of a spread counter, in every lane of the calling wave (one load per lane).
+__device__ __forceinline__ int counter_sum(int32_t *sync, int c) {
+    int v = atomic_ld(counter_sub(sync, c, lane_id()));
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+// The calling wave polls a spread counter until its sum reaches target (bounded, with
+// the same back-off as spin_until).
+__device__ __forceinline__ void counter_wait(int32_t *sync, int c, int target, int32_t *err) {
+    if (counter_sum(sync, c) < target) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        int backoff = 1;
+        for (unsigned n = 1; counter_sum(sync, c) < target; ++n) {
+            if ((n & 15) == 0) {
+                if (__shfl(atomic_ld(err), 0, kWave) == DEVERR_TIMEOUT) break;
+                if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
+                    if (lane_id() == 0) set_error(err, DEVERR_TIMEOUT);
+                    break;
+                }
+            }
+            for (int z = 0; z < backoff; ++z) __builtin_amdgcn_s_sleep(8);
+            backoff = backoff < 16 ? 2 * backoff : 16;
+        }
+    }
+    compiler_fence();
+}
+
+// One wave raises a flag: all replicas (the wave's stores done first).
+__device__ __forceinline__ void flag_raise(int32_t *sync, int f) {
+    wait_vmcnt<0>();
+    compiler_fence();
+    __hip_atomic_store(flag_replica(sync, f, lane_id()), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---- coherent hand-offs (data moved with sc1 accesses) --------------------------------
+
+// Producer workgroup item id: every wave's sc1 stores complete, then counter c += 1.
+__device__ __forceinline__ void wg_count(int32_t *sync, int c, long id) {
+    wait_vmcnt<0>();
+    compiler_fence();
     __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (threadIdx.x == 0) atomic_add(counter_sub(sync, c, id), 1);
+}
+__device__ __forceinline__ void wg_counter_wait(int32_t *sync, int c, int target, int32_t *err) {
+    if (threadIdx.x < kWave) counter_wait(sync, c, target, err);
+    __syncthreads();
+    compiler_fence();
+}
+__device__ __forceinline__ void wg_flag_wait(int32_t *sync, int f, int32_t *err) {
+    if (threadIdx.x < kWave) spin_until<16>(flag_replica(sync, f, blockIdx.x), 1, err);
+    __syncthreads();
+    compiler_fence();
+}
+// Producer workgroup raising a flag once its (and every wave's) stores are done.
+__device__ __forceinline__ void wg_flag_raise(int32_t *sync, int f) {
+    wait_vmcnt<0>();
+    compiler_fence();
+    __syncthreads();
+    if (threadIdx.x < kWave) flag_raise(sync, f);
 }
 
-// Workgroup-wide release of everything written so far, then counter += v.
-__device__ __forceinline__ void wg_release_add(int32_t *ctr, int v) {
+// ---- fenced hand-offs (data moved with ordinary cached accesses) ------------------------
+
+__device__ __forceinline__ void wg_release_count(int32_t *sync, int c) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) atomic_add(counter_sub(sync, c, blockIdx.x), 1);
 }
-
-__device__ __forceinline__ void wave_wait(const int32_t *p, int target, int32_t *err) {
-    spin_until(p, target, err);
+__device__ __forceinline__ void wg_counter_wait_acquire(int32_t *sync, int c, int target, int32_t *err) {
+    wg_counter_wait(sync, c, target, err);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-}
-
-// Wave release, then counter += 1; returns the counter's previous value.
-__device__ __forceinline__ int wave_release_add(int32_t *ctr) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    int old = 0;
-    if (lane_id() == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return __shfl(old, 0, kWave);
 }
 
 __device__ __forceinline__ long round8(long n) { return (n + 7) / 8 * 8; }
-
-// Global index of a row tile: ts[g] / ntn row tiles precede group g.
-__device__ __forceinline__ int row_tile_index(const TileInfo &ti, const int32_t *ts, int ntn) {
-    return ts[ti.g] / ntn + ti.mt;
-}
 
 // ---- items of the steps before the GEMMs (workgroup items, 256 threads) ----------------
 
 template <int MODE>
 __device__ __forceinline__ void front_item(const FusedArgs &a, long i, uint8_t *lds, bool &routed) {
+    const int nr = (int)(a.b_sel - a.b_r);
     if (i < a.b_r) {  // FP8 activations: 64 blocks of 128 per item
         const long nblocks = (long)a.T * a.d / 128;
 #pragma unroll
         for (int pass = 0; pass < 4; ++pass)
-            quant_x_lane((const uint16_t *)a.x, nblocks, a.xq, a.xs, (i * 4 + pass) * 256 + threadIdx.x);
-        wg_release_add(a.sync + SYNC_QUANT, 1);
+            quant_x_lane<true>((const uint16_t *)a.x, nblocks, a.xq, a.xs, (i * 4 + pass) * 256 + threadIdx.x);
+        wg_count(a.sync, CNT_QUANT, i);
     } else if (i < a.b_sel) {  // router
         const int b = (int)(i - a.b_r);
         float *lg = (float *)lds;
         if (a.router == ROUTER_SPLITK) {
             const long w = (long)b * 4 + (threadIdx.x >> 6);
             if (w < (long)(a.E / 32) * a.nks * ((a.T + 31) / 32))
-                route_splitk_wave((const uint16_t *)a.x, (const uint16_t *)a.wr, a.T, a.d, a.E, a.nks, w, a.rpart);
+                route_splitk_wave<true>((const uint16_t *)a.x, (const uint16_t *)a.wr, a.T, a.d, a.E, a.nks, w,
+                                        a.rpart);
         } else if (a.router == ROUTER_MFMA) {
             if constexpr (MODE != MODE_F32)
-                route_mfma_block((const uint16_t *)a.x, (const uint16_t *)a.wr, a.bias, a.T, a.d, a.E, a.k, a.gating, b,
-                             lg, a.idx, a.gate, nullptr, nullptr, a.err);
-        } else if (a.router == ROUTER_VALU8) {
-            route_valu_block<MODE == MODE_F32, 8>(a.x, a.wr, a.bias, a.T, a.d, a.E, a.k, a.gating, b, lg, a.idx,
-                                                   a.gate, nullptr, nullptr, a.err);
+                route_mfma_block<true>((const uint16_t *)a.x, (const uint16_t *)a.wr, a.bias, a.T, a.d, a.E, a.k,
+                                       a.gating, b, lg, a.idx, a.gate, nullptr, nullptr, a.err);
         } else {
-            route_valu_block<MODE == MODE_F32, 32>(a.x, a.wr, a.bias, a.T, a.d, a.E, a.k, a.gating, b, lg, a.idx,
-                                                    a.gate, nullptr, nullptr, a.err);
+            route_valu_block<MODE == MODE_F32, 8, true>(a.x, a.wr, a.bias, a.T, a.d, a.E, a.k, a.gating, b, lg,
+                                                        a.idx, a.gate, nullptr, nullptr, a.err);
         }
-        wg_release_add(a.sync + SYNC_ROUTE, 1);
+        wg_count(a.sync, CNT_ROUTE, b);
     } else if (i < a.b_cnt) {  // split-K router: one token's selection
         if (!routed) {
-            wg_wait(a.sync + SYNC_ROUTE, (int)(a.b_sel - a.b_r), a.err);
+            wg_counter_wait(a.sync, CNT_ROUTE, nr, a.err);
             routed = true;
         }
-        route_sum_select(a.rpart, a.nks, a.T, a.E, a.k, a.gating, a.bias, i - a.b_sel, (float *)lds, a.idx, a.gate,
-                         nullptr, nullptr, a.err);
-        wg_release_add(a.sync + SYNC_SELECT, 1);
+        route_sum_select<true>(a.rpart, a.nks, a.T, a.E, a.k, a.gating, a.bias, i - a.b_sel, (float *)lds, a.idx,
+                               a.gate, nullptr, nullptr, a.err);
+        wg_count(a.sync, CNT_SELECT, i - a.b_sel);
     } else if (i < a.b_plan) {  // dispatch histogram of one block
-        wg_wait(a.router == ROUTER_SPLITK ? a.sync + SYNC_SELECT : a.sync + SYNC_ROUTE,
-                (int)(a.router == ROUTER_SPLITK ? a.T : a.b_sel - a.b_r), a.err);
-        count_block(a.idx, a.T, a.k, a.E, (int)(i - a.b_cnt), (unsigned long long *)lds, a.blockcounts, a.err);
-        wg_release_add(a.sync + SYNC_COUNT, 1);
+        if (a.router == ROUTER_SPLITK) wg_counter_wait(a.sync, CNT_SELECT, a.T, a.err);
+        else wg_counter_wait(a.sync, CNT_ROUTE, nr, a.err);
+        count_block<true>(a.idx, a.T, a.k, a.E, (int)(i - a.b_cnt), (unsigned long long *)lds, a.blockcounts,
+                          a.err);
+        wg_count(a.sync, CNT_COUNT, i - a.b_cnt);
     } else if (i == a.b_plan) {  // scan, tile plans, cleared row-tile counters
-        wg_wait(a.sync + SYNC_COUNT, a.nblk, a.err);
+        if (a.nblk == 1) {
+            // one dispatch block: histogram, scan, plan and scatter in this one item
+            if (a.router == ROUTER_SPLITK) wg_counter_wait(a.sync, CNT_SELECT, a.T, a.err);
+            else wg_counter_wait(a.sync, CNT_ROUTE, nr, a.err);
+            count_block<true>(a.idx, a.T, a.k, a.E, 0, (unsigned long long *)lds, a.blockcounts, a.err);
+            wait_vmcnt<0>();
+            __syncthreads();
+        } else {
+            wg_counter_wait(a.sync, CNT_COUNT, a.nblk, a.err);
+        }
         int32_t *sh = (int32_t *)lds;
-        dispatch_scan_block(a.blockcounts, a.nblk, a.T, a.E, a.S, a.counts, a.offsets, sh);
-        tile_plan_block(a.offsets, a.G, a.bm, a.ntn1, a.bm, a.ntn2, a.ts1, a.ts2, sh);
-        for (int m = threadIdx.x; m < a.nm; m += blockDim.x) a.done1[m] = 0;
-        wg_release_add(a.sync + SYNC_PLAN, 1);
-    } else if (i < a.b_plan + 1 + a.nblk) {  // dispatch scatter of one block
-        wg_wait(a.sync + SYNC_PLAN, 1, a.err);
-        scatter_block(a.idx, a.T, a.k, a.E, (int)(i - a.b_plan - 1), a.blockcounts, a.s2r, a.r2s,
-                      (unsigned long long *)lds);
-        wg_release_add(a.sync + SYNC_SCATTER, 1);
+        dispatch_scan_block<true>(a.blockcounts, a.nblk, a.T, a.E, a.S, a.counts, a.offsets, sh);
+        tile_plan_block<true>(a.offsets, a.G, a.bm, a.ntn1, a.bm, a.ntn2, a.ts1, a.ts2, sh);
+        for (long m = threadIdx.x; m < (long)a.nm * kRowTileSlots; m += blockDim.x) stc<true>(a.done1 + m * kSlot, 0);
+        if (a.nblk == 1) {
+            wait_vmcnt<0>();
+            __syncthreads();
+            scatter_block<true>(a.idx, a.T, a.k, a.E, 0, a.blockcounts, a.s2r, a.r2s, (unsigned long long *)lds);
+            wg_counter_wait(a.sync, CNT_QUANT, (int)a.b_r, a.err);
+            wg_flag_raise(a.sync, FLAG_FRONT);
+        } else {
+            wg_flag_raise(a.sync, FLAG_PLAN);
+        }
+    } else if (a.nblk > 1 && i < a.b_plan + 1 + a.nblk) {  // dispatch scatter of one block
+        wg_flag_wait(a.sync, FLAG_PLAN, a.err);
+        scatter_block<true>(a.idx, a.T, a.k, a.E, (int)(i - a.b_plan - 1), a.blockcounts, a.s2r, a.r2s,
+                            (unsigned long long *)lds);
+        // the last scatter block also waits for the activations, then opens linear1
+        wait_vmcnt<0>();
+        compiler_fence();
+        __syncthreads();
+        int *last = (int *)lds;
+        if (threadIdx.x == 0) *last = atomic_add(a.sync + kSyncTopScatter, 1) == a.nblk - 1;
+        __syncthreads();
+        if (*last) {
+            wg_counter_wait(a.sync, CNT_QUANT, (int)a.b_r, a.err);
+            wg_flag_raise(a.sync, FLAG_FRONT);
+        }
     }
-    // [b_plan + 1 + nblk, b_end): padding to a multiple of 8
+    // the rest up to b_end: padding to a multiple of 8
 }
 
-// Workgroup exit: the last one out clears the counters for the next launch.
-__device__ __forceinline__ void fused_exit(const FusedArgs &a) {
+// Workgroup exit: the last one out clears the synchronisation words for the next launch
+// (a two-level count: one sub-counter per 64 workgroups, then a top counter).
+__device__ __forceinline__ void fused_exit(const FusedArgs &a, uint8_t *lds) {
     __syncthreads();
+    int *last = (int *)lds;
     if (threadIdx.x == 0) {
-        const int old = __hip_atomic_fetch_add(a.sync + SYNC_EXIT, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (old == (int)gridDim.x - 1) {
-            for (int w = 0; w < SYNC_WORDS; ++w)
-                __hip_atomic_store(a.sync + w, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int P = (int)gridDim.x, sub = (int)(blockIdx.x % kSpread);
+        const int nsub = P < kSpread ? P : kSpread, per = (P - sub + kSpread - 1) / kSpread;
+        int l = 0;
+        if (atomic_add(counter_sub(a.sync, CNT_EXIT, sub), 1) == per - 1)
+            l = atomic_add(a.sync + kSyncTopExit, 1) == nsub - 1;
+        *last = l;
+    }
+    __syncthreads();
+    if (*last) {
+        for (int w = threadIdx.x; w < (NUM_COUNTERS + NUM_FLAGS) * kSpread; w += blockDim.x)
+            __hip_atomic_store(a.sync + (long)w * kSlot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x == 0) {
+            __hip_atomic_store(a.sync + kSyncTopExit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.sync + kSyncTopScatter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -176,27 +285,19 @@ __device__ __forceinline__ void fused_tiled(const FusedArgs &a, uint8_t *lds) {
         __syncthreads();  // the previous item may still read its LDS
         front_item<MODE>(a, i, lds, routed);
     }
-    wg_wait(a.sync + SYNC_PLAN, 1, a.err);
+    // everything before linear1, then one acquire: the GEMMs read it with cached loads
+    wg_flag_wait(a.sync, FLAG_FRONT, a.err);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const long N1 = MODE == MODE_F32 ? a.n1 : a.ts1[a.G], N2 = MODE == MODE_F32 ? a.n2 : a.ts2[a.G];
     const long e1 = a.b_end + round8(N1), e2 = e1 + round8(N2), e3 = e2 + a.ncb;
-    bool scattered = false, lin1_all = false, lin2_all = false;
-    for (; i < e3; i += P) {
+    for (; i < e1; i += P) {  // linear1
         __syncthreads();
-        if (i < e1) {  // linear1
-            if (!scattered) {
-                wg_wait(a.sync + SYNC_SCATTER, a.nblk, a.err);
-                if constexpr (MODE == MODE_FP8) wg_wait(a.sync + SYNC_QUANT, (int)a.b_r, a.err);
-                scattered = true;
-            }
-            const long j = i - a.b_end;
-            if constexpr (MODE == MODE_F32) {
-                if (j < N1) {
-                    ffn1_f32_lane((const float *)a.x, a.r2s, (const float *)a.w1, a.offsets, a.G, a.T, a.k, a.d, a.F,
-                                  a.rows, (float *)a.h, j * 256 + threadIdx.x);
-                    wg_release_add(a.sync + SYNC_LIN1, 1);
-                }
-                continue;
-            }
+        const long j = i - a.b_end;
+        if constexpr (MODE == MODE_F32) {
+            if (j < N1)
+                ffn1_f32_lane((const float *)a.x, a.r2s, (const float *)a.w1, a.offsets, a.G, a.T, a.k, a.d, a.F,
+                              a.rows, (float *)a.h, j * 256 + threadIdx.x);
+        } else {
             const int tile = pick_tile((int)j, (int)N1);
             if (tile < 0) continue;
             if constexpr (MODE == MODE_BF16) {
@@ -208,26 +309,24 @@ __device__ __forceinline__ void fused_tiled(const FusedArgs &a, uint8_t *lds) {
                              a.ts1, a.T, a.k, a.d, 2 * a.F, a.F, a.G, a.F};
                 fp8_tile<BM, 256, 4, true, true>(g, tile, lds);
             }
-            const TileInfo ti = decode_tile(tile, a.ts1, a.offsets, a.G, BM);
-            wg_release_add(a.done1 + row_tile_index(ti, a.ts1, a.ntn1), 1);
-        } else if (i < e2) {  // linear2
-            const long j = i - e1;
-            if constexpr (MODE == MODE_F32) {
-                if (j < N2) {
-                    if (!lin1_all) {
-                        wg_wait(a.sync + SYNC_LIN1, (int)N1, a.err);
-                        lin1_all = true;
-                    }
-                    ffn2_f32_lane((const float *)a.h, (const float *)a.w2, a.offsets, a.G, a.d, a.F, a.rows,
-                                  (float *)a.yperm, j * 256 + threadIdx.x);
-                    wg_release_add(a.sync + SYNC_LIN2, 1);
-                }
-                continue;
-            }
+        }
+    }
+    wg_release_count(a.sync, CNT_LIN1);
+    bool waited = false;
+    for (; i < e2; i += P) {  // linear2
+        if (!waited) {
+            wg_counter_wait_acquire(a.sync, CNT_LIN1, (int)P, a.err);
+            waited = true;
+        }
+        __syncthreads();
+        const long j = i - e1;
+        if constexpr (MODE == MODE_F32) {
+            if (j < N2)
+                ffn2_f32_lane((const float *)a.h, (const float *)a.w2, a.offsets, a.G, a.d, a.F, a.rows,
+                              (float *)a.yperm, j * 256 + threadIdx.x);
+        } else {
             const int tile = pick_tile((int)j, (int)N2);
             if (tile < 0) continue;
-            const TileInfo ti = decode_tile(tile, a.ts2, a.offsets, a.G, BM);
-            wg_wait(a.done1 + row_tile_index(ti, a.ts2, a.ntn2), a.ntn1, a.err);
             if constexpr (MODE == MODE_BF16) {
                 GemmArgs g = {(const uint16_t *)a.h, nullptr, (const uint16_t *)a.w2, (uint16_t *)a.yperm, a.offsets,
                               a.ts2, a.T, a.k, a.F, a.d, a.d, a.G, a.F};
@@ -237,17 +336,19 @@ __device__ __forceinline__ void fused_tiled(const FusedArgs &a, uint8_t *lds) {
                              a.yperm, nullptr, a.offsets, a.ts2, a.T, a.k, a.F, a.d, a.d, a.G, a.F};
                 fp8_tile<BM, BN2, 2, false, false>(g, tile, lds);
             }
-            wg_release_add(a.sync + SYNC_LIN2, 1);
-        } else {  // combine
-            if (!lin2_all) {
-                wg_wait(a.sync + SYNC_LIN2, (int)N2, a.err);
-                lin2_all = true;
-            }
-            combine_lane<MODE == MODE_F32>(a.yperm, a.s2r, a.gate, a.y, a.T, a.k, a.d, a.S,
-                                           (i - e2) * 256 + threadIdx.x);
         }
     }
-    fused_exit(a);
+    wg_release_count(a.sync, CNT_LIN2);
+    waited = false;
+    for (; i < e3; i += P) {  // combine
+        if (!waited) {
+            wg_counter_wait_acquire(a.sync, CNT_LIN2, (int)P, a.err);
+            waited = true;
+        }
+        combine_lane<MODE == MODE_F32, false>(a.yperm, a.s2r, a.gate, a.y, a.T, a.k, a.d, a.S,
+                                              (i - e2) * 256 + threadIdx.x);
+    }
+    fused_exit(a, lds);
 }
 
 // ---- decode variant (FP8 x FP4, few rows per group): wave items after the plan --------
@@ -260,64 +361,85 @@ __device__ __forceinline__ void fused_decode(const FusedArgs &a, uint8_t *lds) {
         __syncthreads();
         front_item<MODE_FP8>(a, i, lds, routed);
     }
-    wg_wait(a.sync + SYNC_PLAN, 1, a.err);
-    const long N1 = a.ts1[a.G], N2 = a.ts2[a.G];
+    wg_flag_wait(a.sync, FLAG_FRONT, a.err);
+    // the plan in LDS: tile prefixes of both GEMMs and the group offsets
+    const int G = a.G;
+    int32_t *lts1 = (int32_t *)lds, *lts2 = lts1 + (G + 1), *loffs = lts2 + (G + 1);
+    __syncthreads();
+    for (int g = threadIdx.x; g <= G; g += blockDim.x) {
+        lts1[g] = ldc<true>(a.ts1 + g);
+        lts2[g] = ldc<true>(a.ts2 + g);
+        loffs[g] = ldc<true>(a.offsets + g);
+    }
+    __syncthreads();
+    const long N1 = lts1[G], N2 = lts2[G];
     const long e1 = N1, e2 = e1 + N2, e3 = e2 + a.ncb;
     const int lane = lane_id();
-    bool ready = false, lin2_all = false;
+    bool lin2_all = false;
     const DecArgs d1 = {a.xq, a.xs, a.r2s, a.offsets, a.ts1, (const uint8_t *)a.w1, (const uint8_t *)a.w1s,
-                        a.upart, nullptr, a.rows, a.T, a.k, a.d, 2 * a.F, a.G, a.ks};
+                        a.upart, nullptr, a.rows, a.T, a.k, a.d, 2 * a.F, G, a.ks};
     const DecArgs d2 = {(const uint8_t *)a.h, a.hs, nullptr, a.offsets, a.ts2, (const uint8_t *)a.w2,
-                        (const uint8_t *)a.w2s, nullptr, (uint16_t *)a.yperm, a.rows, a.T, a.k, a.F, a.d, a.G, 1};
+                        (const uint8_t *)a.w2s, nullptr, (uint16_t *)a.yperm, a.rows, a.T, a.k, a.F, a.d, G, 1};
     const int nfb = a.F / 128;
     for (long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6); w < e3; w += 4 * P) {
         if (w < e1) {  // linear1 K slice of a (32 rows x 32 columns) tile
-            if (!ready) {
-                wave_wait(a.sync + SYNC_SCATTER, a.nblk, a.err);
-                wave_wait(a.sync + SYNC_QUANT, (int)a.b_r, a.err);
-                ready = true;
-            }
             const int tile = (int)w;
-            fp8_decode_tile<true>(d1, tile);
-            const TileInfo ti = decode_tile(tile, a.ts1, a.offsets, a.G, 32);
-            int32_t *ctr = a.done1 + row_tile_index(ti, a.ts1, a.ntn1);
-            if (wave_release_add(ctr) == a.ntn1 - 1) {
+            fp8_decode_tile<true, true>(d1, tile, lts1, loffs);
+            const TileInfo ti = decode_tile(tile, lts1, loffs, G, 32);
+            int32_t *rt = a.done1 + (long)(lts1[ti.g] / a.ntn1 + ti.mt) * kRowTileSlots * kSlot;
+            // two-level count of this row tile's linear1 items: sub-counter (item % 8), then top
+            wait_vmcnt<0>();
+            compiler_fence();
+            int done = 0;
+            if (lane == 0 && atomic_add(rt + (ti.nt % 8) * kSlot, 1) == a.ntn1 / 8 - 1)
+                done = atomic_add(rt + 8 * kSlot, 1) == 7;
+            if (__shfl(done, 0, kWave)) {
                 // last slice of this row tile: SwiGLU + e4m3 for its rows, then open it to linear2
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
                 for (long q = 0; q < (long)ti.nrows * nfb; ++q)
-                    decode_swiglu_wave(a.upart, a.rows, a.F, a.ks, (uint8_t *)a.h, a.hs,
-                                       (long)ti.row0 * nfb + q);
-                wave_release_add(ctr);
+                    decode_swiglu_wave<true>(a.upart, a.rows, a.F, a.ks, (uint8_t *)a.h, a.hs,
+                                             (long)ti.row0 * nfb + q);
+                wait_vmcnt<0>();
+                compiler_fence();
+                if (lane < 8) __hip_atomic_store(rt + (9 + lane) * kSlot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         } else if (w < e2) {  // linear2 tile
             const int tile = (int)(w - e1);
-            const TileInfo ti = decode_tile(tile, a.ts2, a.offsets, a.G, 32);
-            wave_wait(a.done1 + row_tile_index(ti, a.ts2, a.ntn2), a.ntn1 + 1, a.err);
-            fp8_decode_tile<false>(d2, tile);
-            wave_release_add(a.sync + SYNC_LIN2);
+            const TileInfo ti = decode_tile(tile, lts2, loffs, G, 32);
+            const int32_t *rt = a.done1 + (long)(lts2[ti.g] / a.ntn2 + ti.mt) * kRowTileSlots * kSlot;
+            spin_until<16>(rt + (9 + w % 8) * kSlot, 1, a.err);
+            fp8_decode_tile<false, true>(d2, tile, lts2, loffs);
+            wait_vmcnt<0>();
+            compiler_fence();
+            if (lane == 0) atomic_add(counter_sub(a.sync, CNT_LIN2, w), 1);
         } else {  // combine: 64 lanes x 8 columns
             if (!lin2_all) {
-                wave_wait(a.sync + SYNC_LIN2, (int)N2, a.err);
+                counter_wait(a.sync, CNT_LIN2, (int)N2, a.err);
                 lin2_all = true;
             }
-            combine_lane<false>(a.yperm, a.s2r, a.gate, a.y, a.T, a.k, a.d, a.S, (w - e2) * kWave + lane);
+            // y_perm lines are written by two linear2 tiles each, all finished before this read
+            combine_lane<false, false>(a.yperm, a.s2r, a.gate, a.y, a.T, a.k, a.d, a.S, (w - e2) * kWave + lane);
         }
     }
-    fused_exit(a);
+    fused_exit(a, lds);
 }
 
-template <int MODE, int BM, int BN2, bool DEC>
+template <int MODE, int BM, int BN2>
 __global__ __launch_bounds__(256) void fused_layer_kernel(FusedArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    if constexpr (DEC) fused_decode(a, lds);
-    else fused_tiled<MODE, BM, BN2>(a, lds);
+    fused_tiled<MODE, BM, BN2>(a, lds);
+}
+
+// The decode variant streams weights: it is held to 128 registers so that four waves
+// share each SIMD.
+template <int UNUSED = 0>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void fused_decode_kernel(FusedArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    fused_decode(a, lds);
 }
 
 // Host side: a cooperative launch of as many workgroups as fit on the device at once
 // (at most cu_limit CUs' worth when cu_limit > 0).
-template <int MODE, int BM, int BN2, bool DEC>
-hipError_t launch_fused_kernel(FusedArgs &a, size_t lds, int cu_limit, hipStream_t st) {
-    const void *fn = (const void *)fused_layer_kernel<MODE, BM, BN2, DEC>;
+inline hipError_t launch_fused_fn(const void *fn, FusedArgs &a, size_t lds, int cu_limit, hipStream_t st) {
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -336,6 +458,11 @@ hipError_t launch_fused_kernel(FusedArgs &a, size_t lds, int cu_limit, hipStream
     e = hipLaunchCooperativeKernel(fn, dim3(P), dim3(256), args, (unsigned)lds, st);
     prof_end("layer_fused", st);
     return e;
+}
+
+template <int MODE, int BM, int BN2>
+hipError_t launch_fused_kernel(FusedArgs &a, size_t lds, int cu_limit, hipStream_t st) {
+    return launch_fused_fn((const void *)fused_layer_kernel<MODE, BM, BN2>, a, lds, cu_limit, st);
 }
 
 }  // namespace moe

@@ -4,11 +4,11 @@
 namespace moe {
 
 hipError_t launch_fused_fp8(FusedArgs &a, bool decode, int bm, int bn2, size_t lds, int cu_limit, hipStream_t st) {
-    if (decode) return launch_fused_kernel<MODE_FP8, 32, 32, true>(a, lds, cu_limit, st);
-    if (bm == 256 && bn2 == 256) return launch_fused_kernel<MODE_FP8, 256, 256, false>(a, lds, cu_limit, st);
-    if (bm == 256) return launch_fused_kernel<MODE_FP8, 256, 128, false>(a, lds, cu_limit, st);
-    if (bn2 == 256) return launch_fused_kernel<MODE_FP8, 128, 256, false>(a, lds, cu_limit, st);
-    return launch_fused_kernel<MODE_FP8, 128, 128, false>(a, lds, cu_limit, st);
+    if (decode) return launch_fused_fn((const void *)fused_decode_kernel<0>, a, lds, cu_limit, st);
+    if (bm == 256 && bn2 == 256) return launch_fused_kernel<MODE_FP8, 256, 256>(a, lds, cu_limit, st);
+    if (bm == 256) return launch_fused_kernel<MODE_FP8, 256, 128>(a, lds, cu_limit, st);
+    if (bn2 == 256) return launch_fused_kernel<MODE_FP8, 128, 256>(a, lds, cu_limit, st);
+    return launch_fused_kernel<MODE_FP8, 128, 128>(a, lds, cu_limit, st);
 }
 
 }  // namespace moe

@@ -341,16 +341,25 @@ struct DecArgs {
     int T, k, K, N, G, ks;
 };
 
-template <bool LIN1>
-__device__ __forceinline__ void fp8_decode_tile(const DecArgs &a, int tile) {
-    int g, lo = 0, hi = a.G - 1;
+// One (group, 32-row tile, 32 output columns, K slice) tile; ts / offs may live in LDS.
+// K advances 256 per iteration (four MFMAs): the four steps' B scales arrive in two dword
+// loads and their A scales in two floats.
+//
+// COH (the persistent kernel): the outputs -- linear1 partial sums, linear2 rows -- are
+// stored device-coherently, and linear2's A scales are loaded so (an h-scale line can
+// hold rows of two row tiles, finished by different waves).  Every other input is read
+// through the caches: each of its lines has a single writer, which finished before any
+// reader was let in, so no cache can hold an older copy.
+template <bool LIN1, bool COH>
+__device__ __forceinline__ void fp8_decode_tile(const DecArgs &a, int tile, const int32_t *ts, const int32_t *offs) {
+    int lo = 0, hi = a.G - 1;
     while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
-        if (a.tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
+        if (ts[mid] <= tile) lo = mid; else hi = mid - 1;
     }
-    g = lo;
-    const int rb = a.offsets[g], cnt = a.offsets[g + 1] - rb;
-    const int mtiles = (cnt + 31) / 32, local = tile - a.tile_start[g];
+    const int g = lo;
+    const int rb = offs[g], cnt = offs[g + 1] - rb;
+    const int mtiles = (cnt + 31) / 32, local = tile - ts[g];
     const int mt = local % mtiles, rest = local / mtiles;
     const int nt = LIN1 ? rest / a.ks : rest, ksl = LIN1 ? rest % a.ks : 0;
     const int row0 = rb + mt * 32, nrows = min(32, cnt - mt * 32);
@@ -360,52 +369,62 @@ __device__ __forceinline__ void fp8_decode_tile(const DecArgs &a, int tile) {
     const long grow = row0 + (r < nrows ? r : 0);
     const long src = LIN1 ? row_token(grow, a.row_to_slot, a.T, a.k) : grow;
     const int KB = a.K / 128;
-    const uint8_t *pa = a.A + src * a.K;
+    const size_t arow = (size_t)src * a.K;  // byte offset of the A row
     const float *psa = a.As + src * KB;
     const long n = (long)nt * 32 + r;
     const uint8_t *pb = a.B + ((long)g * a.N + n) * (a.K / 2);
     const uint8_t *psb = a.Bs + ((long)g * a.N + n) * (a.K / 32);
-    const int kc = a.K / a.ks, kbeg = ksl * kc;
+    const int kc = a.K / a.ks, kbeg = ksl * kc, kend = kbeg + kc;
 
     f32x16 acc = (f32x16){};
-    const int kend = kbeg + kc;  // kc is a multiple of 64
-#define DEC_STEPS(U, k0)                                                                               \
-    do {                                                                                               \
-        i32x4 alo[U], ahi[U], bq[U];                                                                   \
-        int sa[U], sb[U];                                                                              \
-        _Pragma("unroll") for (int u = 0; u < U; ++u) {                                                \
-            const int kk = (k0) + 64 * u;                                                              \
-            /* fp8 A operand: K {16 kh..+15} and {32 + 16 kh..+15} of the 64-wide step */             \
-            alo[u] = *(const i32x4 *)(pa + kk + 16 * kh);                                              \
-            ahi[u] = *(const i32x4 *)(pa + kk + 32 + 16 * kh);                                         \
-            /* fp4 B operand: 32 consecutive K from 32 kh, one e8m0 block */                           \
-            bq[u] = *(const i32x4 *)(pb + (kk + 32 * kh) / 2);                                         \
-            sb[u] = psb[(kk + 32 * kh) / 32];                                                          \
-            sa[u] = (int)((__float_as_uint(psa[kk / 128]) >> 23) & 0xFF);                              \
-        }                                                                                              \
-        _Pragma("unroll") for (int u = 0; u < U; ++u) {                                                \
-            i32x8 av = {alo[u][0], alo[u][1], alo[u][2], alo[u][3], ahi[u][0], ahi[u][1], ahi[u][2], ahi[u][3]}; \
-            i32x8 bv = {bq[u][0], bq[u][1], bq[u][2], bq[u][3], 0, 0, 0, 0};                           \
-            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 4, 0, sa[u], 0, sb[u]); \
-        }                                                                                              \
-    } while (0)
     int k0 = kbeg;
-    for (; k0 + 256 <= kend; k0 += 256) DEC_STEPS(4, k0);
-    for (; k0 < kend; k0 += 64) DEC_STEPS(1, k0);
-#undef DEC_STEPS
+    for (; k0 + 256 <= kend; k0 += 256) {
+        i32x4 alo[4], ahi[4], bq[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int kk = k0 + 64 * u;
+            // fp8 A operand: K {16 kh..+15} and {32 + 16 kh..+15} of the 64-wide step
+            alo[u] = *(const i32x4 *)(a.A + arow + kk + 16 * kh);
+            ahi[u] = *(const i32x4 *)(a.A + arow + kk + 32 + 16 * kh);
+            // fp4 B operand: 32 consecutive K from 32 kh, one e8m0 block
+            bq[u] = *(const i32x4 *)(pb + (kk + 32 * kh) / 2);
+        }
+        const uint32_t sb01 = *(const uint32_t *)(psb + k0 / 32), sb23 = *(const uint32_t *)(psb + k0 / 32 + 4);
+        const float sa01 = ldc<COH && !LIN1>(psa + k0 / 128), sa23 = ldc<COH && !LIN1>(psa + k0 / 128 + 1);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            i32x8 av = {alo[u][0], alo[u][1], alo[u][2], alo[u][3], ahi[u][0], ahi[u][1], ahi[u][2], ahi[u][3]};
+            i32x8 bv = {bq[u][0], bq[u][1], bq[u][2], bq[u][3], 0, 0, 0, 0};
+            const uint32_t sbw = u < 2 ? sb01 : sb23;
+            const int sb = (int)((sbw >> (8 * (2 * (u & 1) + kh))) & 0xFF);
+            const int sa = (int)((__float_as_uint(u < 2 ? sa01 : sa23) >> 23) & 0xFF);
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 4, 0, sa, 0, sb);
+        }
+    }
+    for (; k0 < kend; k0 += 64) {
+        const i32x4 lo4 = *(const i32x4 *)(a.A + arow + k0 + 16 * kh);
+        const i32x4 hi4 = *(const i32x4 *)(a.A + arow + k0 + 32 + 16 * kh);
+        const i32x4 b4 = *(const i32x4 *)(pb + (k0 + 32 * kh) / 2);
+        const int sb = psb[(k0 + 32 * kh) / 32];
+        const int sa = (int)((__float_as_uint(ldc<COH && !LIN1>(psa + k0 / 128)) >> 23) & 0xFF);
+        i32x8 av = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        i32x8 bv = {b4[0], b4[1], b4[2], b4[3], 0, 0, 0, 0};
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 4, 0, sa, 0, sb);
+    }
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         const int row = 8 * (q >> 2) + 4 * kh + (q & 3);
         if (row >= nrows) continue;
         const long orow = row0 + row;
-        if (LIN1) a.part[((long)ksl * a.rows + orow) * a.N + n] = acc[q];
-        else a.Y[orow * a.N + n] = f32_to_bf16(acc[q]);
+        if (LIN1) stc<COH>(a.part + ((long)ksl * a.rows + orow) * a.N + n, acc[q]);
+        else stc16<COH>(a.Y, (size_t)(orow * a.N + n), f32_to_bf16(acc[q]));
     }
 }
 
 // Sums the K slices of linear1 in order, applies SwiGLU and quantises h to e4m3 with one
 // power-of-two scale per 128 columns.  One wave per (row, 128-column block): wid = row *
 // (F / 128) + block.
+template <bool COH>
 __device__ __forceinline__ void decode_swiglu_wave(const float *__restrict__ part, long rows, int F, int ks,
                                                   uint8_t *__restrict__ hq, float *__restrict__ hs, long wid) {
     const int lane = lane_id();
@@ -415,8 +434,8 @@ __device__ __forceinline__ void decode_swiglu_wave(const float *__restrict__ par
     float gsum[2] = {0.0f, 0.0f}, usum[2] = {0.0f, 0.0f};
     for (int q = 0; q < ks; ++q) {
         const float *p = part + ((long)q * rows + r) * (2L * F);
-        gsum[0] += p[f]; gsum[1] += p[f + 1];
-        usum[0] += p[F + f]; usum[1] += p[F + f + 1];
+        gsum[0] += ldc<COH>(p + f); gsum[1] += ldc<COH>(p + f + 1);
+        usum[0] += ldc<COH>(p + F + f); usum[1] += ldc<COH>(p + F + f + 1);
     }
     float h[2];
 #pragma unroll
@@ -426,8 +445,8 @@ __device__ __forceinline__ void decode_swiglu_wave(const float *__restrict__ par
     const int e = e4m3_block_exponent(amax);
     const float inv = ldexpf(1.0f, -e);
     const uint32_t c = cvt_e4m3x2(h[0] * inv, h[1] * inv);
-    *(uint16_t *)(hq + r * F + f) = (uint16_t)c;
-    if (lane == 0) hs[r * nfb + fb] = ldexpf(1.0f, e);
+    stc16<COH>((uint16_t *)hq, (size_t)((r * F + f) / 2), (uint16_t)c);
+    if (lane == 0) stc<COH>(hs + r * nfb + fb, ldexpf(1.0f, e));
 }
 
 }  // namespace moe

@@ -68,18 +68,35 @@ hipError_t launch_combine(const Shape &s, const void *y_perm, const int32_t *slo
 // only on items with smaller numbers, through counters in the workspace, so every wait
 // ends once the grid is resident.
 
-enum SyncWord {
-    SYNC_QUANT = 0,  // FP8 activation items done
-    SYNC_ROUTE,      // router items done
-    SYNC_SELECT,     // split-K router: tokens selected
-    SYNC_COUNT,      // dispatch histogram blocks done
-    SYNC_PLAN,       // scan and tile plans published
-    SYNC_SCATTER,    // dispatch scatter blocks done
-    SYNC_LIN1,       // linear1 items done (fp32 path)
-    SYNC_LIN2,       // linear2 items done
-    SYNC_EXIT,       // workgroups finished (the last one clears every word)
-    SYNC_WORDS = 16
+// Synchronisation words, in a workspace region of kSyncInts ints that must be zero before
+// the first launch (every launch leaves it zero).  Same-address atomics serialise at the
+// memory (about 12 ns each on MI355X), so a counter bumped by many items is spread over
+// kSpread sub-counters, and a flag polled by many waves is written to kSpread replicas;
+// every one sits in its own 128-byte slot.
+constexpr int kSpread = 64;
+constexpr int kSlot = 32;  // ints per 128-byte slot
+enum SyncCounter {
+    CNT_QUANT = 0,  // FP8 activation items done
+    CNT_ROUTE,      // router items done
+    CNT_SELECT,     // split-K router: tokens selected
+    CNT_COUNT,      // dispatch histogram blocks done
+    CNT_SCATTER,    // dispatch scatter blocks done
+    CNT_LIN1,       // tiled path: workgroups past linear1
+    CNT_LIN2,       // linear2 items (decode) or workgroups past linear2 (tiled) done
+    CNT_EXIT,       // workgroups finished
+    NUM_COUNTERS
 };
+enum SyncFlag {
+    FLAG_PLAN = 0,  // scan and tile plans published
+    FLAG_FRONT,     // everything before linear1 done: activations, plan, permutation
+    NUM_FLAGS
+};
+constexpr int kSyncTopExit = (NUM_COUNTERS + NUM_FLAGS) * kSpread * kSlot;  // single counters
+constexpr int kSyncTopScatter = kSyncTopExit + kSlot;
+constexpr size_t kSyncInts = (size_t)kSyncTopScatter + kSlot;
+// decode path, per 32-row tile: 8 sub-counters of its linear1 items, their top counter,
+// and 8 replicas of its "h ready" flag
+constexpr int kRowTileSlots = 17;
 
 enum RouterKind { ROUTER_SPLITK = 0, ROUTER_MFMA = 1, ROUTER_VALU8 = 2, ROUTER_VALU32 = 3 };
 
@@ -104,7 +121,7 @@ struct FusedArgs {
     int router, nks, nblk;
     int bm, ntn1, ntn2, ks;
     long rows;
-    int nm;   // row tiles bound (counters in done1)
+    int nm;   // row tiles bound (kRowTileSlots slots each in done1)
     // workgroup item ranges: [0, b_r) quant, [b_r, b_sel) router, [b_sel, b_cnt) select,
     // [b_cnt, b_plan) histogram, b_plan plan, [b_plan + 1, b_end) scatter, then the GEMMs
     long b_r, b_sel, b_cnt, b_plan, b_end;

@@ -11,7 +11,7 @@ __global__ __launch_bounds__(256) void route_valu_kernel(const void *__restrict_
                                                         int gating, int32_t *idx, float *gate, float *logits,
                                                         float *keys, int32_t *err) {
     extern __shared__ float lds_logits[];  // [4][E]
-    route_valu_block<F32, CH>(x, wr, bias, T, d, E, k, gating, blockIdx.x, lds_logits, idx, gate, logits, keys,
+    route_valu_block<F32, CH, false>(x, wr, bias, T, d, E, k, gating, blockIdx.x, lds_logits, idx, gate, logits, keys,
                               err);
 }
 
@@ -21,14 +21,14 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const uint16_t *__restr
                                                         int gating, int32_t *idx, float *gate, float *logits,
                                                         float *keys, int32_t *err) {
     extern __shared__ float lds_logits[];  // [32][E]
-    route_mfma_block(x, wr, bias, T, d, E, k, gating, blockIdx.x, lds_logits, idx, gate, logits, keys, err);
+    route_mfma_block<false>(x, wr, bias, T, d, E, k, gating, blockIdx.x, lds_logits, idx, gate, logits, keys, err);
 }
 
 // one wave per (expert tile, K slice, token tile)
 __global__ __launch_bounds__(64) void route_splitk_kernel(const uint16_t *__restrict__ x,
                                                          const uint16_t *__restrict__ wr, int T, int d, int E,
                                                          int nks, float *__restrict__ part) {
-    route_splitk_wave(x, wr, T, d, E, nks, blockIdx.x, part);
+    route_splitk_wave<false>(x, wr, T, d, E, nks, blockIdx.x, part);
 }
 
 // one workgroup per token
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float *__restri
                                                           int32_t *idx, float *gate, float *logits, float *keys,
                                                           int32_t *err) {
     extern __shared__ float lg[];  // [E]
-    route_sum_select(part, nks, T, E, k, gating, bias, blockIdx.x, lg, idx, gate, logits, keys, err);
+    route_sum_select<false>(part, nks, T, E, k, gating, bias, blockIdx.x, lg, idx, gate, logits, keys, err);
 }
 
 // Router work layout: the split-K path is used for few tokens (bf16, E a multiple of 32).

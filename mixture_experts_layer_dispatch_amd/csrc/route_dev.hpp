@@ -23,6 +23,7 @@ __device__ __forceinline__ float sigmoidf_(float l) { return 1.0f / (1.0f + expf
 
 // One wave selects the top-k of token t whose E logits sit in LDS (lg[0..E)).
 // Keys for expert e live in lane e % 64, slot e / 64.
+template <bool COH>
 __device__ __forceinline__ void select_token(const float *lg, int E, int k, int gating, const float *bias, long t,
                                              int32_t *idx, float *gate, float *logits, float *keys, int32_t *err) {
     const int lane = lane_id();
@@ -91,8 +92,8 @@ __device__ __forceinline__ void select_token(const float *lg, int E, int k, int 
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j)
         if (j < k && lane == j) {
-            idx[t * k + j] = sel[j];
-            gate[t * k + j] = v[j] / sum;
+            stc<COH>(idx + t * k + j, sel[j]);
+            stc<COH>(gate + t * k + j, v[j] / sum);
         }
 }
 
@@ -147,7 +148,7 @@ __device__ __forceinline__ void route_valu_token(const void *__restrict__ xv, co
 }
 
 // 256 threads: tokens 4 b .. 4 b + 3, one wave each; lds holds [4][E] floats.
-template <bool F32, int CH>
+template <bool F32, int CH, bool COH>
 __device__ __forceinline__ void route_valu_block(const void *x, const void *wr, const float *bias, int T, int d,
                                                  int E, int k, int gating, int b, float *lds, int32_t *idx,
                                                  float *gate, float *logits, float *keys, int32_t *err) {
@@ -156,7 +157,7 @@ __device__ __forceinline__ void route_valu_block(const void *x, const void *wr, 
     float *lg = lds + wave * E;
     if (t < T) route_valu_token<F32, CH>(x, wr, d, E, t, lg);
     __syncthreads();
-    if (t < T) select_token(lg, E, k, gating, bias, t, idx, gate, logits, keys, err);
+    if (t < T) select_token<COH>(lg, E, k, gating, bias, t, idx, gate, logits, keys, err);
 }
 
 // ---- MFMA router (bf16, E a multiple of 32): 32 tokens per workgroup ----------
@@ -165,9 +166,10 @@ __device__ __forceinline__ void route_valu_block(const void *x, const void *wr, 
 // B[k 8*(l/32)..+8][col l%32]; result register r of lane l is
 // C[row 8*(r/4) + 4*(l/32) + r%4][col l%32].  Rows are tokens, columns experts.
 constexpr int kRouteTok = 32;
-constexpr int kRouteMaxNT = 8;  // n-tiles (32 experts) per wave: E <= 1024 over 4 waves
 
-// 256 threads: tokens 32 b .. 32 b + 31; lds holds [32][E] floats.
+// 256 threads: tokens 32 b .. 32 b + 31; lds holds [32][E] floats.  Passes of 8 expert
+// tiles: wave w owns tiles p + w and p + w + 4 of pass p (two accumulators).
+template <bool COH>
 __device__ __forceinline__ void route_mfma_block(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
                                                  const float *__restrict__ bias, int T, int d, int E, int k,
                                                  int gating, int b, float *lds, int32_t *idx, float *gate,
@@ -178,51 +180,46 @@ __device__ __forceinline__ void route_mfma_block(const uint16_t *__restrict__ x,
     long trow = t0 + (lane & 31);
     if (trow >= T) trow = T - 1;
     const uint16_t *xa = x + trow * d + 8 * (lane >> 5);
-    const uint16_t *wb[kRouteMaxNT];
-    f32x16 acc[kRouteMaxNT];
-    int my = 0;
+    for (int p = 0; p < ntile; p += 8) {
+        const int nt0 = p + wave, nt1 = p + wave + 4;
+        const bool has0 = nt0 < ntile, has1 = nt1 < ntile;
+        const uint16_t *wb0 = wr + (long)((has0 ? nt0 : 0) * 32 + (lane & 31)) * d + 8 * (lane >> 5);
+        const uint16_t *wb1 = wr + (long)((has1 ? nt1 : 0) * 32 + (lane & 31)) * d + 8 * (lane >> 5);
+        f32x16 acc0 = (f32x16){}, acc1 = (f32x16){};
+        if (has0) {
+            for (int k0 = 0; k0 < d; k0 += 64) {
+                uint4 av[4], bv[4];
 #pragma unroll
-    for (int i = 0; i < kRouteMaxNT; ++i) {
-        int nt = wave + 4 * i;
-        wb[i] = wr + (long)((nt < ntile ? nt : 0) * 32 + (lane & 31)) * d + 8 * (lane >> 5);
-        acc[i] = (f32x16){};
-        if (nt < ntile) my = i + 1;
-    }
-    if (my > 0) {
-        for (int k0 = 0; k0 < d; k0 += 64) {
-            uint4 av[4];
+                for (int u = 0; u < 4; ++u) {
+                    av[u] = *(const uint4 *)(xa + k0 + 16 * u);
+                    bv[u] = *(const uint4 *)(wb0 + k0 + 16 * u);
+                }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) av[u] = *(const uint4 *)(xa + k0 + 16 * u);
+                for (int u = 0; u < 4; ++u)
+                    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[u]),
+                                                                   __builtin_bit_cast(bf16x8, bv[u]), acc0, 0, 0, 0);
+                if (has1) {
 #pragma unroll
-            for (int i = 0; i < kRouteMaxNT; ++i) {
-                if (i < my) {
-                    uint4 bv[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) bv[u] = *(const uint4 *)(wb[i] + k0 + 16 * u);
+                    for (int u = 0; u < 4; ++u) bv[u] = *(const uint4 *)(wb1 + k0 + 16 * u);
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
-                        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[u]),
-                                                                         __builtin_bit_cast(bf16x8, bv[u]), acc[i],
-                                                                         0, 0, 0);
+                        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[u]),
+                                                                       __builtin_bit_cast(bf16x8, bv[u]), acc1, 0, 0,
+                                                                       0);
                 }
             }
         }
-    }
 #pragma unroll
-    for (int i = 0; i < kRouteMaxNT; ++i) {
-        int nt = wave + 4 * i;
-        if (nt < ntile) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                int row = 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-                lds[row * E + nt * 32 + (lane & 31)] = acc[i][r];
-            }
+        for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+            if (has0) lds[row * E + nt0 * 32 + (lane & 31)] = acc0[r];
+            if (has1) lds[row * E + nt1 * 32 + (lane & 31)] = acc1[r];
         }
     }
     __syncthreads();
     for (int tr = wave; tr < kRouteTok; tr += 4) {
         long t = t0 + tr;
-        if (t < T) select_token(lds + tr * E, E, k, gating, bias, t, idx, gate, logits, keys, err);
+        if (t < T) select_token<COH>(lds + tr * E, E, k, gating, bias, t, idx, gate, logits, keys, err);
     }
 }
 
@@ -232,6 +229,7 @@ __device__ __forceinline__ void route_mfma_block(const uint16_t *__restrict__ x,
 // token tile) waves streams W_r once across the whole chip.  Partial logits land in
 // part[ks][t][e] and route_sum_select adds them in ks order (fixed, so deterministic).
 // Wave item w = (tt * nks + ks) * (E / 32) + et.
+template <bool COH>
 __device__ __forceinline__ void route_splitk_wave(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
                                                   int T, int d, int E, int nks, long w, float *__restrict__ part) {
     const int lane = lane_id();
@@ -261,29 +259,34 @@ __device__ __forceinline__ void route_splitk_wave(const uint16_t *__restrict__ x
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         long t = tt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (t < T) part[((long)ks * T + t) * E + et * 32 + (lane & 31)] = acc[r];
+        if (t < T) stc<COH>(part + ((long)ks * T + t) * E + et * 32 + (lane & 31), acc[r]);
     }
 }
 
-// 256 threads, token t: thread e adds expert e's K slices in slice order (unconditional,
-// clamped loads: a load under a branch would be waited for before the branch joins,
-// serialising the slices), then wave 0 selects.  lg: E floats of LDS.
+// 256 threads, token t: thread e adds expert e's K slices in slice order, 16 loads in
+// flight at a time (unconditional, clamped loads: a load under a branch would be waited
+// for before the branch joins, serialising the slices); then wave 0 selects.  lg: E
+// floats of LDS.
+template <bool COH>
 __device__ __forceinline__ void route_sum_select(const float *__restrict__ part, int nks, int T, int E, int k,
                                                  int gating, const float *__restrict__ bias, long t, float *lg,
                                                  int32_t *idx, float *gate, float *logits, float *keys,
                                                  int32_t *err) {
+    constexpr int CH = 16;
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        float v[64];
-#pragma unroll
-        for (int q = 0; q < 64; ++q) v[q] = part[((long)(q < nks ? q : nks - 1) * T + t) * E + e];
         float s = 0.0f;
+        for (int q0 = 0; q0 < nks; q0 += CH) {
+            float v[CH];
 #pragma unroll
-        for (int q = 0; q < 64; ++q)
-            if (q < nks) s += v[q];
+            for (int q = 0; q < CH; ++q) v[q] = ldc<COH>(part + ((long)min(q0 + q, nks - 1) * T + t) * E + e);
+#pragma unroll
+            for (int q = 0; q < CH; ++q)
+                if (q0 + q < nks) s += v[q];
+        }
         lg[e] = s;
     }
     __syncthreads();
-    if (threadIdx.x < kWave) select_token(lg, E, k, gating, bias, t, idx, gate, logits, keys, err);
+    if (threadIdx.x < kWave) select_token<COH>(lg, E, k, gating, bias, t, idx, gate, logits, keys, err);
 }
 
 }  // namespace moe
