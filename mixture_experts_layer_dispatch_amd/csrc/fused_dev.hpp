@@ -56,9 +56,9 @@ __device__ __forceinline__ int atomic_add(int32_t *p, int v) {
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
 // Lane 0 spins until *p >= target, or until a timeout is (or was) reported.  The sleep
-// between polls doubles up to MAXSLEEP x 8 x 64 cycles: a thousand workgroups polling
-// one word at full rate would starve the memory channel that serves it, and with it the
-// very producers they wait for.
+// between polls doubles up to MAXSLEEP x 8 x 64 cycles: many waves polling one word at
+// full rate would starve the memory channel that serves it, and with it the very
+// producers they wait for; a word with few pollers keeps a short sleep (low latency).
 template <int MAXSLEEP>
 __device__ __forceinline__ void spin_until(const int32_t *p, int target, int32_t *err) {
     if (lane_id() == 0 && atomic_ld(p) < target) {
@@ -98,6 +98,7 @@ __device__ __forceinline__ int counter_sum(int32_t *sync, int c) {
 
 // The calling wave polls a spread counter until its sum reaches target (bounded, with
 // the same back-off as spin_until).
+template <int MAXSLEEP>
 __device__ __forceinline__ void counter_wait(int32_t *sync, int c, int target, int32_t *err) {
     if (counter_sum(sync, c) < target) {
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -111,7 +112,7 @@ __device__ __forceinline__ void counter_wait(int32_t *sync, int c, int target, i
                 }
             }
             for (int z = 0; z < backoff; ++z) __builtin_amdgcn_s_sleep(8);
-            backoff = backoff < 16 ? 2 * backoff : 16;
+            backoff = backoff < MAXSLEEP ? 2 * backoff : MAXSLEEP;
         }
     }
     compiler_fence();
@@ -133,13 +134,16 @@ __device__ __forceinline__ void wg_count(int32_t *sync, int c, long id) {
     __syncthreads();
     if (threadIdx.x == 0) atomic_add(counter_sub(sync, c, id), 1);
 }
+// (the steps before the GEMMs have a few waiting workgroups: a short sleep by default)
+template <int MAXSLEEP = 1>
 __device__ __forceinline__ void wg_counter_wait(int32_t *sync, int c, int target, int32_t *err) {
-    if (threadIdx.x < kWave) counter_wait(sync, c, target, err);
+    if (threadIdx.x < kWave) counter_wait<MAXSLEEP>(sync, c, target, err);
     __syncthreads();
     compiler_fence();
 }
+// (every workgroup polls: kSpread replicas keep each word to a few pollers)
 __device__ __forceinline__ void wg_flag_wait(int32_t *sync, int f, int32_t *err) {
-    if (threadIdx.x < kWave) spin_until<16>(flag_replica(sync, f, blockIdx.x), 1, err);
+    if (threadIdx.x < kWave) spin_until<2>(flag_replica(sync, f, blockIdx.x), 1, err);
     __syncthreads();
     compiler_fence();
 }
@@ -158,8 +162,9 @@ __device__ __forceinline__ void wg_release_count(int32_t *sync, int c) {
     __syncthreads();
     if (threadIdx.x == 0) atomic_add(counter_sub(sync, c, blockIdx.x), 1);
 }
+// (every workgroup waits: the long sleep)
 __device__ __forceinline__ void wg_counter_wait_acquire(int32_t *sync, int c, int target, int32_t *err) {
-    wg_counter_wait(sync, c, target, err);
+    wg_counter_wait<16>(sync, c, target, err);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
@@ -373,47 +378,62 @@ __device__ __forceinline__ void fused_decode(const FusedArgs &a, uint8_t *lds) {
     }
     __syncthreads();
     const long N1 = lts1[G], N2 = lts2[G];
-    const long e1 = N1, e2 = e1 + N2, e3 = e2 + a.ncb;
+    const int nfb = a.F / 128;
+    const long MT = N1 / a.ntn1;  // row tiles
+    const long e1 = N1, es = e1 + MT * nfb, e2 = es + N2, e3 = e2 + a.ncb;
     const int lane = lane_id();
     bool lin2_all = false;
     const DecArgs d1 = {a.xq, a.xs, a.r2s, a.offsets, a.ts1, (const uint8_t *)a.w1, (const uint8_t *)a.w1s,
                         a.upart, nullptr, a.rows, a.T, a.k, a.d, 2 * a.F, G, a.ks};
     const DecArgs d2 = {(const uint8_t *)a.h, a.hs, nullptr, a.offsets, a.ts2, (const uint8_t *)a.w2,
                         (const uint8_t *)a.w2s, nullptr, (uint16_t *)a.yperm, a.rows, a.T, a.k, a.F, a.d, G, 1};
-    const int nfb = a.F / 128;
+    auto row_tile = [&](long m) { return a.done1 + m * kRowTileSlots * kSlot; };
     for (long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6); w < e3; w += 4 * P) {
         if (w < e1) {  // linear1 K slice of a (32 rows x 32 columns) tile
             const int tile = (int)w;
             fp8_decode_tile<true, true>(d1, tile, lts1, loffs);
             const TileInfo ti = decode_tile(tile, lts1, loffs, G, 32);
-            int32_t *rt = a.done1 + (long)(lts1[ti.g] / a.ntn1 + ti.mt) * kRowTileSlots * kSlot;
-            // two-level count of this row tile's linear1 items: sub-counter (item % 8), then top
+            int32_t *rt = row_tile(lts1[ti.g] / a.ntn1 + ti.mt);
+            // two-level count of this row tile's linear1 items: sub-counter (item % 8), then
+            // top; the last one opens the tile's SwiGLU blocks
             wait_vmcnt<0>();
             compiler_fence();
             int done = 0;
             if (lane == 0 && atomic_add(rt + (ti.nt % 8) * kSlot, 1) == a.ntn1 / 8 - 1)
                 done = atomic_add(rt + 8 * kSlot, 1) == 7;
-            if (__shfl(done, 0, kWave)) {
-                // last slice of this row tile: SwiGLU + e4m3 for its rows, then open it to linear2
-                for (long q = 0; q < (long)ti.nrows * nfb; ++q)
-                    decode_swiglu_wave<true>(a.upart, a.rows, a.F, a.ks, (uint8_t *)a.h, a.hs,
-                                             (long)ti.row0 * nfb + q);
-                wait_vmcnt<0>();
-                compiler_fence();
-                if (lane < 8) __hip_atomic_store(rt + (9 + lane) * kSlot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (__shfl(done, 0, kWave) && lane < 8)
+                __hip_atomic_store(rt + (9 + lane) * kSlot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (w < es) {  // SwiGLU + e4m3 of one 128-column block of a row tile
+            const long m = (w - e1) / nfb;
+            const int fb = (int)((w - e1) % nfb);
+            int lo = 0, hi = G - 1;  // group of row tile m
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (lts1[mid] <= m * a.ntn1) lo = mid; else hi = mid - 1;
             }
+            const int mt = (int)(m - lts1[lo] / a.ntn1);
+            const int row0 = loffs[lo] + 32 * mt, nrows = min(32, loffs[lo + 1] - loffs[lo] - 32 * mt);
+            int32_t *rt = row_tile(m);
+            spin_until<2>(rt + (9 + (int)(w % 8)) * kSlot, 1, a.err);
+            for (int r = 0; r < nrows; ++r)
+                decode_swiglu_wave<true>(a.upart, a.rows, a.F, a.ks, (uint8_t *)a.h, a.hs, (long)(row0 + r) * nfb + fb);
+            wait_vmcnt<0>();
+            compiler_fence();
+            int done = 0;
+            if (lane == 0) done = atomic_add(rt + 17 * kSlot, 1) == nfb - 1;
+            if (__shfl(done, 0, kWave) && lane < 8)
+                __hip_atomic_store(rt + (18 + lane) * kSlot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else if (w < e2) {  // linear2 tile
-            const int tile = (int)(w - e1);
+            const int tile = (int)(w - es);
             const TileInfo ti = decode_tile(tile, lts2, loffs, G, 32);
-            const int32_t *rt = a.done1 + (long)(lts2[ti.g] / a.ntn2 + ti.mt) * kRowTileSlots * kSlot;
-            spin_until<16>(rt + (9 + w % 8) * kSlot, 1, a.err);
+            spin_until<4>(row_tile(lts2[ti.g] / a.ntn2 + ti.mt) + (18 + (int)(w % 8)) * kSlot, 1, a.err);
             fp8_decode_tile<false, true>(d2, tile, lts2, loffs);
             wait_vmcnt<0>();
             compiler_fence();
             if (lane == 0) atomic_add(counter_sub(a.sync, CNT_LIN2, w), 1);
         } else {  // combine: 64 lanes x 8 columns
             if (!lin2_all) {
-                counter_wait(a.sync, CNT_LIN2, (int)N2, a.err);
+                counter_wait<4>(a.sync, CNT_LIN2, (int)N2, a.err);
                 lin2_all = true;
             }
             // y_perm lines are written by two linear2 tiles each, all finished before this read

@@ -29,8 +29,7 @@ struct Shape {
 };
 
 // router: logits, keys, top-k, gates.  part: fp32 scratch of route_splitk_slices(s) * T * E
-// partial logits (few-token split-K path), or nullptr to always use the one-pass kernels.
-constexpr int kRouteSplitMaxT = 128;
+// partial logits (split-K path), or nullptr to always use the one-pass kernels.
 int route_splitk_slices(const Shape &s);
 long route_splitk_waves(const Shape &s, int nks);
 hipError_t launch_route(const Shape &s, const void *x, const void *wr, const float *bias, int32_t *idx,
@@ -94,9 +93,10 @@ enum SyncFlag {
 constexpr int kSyncTopExit = (NUM_COUNTERS + NUM_FLAGS) * kSpread * kSlot;  // single counters
 constexpr int kSyncTopScatter = kSyncTopExit + kSlot;
 constexpr size_t kSyncInts = (size_t)kSyncTopScatter + kSlot;
-// decode path, per 32-row tile: 8 sub-counters of its linear1 items, their top counter,
-// and 8 replicas of its "h ready" flag
-constexpr int kRowTileSlots = 17;
+// decode path, per 32-row tile: 8 sub-counters of its linear1 items (slots 0-7), their
+// top counter (8), 8 replicas of its "partial sums ready" flag (9-16), the counter of its
+// SwiGLU blocks (17) and 8 replicas of its "h ready" flag (18-25)
+constexpr int kRowTileSlots = 26;
 
 enum RouterKind { ROUTER_SPLITK = 0, ROUTER_MFMA = 1, ROUTER_VALU8 = 2, ROUTER_VALU32 = 3 };
 

@@ -40,13 +40,16 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float *__restri
     route_sum_select<false>(part, nks, T, E, k, gating, bias, blockIdx.x, lg, idx, gate, logits, keys, err);
 }
 
-// Router work layout: the split-K path is used for few tokens (bf16, E a multiple of 32).
+// Router work layout: bf16 activations with E a multiple of 32 use the split-K kernel at
+// every T -- one wave per (32 tokens, 32 experts, K slice), with as many K slices (whole
+// multiples of 64) as keep the waves near 2048, so that even a few tokens spread W_r over
+// the whole chip.  fp32 or other E: the one-pass VALU kernel.
 int route_splitk_slices(const Shape &s) {
-    if (s.mode == MODE_F32 || s.E % 32 != 0 || s.T > kRouteSplitMaxT || s.T == 0) return 0;
-    const int tiles = (s.E / 32) * ((s.T + 31) / 32);
+    if (s.mode == MODE_F32 || s.E % 32 != 0 || s.T == 0) return 0;
+    const long tiles = (long)(s.E / 32) * ((s.T + 31) / 32);
     int best = 1;
-    for (int q = 1; q <= 64; ++q)  // slices of K: a multiple of 64 each, ~512 waves in all
-        if (s.d % (64 * q) == 0 && tiles * q <= 512) best = q;
+    for (int q = 1; q <= 64; ++q)
+        if (s.d % (64 * q) == 0 && tiles * q <= 2048) best = q;
     return best;
 }
 

@@ -16,85 +16,99 @@
 
 namespace moe {
 
-constexpr int kMaxKeysPerLane = 16;  // E <= 1024 over 64 lanes
-constexpr int kMaxK = 16;
 
 __device__ __forceinline__ float sigmoidf_(float l) { return 1.0f / (1.0f + expf(-l)); }
 
-// One wave selects the top-k of token t whose E logits sit in LDS (lg[0..E)).
-// Keys for expert e live in lane e % 64, slot e / 64.
-template <bool COH>
-__device__ __forceinline__ void select_token(const float *lg, int E, int k, int gating, const float *bias, long t,
-                                             int32_t *idx, float *gate, float *logits, float *keys, int32_t *err) {
+// Order-preserving 64-bit key: the float key's bits mapped so that unsigned order is float
+// order (-0 taken as +0, so the two compare equal), then the complemented expert index, so
+// that the larger of two packed keys is the larger key and, on equal keys, the lower expert
+// index.  0 lies below every real key.
+__device__ __forceinline__ uint64_t pack_key(float key, int e) {
+    uint32_t u = __float_as_uint(key == 0.0f ? 0.0f : key);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)e;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)v, m, kWave), hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// One wave selects the top-k of token t whose E logits sit in LDS (lg[0..E)); expert e
+// lives in lane e % 64, slot e / 64 (NPER slots per lane).  Each of the k rounds takes the
+// wave-wide maximum of the packed keys -- a stable descending order with ties to the lower
+// expert index -- and lane j keeps the j-th choice, then works out its gate.
+template <int NPER, bool COH>
+__device__ __forceinline__ void select_token_n(const float *lg, int E, int k, int gating, const float *bias, long t,
+                                               int32_t *idx, float *gate, float *logits, float *keys,
+                                               int32_t *err) {
     const int lane = lane_id();
-    const int nper = (E + kWave - 1) / kWave;
-    float key[kMaxKeysPerLane];
-    uint32_t taken = 0;  // bit i: slot i unavailable
+    uint64_t pk[NPER];
     bool bad = false;
 #pragma unroll
-    for (int i = 0; i < kMaxKeysPerLane; ++i) {
-        int e = lane + kWave * i;
-        key[i] = -INFINITY;
-        if (i < nper && e < E) {
-            float l = lg[e];
-            float s = gating == GATE_SIGMOID ? sigmoidf_(l) : l;
-            float kk = s + (bias ? bias[e] : 0.0f);
-            key[i] = kk;
+    for (int i = 0; i < NPER; ++i) {
+        const int e = lane + kWave * i;
+        pk[i] = 0;
+        if (e < E) {
+            const float l = lg[e];
+            const float s = gating == GATE_SIGMOID ? sigmoidf_(l) : l;
+            const float kk = s + (bias ? bias[e] : 0.0f);
             bad |= !isfinite(kk);
             if (logits) logits[t * E + e] = l;
             if (keys) keys[t * E + e] = kk;
-        } else {
-            taken |= 1u << i;
+            pk[i] = pack_key(kk, e);
         }
     }
     if (__any(bad) && lane == 0) set_error(err, DEVERR_NONFINITE);
 
-    int sel[kMaxK];
+    int mine = 0;  // lane j < k: the j-th choice
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = pk[0];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-        sel[j] = 0;
-        if (j < k) {
-            float bk = -INFINITY;
-            int bi = 0x7fffffff;
+        for (int i = 1; i < NPER; ++i) best = pk[i] > best ? pk[i] : best;
+        best = wave_max_u64(best);
+        // only non-finite keys leave nothing above 0 (an error already reported): expert 0
+        const int e = best ? (int)~(uint32_t)best : 0;
 #pragma unroll
-            for (int i = 0; i < kMaxKeysPerLane; ++i) {
-                int e = lane + kWave * i;
-                bool ok = !(taken >> i & 1u);
-                if (ok && (key[i] > bk || (key[i] == bk && e < bi))) { bk = key[i]; bi = e; }
-            }
-#pragma unroll
-            for (int m = 32; m >= 1; m >>= 1) {
-                float ok_ = __shfl_xor(bk, m, kWave);
-                int oi = __shfl_xor(bi, m, kWave);
-                if (ok_ > bk || (ok_ == bk && oi < bi)) { bk = ok_; bi = oi; }
-            }
-            if (bi == 0x7fffffff) bi = 0;  // only with non-finite keys (error already flagged)
-            if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
-            sel[j] = bi;
-        }
+        for (int i = 0; i < NPER; ++i)
+            if (lane + kWave * i == e) pk[i] = 0;
+        mine = lane == j ? e : mine;
     }
 
-    // gates from the unbiased scores of the chosen experts
-    float v[kMaxK];
-    float m = -INFINITY, sum = 0.0f;
+    // gates from the unbiased scores of the chosen experts (lanes 0 .. k-1)
+    const bool chosen = lane < k;
+    const float l = lg[chosen ? mine : 0];
+    float v;
     if (gating == GATE_SIGMOID) {
-#pragma unroll
-        for (int j = 0; j < kMaxK; ++j)
-            if (j < k) { v[j] = sigmoidf_(lg[sel[j]]); sum += v[j]; }
+        v = chosen ? sigmoidf_(l) : 0.0f;
     } else {
+        float m = chosen ? l : -INFINITY;
 #pragma unroll
-        for (int j = 0; j < kMaxK; ++j)
-            if (j < k) m = fmaxf(m, lg[sel[j]]);
-#pragma unroll
-        for (int j = 0; j < kMaxK; ++j)
-            if (j < k) { v[j] = expf(lg[sel[j]] - m); sum += v[j]; }
+        for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, kWave));
+        v = chosen ? expf(l - m) : 0.0f;
     }
+    float sum = v;
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-        if (j < k && lane == j) {
-            stc<COH>(idx + t * k + j, sel[j]);
-            stc<COH>(gate + t * k + j, v[j] / sum);
-        }
+    for (int s = 32; s >= 1; s >>= 1) sum += __shfl_xor(sum, s, kWave);
+    if (chosen) {
+        stc<COH>(idx + t * k + lane, mine);
+        stc<COH>(gate + t * k + lane, v / sum);
+    }
+}
+
+template <bool COH>
+__device__ __forceinline__ void select_token(const float *lg, int E, int k, int gating, const float *bias, long t,
+                                             int32_t *idx, float *gate, float *logits, float *keys, int32_t *err) {
+    if (E <= 64) select_token_n<1, COH>(lg, E, k, gating, bias, t, idx, gate, logits, keys, err);
+    else if (E <= 128) select_token_n<2, COH>(lg, E, k, gating, bias, t, idx, gate, logits, keys, err);
+    else if (E <= 256) select_token_n<4, COH>(lg, E, k, gating, bias, t, idx, gate, logits, keys, err);
+    else if (E <= 512) select_token_n<8, COH>(lg, E, k, gating, bias, t, idx, gate, logits, keys, err);
+    else select_token_n<16, COH>(lg, E, k, gating, bias, t, idx, gate, logits, keys, err);
 }
 
 // ---- VALU router: one wave per token (small E, or fp32 activations) ----------
