@@ -7,10 +7,17 @@ seeded synthetic tokens with random-init weights of the workload's shape, all
 resident in HBM before timing starts.  The default workload is the
 Mixtral-shaped bf16 layer (T=4096, d=4096, E=8, k=2, F=14336).
 
+Both entry points compute the same layer: the persistent single-launch kernel
+(moe_layer_fused) and the chain of step kernels (route, dispatch, ffn, combine).  By
+default both are timed and the faster one gives the reported value; the JSON names it
+and carries both times.
+
 Prints one JSON line: whole-layer active TFLOP/s (value), tokens/s, the roofline
 of the dominant kernel (its algorithmic work over its mean duration, measured with
 HIP events on its own stream during a timed pass), and the CPU oracle's rate on a
-bounded token sample (cpu_baseline).
+bounded token sample (cpu_baseline).  roofline.traffic is the HBM traffic of that
+kernel from hardware counters (profiles/traffic.txt), reported only while the kernel
+sources still hash to the ones the counters were taken with.
 """
 from __future__ import annotations
 
@@ -42,7 +49,11 @@ def parse():
     ap.add_argument("--workload", default="mixtral_bf16",
                     help="tiny_f32 | mixtral_bf16 | dsv3_bf16 | dsv3_fp8fp4 | decode_fp8fp4")
     ap.add_argument("--T", type=int, default=None, help="tokens (default: the workload's)")
-    ap.add_argument("--path", choices=["fused", "unfused"], default="fused")
+    ap.add_argument("--path", choices=["best", "fused", "unfused"], default="best",
+                    help="entry point to report (best: time both, report the faster)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of this many MiB five times (the known-size "
+                         "kernel that scales the HBM byte counters) and exit")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-oracle sample budget")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--flush-mb", type=int, default=None,
@@ -85,10 +96,55 @@ def kernel_work(w, name, counts):
         return 2.0 * w.T * w.d * w.E, w.T * w.d * act + w.E * w.d * act + w.T * w.k * 8
     if name == "combine":
         return 2.0 * w.T * w.d * (w.k + w.S), rows * w.d * (4 if w.mode == "f32" else 2) + w.T * w.d * act
-    if name == "fused":
+    if name in ("fused", "layer_fused"):
         f_e, f_r = flops_of(w)
         return f_e + f_r, touched * (w1b + w2b) + w.E * w.d * act + 2 * w.T * w.d * act
     return 0.0, 0.0
+
+
+def sources_hash() -> str:
+    """Hash of the kernel sources, csrc/*.hip and *.hpp (hardware counters are valid for these only)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_layer_dispatch_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".hpp")))
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_of(w, kernel):
+    """HBM bytes per launch of `kernel` on workload w from profiles/traffic.txt: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch, mean over the kernel's dispatches) each scaled by the ratio of
+    known bytes to counter bytes for a plain copy.  None when absent or when the sources changed."""
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
+    if not os.path.exists(path):
+        return None
+    cur = sources_hash()
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("#") or "=" not in line:
+                continue
+            kv = dict(tok.split("=", 1) for tok in line.split() if "=" in tok)
+            if kv.get("workload") == w.name and int(kv.get("T", -1)) == w.T and kv.get("kernel") == kernel:
+                if kv.get("sources") != cur:
+                    return None
+                return (float(kv["fetch_kib"]) * float(kv["fetch_scale"]) +
+                        float(kv["write_kib"]) * float(kv["write_scale"])) * 1024.0
+    return None
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copied {mib} MiB five times (read {mib} MiB and write {mib} MiB per copy)")
 
 
 def main():
@@ -98,6 +154,10 @@ def main():
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr, flush=True)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import torch
     import mixture_experts_layer_dispatch_amd as moe
@@ -150,23 +210,21 @@ def main():
     def step_unfused():
         moe.layer_unfused(cfg, x, wr, w1, w2, w1s, w2s, bias, ws=ws)
 
-    step = step_fused if args.path == "fused" else step_unfused
+    steps_of = {"fused": step_fused, "unfused": step_unfused}
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    assert moe.read_device_error(cfg, ws) == 0, "device error during warm-up"
-
-    # ---- timed region ---------------------------------------------------------------
-    if flush_buf is None:
-        torch.cuda.synchronize()
-        ts = time.perf_counter()
-        for _ in range(args.steps):
+    def time_path(step):
+        """Warm-up, then exactly args.steps timed steps bracketed by synchronisations."""
+        for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
-        ms = (time.perf_counter() - ts) * 1e3 / args.steps
-        timing = "wall clock over the timed steps"
-    else:
+        assert moe.read_device_error(cfg, ws) == 0, "device error during warm-up"
+        if flush_buf is None:
+            torch.cuda.synchronize()
+            ts = time.perf_counter()
+            for _ in range(args.steps):
+                step()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - ts) * 1e3 / args.steps
         # a cache flush runs between steps, so each step is timed alone on the stream
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
@@ -177,9 +235,19 @@ def main():
             step()
             b.record()
         torch.cuda.synchronize()
-        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-        timing = f"HIP events around each step; {flush_mb} MiB read between steps to evict caches"
-    log(f"{args.path} step: {ms:.4f} ms")
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    # ---- timed region(s) --------------------------------------------------------------
+    timed = {}
+    for name in (("fused", "unfused") if args.path == "best" else (args.path,)):
+        timed[name] = time_path(steps_of[name])
+        log(f"{name} step: {timed[name]:.4f} ms")
+    path = min(timed, key=timed.get)
+    ms = timed[path]
+    step = steps_of[path]
+    timing = ("wall clock over the timed steps" if flush_buf is None else
+              f"HIP events around each step; {flush_mb} MiB read between steps to evict caches")
+    assert moe.read_device_error(cfg, ws) == 0, "device error during the timed steps"
 
     # ---- per-kernel timing (HIP events on the launch stream, same steps) ------------------
     moe.profile_report()
@@ -193,17 +261,6 @@ def main():
     moe.profile_enable(False)
     kernels = {n: {"launches_per_step": c / args.steps, "mean_ms": t / c} for n, (c, t) in prof.items()}
     log("kernels: " + ", ".join(f"{n} {v['mean_ms']:.4f}ms" for n, v in kernels.items()))
-
-    # the other path, for the fused / unfused ratio
-    other = step_unfused if args.path == "fused" else step_fused
-    for _ in range(3):
-        other()
-    torch.cuda.synchronize()
-    ts = time.perf_counter()
-    for _ in range(args.steps):
-        other()
-    torch.cuda.synchronize()
-    ms_other = (time.perf_counter() - ts) * 1e3 / args.steps
 
     counts_np = counts.cpu().numpy()
     f_exp, f_rt = flops_of(w)
@@ -227,7 +284,9 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": kf / (kms * 1e-3) / 1e12, "peak": peak_f, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    tr = traffic_of(w, dom)
+    roof["traffic"] = tr
+    roof["traffic_unit"] = "bytes per launch"
     roof["kernel"] = dom
     roof["work_per_launch"] = {"flop": kf, "bytes": kb}
 
@@ -267,14 +326,14 @@ def main():
         "dtype": {"f32": "f32", "bf16": "bf16", "fp8_mxfp4": "fp8e4m3 x mxfp4"}[w.mode],
         "data": "synthetic (seeded Philox4x32-10 normals; random-init weights of the workload's shape)",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "F": w.F, "n_shared": w.S,
-                   "gating": w.gating, "zipf_alpha": w.zipf_alpha, "path": args.path, "timing": timing},
+                   "gating": w.gating, "zipf_alpha": w.zipf_alpha, "path": path, "timing": timing},
         "tokens_per_s": tok_s,
         "active_tflop": {"experts": f_exp / 1e12, "router": f_rt / 1e12},
         "algorithmic_GBps": gbs,
         "hbm_frac": gbs / PEAK_HBM,
         "mfma_frac": tflops / peak_f,
-        "other_path_ms": ms_other,
-        "fused_speedup_vs_unfused": (ms_other / ms) if args.path == "fused" else (ms / ms_other),
+        "path_ms": timed,
+        "fused_speedup_vs_unfused": (timed["unfused"] / timed["fused"]) if len(timed) == 2 else None,
         "kernels": kernels,
         "experts_touched": touched,
         "max_group_rows": int(counts_np.max()),

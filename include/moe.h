@@ -132,7 +132,10 @@ moe_status moe_device_check(void);
 size_t moe_workspace_bytes(const moe_cfg *cfg);
 
 /*
- * Clears the sticky error word (stream-ordered).  Call once on a new workspace.
+ * Clears the sticky error word and the persistent kernel's synchronisation words
+ * (stream-ordered).  A workspace must be zero-filled, or cleared by this call, before
+ * its first moe_layer_fused; every moe_layer_fused launch leaves those words zero
+ * again (also after a timeout), so one clear per workspace suffices.
  */
 moe_status moe_clear_device_error(const moe_cfg *cfg, void *ws, size_t ws_bytes, hipStream_t stream);
 
@@ -152,7 +155,7 @@ moe_status moe_read_device_error(const moe_cfg *cfg, const void *ws, int32_t *co
  *  topk_gate [T, k] fp32 out: gates
  *  logits [T, E]    fp32 out or NULL: x W_r^T
  *  keys [T, E]      fp32 out or NULL: selection keys
- *  ws: workspace (only the error word is used).
+ *  ws: workspace (the error word and the split-K partial logits).
  */
 moe_status moe_route(const moe_cfg *cfg, const void *x, const void *w_router, const float *bias,
                      int32_t *topk_idx, float *topk_gate, float *logits, float *keys, void *ws,
@@ -202,8 +205,13 @@ moe_status moe_combine(const moe_cfg *cfg, const void *y_perm, const int32_t *sl
                        const float *topk_gate, void *y, hipStream_t stream);
 
 /*
- * The whole layer in one persistent launch: route, dispatch, linear1 + SwiGLU,
- * linear2 and combine, chained on device with bounded waits.  Bitwise equal to
+ * The whole layer in one persistent launch (Mega MoE wiki, "One-line definition":
+ * the dispatch -> linear1 -> SwiGLU -> linear2 -> combine chain as one kernel): route,
+ * dispatch, linear1 + SwiGLU, linear2 and combine, chained on device through
+ * counters in the workspace with bounded waits.  A cooperative launch of every
+ * workgroup the device (or cfg->cu_limit CUs) can hold at once; MOE_ERR_LAUNCH if the
+ * runtime cannot make it co-resident.  A wait that exceeds 2 s sets
+ * MOE_DEVERR_TIMEOUT and the call's outputs are then unspecified.  Bitwise equal to
  * moe_route -> moe_dispatch -> moe_ffn -> moe_combine on the same inputs.
  *  x [T, d], w_router [E, d], bias [E] or NULL, w: as above; y [T, d] out.
  *  topk_idx_out [T, k], topk_gate_out [T, k], counts_out [G]: optional copies (NULL to skip).
