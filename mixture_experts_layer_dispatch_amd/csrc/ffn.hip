@@ -21,6 +21,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     if (tile >= 0) bf16_tile<BM, BN, SWIGLU, GATHER>(a, tile, lds);
 }
 
+template <bool SWIGLU, bool GATHER>
+__global__ __launch_bounds__(512) void gemm_bf16_kernel8(GemmArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tile = pick_tile(blockIdx.x, a.tile_start[a.G]);
+    if (tile >= 0) bf16_tile8<SWIGLU, GATHER>(a, tile, lds);
+}
+
 __global__ __launch_bounds__(256) void ffn1_f32_kernel(const float *__restrict__ x, const int32_t *__restrict__ r2s,
                                                       const float *__restrict__ w1, const int32_t *__restrict__ offsets,
                                                       int G, int T, int k, int d, int F, long rows,
@@ -95,6 +102,21 @@ static hipError_t launch_gemm(const char *name, dim3 grid, const GemmArgs &a, hi
     return hipGetLastError();
 }
 
+// 256 x 256 tiles: the 8-wave kernel
+template <bool SWIGLU, bool GATHER>
+static hipError_t launch_gemm8(const char *name, dim3 grid, const GemmArgs &a, hipStream_t st) {
+    constexpr size_t lds = bf16_tile8_lds();
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void *)gemm_bf16_kernel8<SWIGLU, GATHER>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    MOE_LAUNCH(name, (gemm_bf16_kernel8<SWIGLU, GATHER>), grid, dim3(512), lds, st, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_fp8_ffn(const Shape &s, const FfnPlan &p, const uint8_t *w1, const uint8_t *w1s,
                           const uint8_t *w2, const uint8_t *w2s, const uint8_t *xq, const float *xs,
                           const int32_t *offsets, const int32_t *row_to_slot, uint8_t *h, float *hs, void *y_perm,
@@ -132,10 +154,10 @@ hipError_t launch_ffn(const Shape &s, const FfnPlan &p, const void *w1, const vo
     GemmArgs a2 = {(const uint16_t *)h, nullptr, (const uint16_t *)w2, (uint16_t *)y_perm, offsets, ts2,
                    s.T, s.k, s.F, s.d, s.d, G, s.F};
     hipError_t e;
-    if (p.bm1 == 256) e = launch_gemm<256, 256, true, true>("linear1", grid_for(p.bm1, ntn1), a1, st);
+    if (p.bm1 == 256) e = launch_gemm8<true, true>("linear1", grid_for(p.bm1, ntn1), a1, st);
     else e = launch_gemm<128, 256, true, true>("linear1", grid_for(p.bm1, ntn1), a1, st);
     if (e != hipSuccess) return e;
-    if (p.bm2 == 256 && p.bn2 == 256) e = launch_gemm<256, 256, false, false>("linear2", grid_for(p.bm2, ntn2), a2, st);
+    if (p.bm2 == 256 && p.bn2 == 256) e = launch_gemm8<false, false>("linear2", grid_for(p.bm2, ntn2), a2, st);
     else if (p.bn2 == 256) e = launch_gemm<128, 256, false, false>("linear2", grid_for(p.bm2, ntn2), a2, st);
     else if (p.bm2 == 256) e = launch_gemm<256, 128, false, false>("linear2", grid_for(p.bm2, ntn2), a2, st);
     else e = launch_gemm<128, 128, false, false>("linear2", grid_for(p.bm2, ntn2), a2, st);

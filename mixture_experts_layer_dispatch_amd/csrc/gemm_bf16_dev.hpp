@@ -221,6 +221,186 @@ __device__ __forceinline__ void bf16_tile(const GemmArgs &a, int tile, uint8_t *
     }
 }
 
+// ---- bf16 grouped GEMM, 8 waves on a 256 x 256 tile ------------------------------------
+//
+// Two waves per SIMD (512 threads), each owning a 128 x 64 block of 32x32 MFMA tiles
+// (linear1: 32 gate and the matching 32 up columns), so that one wave's MFMAs fill the
+// pipe while the other waits on LDS or a barrier.  BK = 32, NS = 5 LDS stages of 32 KB
+// (the whole 160 KB), all of them in flight: stage s is published by the barrier of pass
+// s - 1, so its DMA has NS - 1 passes to land.
+//
+// Each pass multiplies the k16 half h = 0 of stage kt (fragments in F0) while reading the
+// h = 1 fragments into F1, waits for its own loads, passes the one barrier (stage kt + 1
+// published, every wave done with stage kt), then multiplies F1 while reading the h = 0
+// fragments of stage kt + 1 into F0.  Measured on MI355X, a burst of 4 DMA instructions
+// per wave right after the barrier saturated the per-CU address path for ~400 cycles and
+// stalled both waves of a SIMD; each stage is therefore loaded in two halves of 2
+// instructions: its B rows in the first half of pass s - NS + 1 and its A rows in the
+// second half of pass s - NS, each into the buffer freed by the barrier of pass s - NS.
+// Fragment reads, DMAs and MFMAs are interleaved with scheduling group barriers.  The
+// accumulation order over k is that of bf16_tile, so results are identical bit for bit.
+//
+// One tile per call; lds holds bf16_tile8_lds() bytes; same caller contract as bf16_tile.
+constexpr size_t bf16_tile8_lds() { return 5 * (size_t)(256 + 256) * 64; }
+
+template <bool SWIGLU, bool GATHER>
+__device__ __forceinline__ void bf16_tile8(const GemmArgs &a, int tile, uint8_t *lds) {
+    constexpr int BM = 256, BN = 256, BK = 32, NS = 5;
+    constexpr int TM = 4, TN = 2;                          // wave block 128 x 64
+    constexpr int CPR = BK / 8, RPI = 64 / CPR;            // 16 rows per DMA instruction
+    constexpr int IA = BM / (8 * RPI), IB = BN / (8 * RPI);  // 2 + 2 DMA instructions per wave and stage
+    constexpr int PER = IA + IB;
+    constexpr int ROWB = BK * 2;
+    constexpr int STAGE = (BM + BN) * ROWB;
+    static_assert(IA == 2 && IB == 2, "interleave pattern assumes two A and two B instructions");
+
+    const TileInfo ti = decode_tile(tile, a.tile_start, a.offsets, a.G, BM);
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int lrow = lane / CPR, lphys = lane % CPR;
+
+    const uint16_t *pa[IA];
+#pragma unroll
+    for (int q = 0; q < IA; ++q) {
+        const int r = RPI * (wave * IA + q) + lrow;
+        const long grow = ti.row0 + (r < ti.nrows ? r : 0);
+        const long src = GATHER ? row_token(grow, a.row_to_slot, a.T, a.k) : grow;
+        pa[q] = a.A + src * a.K + ((lphys ^ swz_key<BK>(r)) * 8);
+    }
+    const int f0 = ti.nt * (BN / 2), n0 = ti.nt * BN;
+    const uint16_t *pb[IB];
+#pragma unroll
+    for (int q = 0; q < IB; ++q) {
+        const int r = RPI * (wave * IB + q) + lrow;
+        const long wrow = SWIGLU ? (r < BN / 2 ? f0 + r : a.F + f0 + r - BN / 2) : n0 + r;
+        pb[q] = a.B + ((long)ti.g * a.Ntot + wrow) * a.K + ((lphys ^ swz_key<BK>(r)) * 8);
+    }
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){};
+
+    int aoff[2][TM], boff[2][TN];
+    const int khalf = lane >> 5;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) aoff[h][i] = swz_off<BK>(wm * 128 + i * 32 + (lane & 31), h * 2 + khalf);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int base = SWIGLU ? (j == 0 ? wn * 32 : BN / 2 + wn * 32) : wn * 64 + j * 32;
+            boff[h][j] = BM * ROWB + swz_off<BK>(base + (lane & 31), h * 2 + khalf);
+        }
+    }
+    const int nk = a.K / BK;
+
+#define MOE_BARRIER()                          \
+    do {                                       \
+        asm volatile("" ::: "memory");         \
+        __builtin_amdgcn_s_barrier();          \
+        asm volatile("" ::: "memory");         \
+    } while (0)
+    // DMA of the A (resp. B) rows of stage s into buffer s % NS; past the last stage it
+    // re-reads the last one into a free buffer that is never read again
+#define MOE_DMA_A(s)                                                                             \
+    do {                                                                                         \
+        const int s_ = (s);                                                                      \
+        uint8_t *st_ = lds + (s_ % NS) * STAGE;                                                  \
+        const int ko_ = (s_ < nk ? s_ : nk - 1) * BK;                                            \
+        _Pragma("unroll") for (int q = 0; q < IA; ++q) lds_dma16(pa[q] + ko_, st_ + (wave * IA + q) * 1024); \
+    } while (0)
+#define MOE_DMA_B(s)                                                                             \
+    do {                                                                                         \
+        const int s_ = (s);                                                                      \
+        uint8_t *st_ = lds + (s_ % NS) * STAGE;                                                  \
+        const int ko_ = (s_ < nk ? s_ : nk - 1) * BK;                                            \
+        _Pragma("unroll") for (int q = 0; q < IB; ++q)                                           \
+            lds_dma16(pb[q] + ko_, st_ + BM * ROWB + (wave * IB + q) * 1024);                    \
+    } while (0)
+#define MOE_READ(F, s, h)                                                                        \
+    do {                                                                                         \
+        const uint8_t *st_ = lds + ((s) % NS) * STAGE;                                           \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i)                                           \
+            F[i] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(st_ + aoff[h][i]));               \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j)                                           \
+            F[TM + j] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(st_ + boff[h][j]));          \
+    } while (0)
+#define MOE_MMA(F)                                                                               \
+    do {                                                                                         \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i)                                           \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j)                                       \
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[i], F[TM + j], acc[i][j], 0, 0, 0); \
+    } while (0)
+    // per half pass: 8 MFMAs, 6 fragment reads and 2 DMA instructions, interleaved
+#define MOE_INTERLEAVE()                                                                         \
+    do {                                                                                         \
+        _Pragma("unroll") for (int r_ = 0; r_ < 2; ++r_) {                                       \
+            _Pragma("unroll") for (int q_ = 0; q_ < 3; ++q_) {                                   \
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                               \
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                               \
+            }                                                                                    \
+            __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                   \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
+        }                                                                                        \
+        __builtin_amdgcn_sched_barrier(0);                                                       \
+    } while (0)
+
+    bf16x8 F0[TM + TN], F1[TM + TN];
+    // prologue: stages 0 .. NS-2 whole and the A rows of stage NS-1; stage 0 published
+#pragma unroll
+    for (int s0 = 0; s0 < NS - 1; ++s0) {
+        MOE_DMA_A(s0);
+        MOE_DMA_B(s0);
+    }
+    MOE_DMA_A(NS - 1);
+    wait_vmcnt<(NS - 2) * PER + IA>();
+    MOE_BARRIER();
+    MOE_READ(F0, 0, 0);
+    wait_lgkmcnt0();
+    for (int kt = 0; kt < nk; ++kt) {
+        MOE_READ(F1, kt, 1);
+        MOE_DMA_B(kt + NS - 1);
+        MOE_MMA(F0);
+        MOE_INTERLEAVE();
+        wait_vmcnt<(NS - 2) * PER>();  // own loads of stage kt+1 landed (kt+2 .. kt+NS-1 may fly)
+        wait_lgkmcnt0();
+        MOE_BARRIER();
+        __builtin_amdgcn_sched_barrier(0);
+        MOE_DMA_A(kt + NS);
+        MOE_READ(F0, (kt + 1 < nk ? kt + 1 : kt), 0);  // the last pass re-reads a published stage
+        MOE_MMA(F1);
+        MOE_INTERLEAVE();
+        wait_lgkmcnt0();
+    }
+    wait_vmcnt<0>();
+#undef MOE_BARRIER
+#undef MOE_DMA_A
+#undef MOE_DMA_B
+#undef MOE_READ
+#undef MOE_MMA
+#undef MOE_INTERLEAVE
+
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+            if (row >= ti.nrows) continue;
+            const long grow = ti.row0 + row;
+            if (SWIGLU) {
+                const float gv = acc[i][0][r], uv = acc[i][1][r];
+                const float h = gv / (1.0f + __expf(-gv)) * uv;
+                a.C[grow * a.F + f0 + wn * 32 + (lane & 31)] = f32_to_bf16(h);
+            } else {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) a.C[grow * a.ldc + n0 + wn * 64 + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][r]);
+            }
+        }
+    }
+}
+
 // ---- fp32 path: one lane per output element ------------------------------------
 
 __device__ __forceinline__ int group_of_row(long r, const int32_t *__restrict__ offsets, int G) {
