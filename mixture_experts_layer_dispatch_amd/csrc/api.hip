@@ -5,6 +5,7 @@
 #include <mutex>
 
 #include "../../include/moe.h"
+
 #include "kernels.hpp"
 
 using namespace moe;

@@ -27,6 +27,28 @@ static hipError_t launch_fp8(const char *name, dim3 grid, const Fp8Args &a, hipS
     return hipGetLastError();
 }
 
+template <bool SWIGLU>
+__global__ __launch_bounds__(512) void gemm_fp8_kernel8(Fp8Args a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tile = pick_tile(blockIdx.x, a.tile_start[a.G]);
+    if (tile >= 0) fp8_tile8<SWIGLU ? 1 : 2, SWIGLU ? 8 : 4, SWIGLU, SWIGLU>(a, tile, lds);
+}
+
+// 256 x 256 tiles: the 8-wave kernel (linear1 gathers its rows, linear2 does not)
+template <bool SWIGLU>
+static hipError_t launch_fp8_8(const char *name, dim3 grid, const Fp8Args &a, hipStream_t st) {
+    constexpr size_t lds = fp8_tile8_lds();
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void *)gemm_fp8_kernel8<SWIGLU>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    MOE_LAUNCH(name, gemm_fp8_kernel8<SWIGLU>, grid, dim3(512), lds, st, a);
+    return hipGetLastError();
+}
+
 constexpr long kDecodeMaxWaves = 1L << 20;  // grid cap; the kernels stride over any excess tiles
 
 // The grid is an upper bound of the tile count (non-empty groups only), so a tail round of
@@ -83,10 +105,14 @@ hipError_t launch_fp8_ffn(const Shape &s, const FfnPlan &p, const uint8_t *w1, c
     Fp8Args a1 = {xq, xs, row_to_slot, w1, w1s, h, hs, offsets, ts1, s.T, s.k, s.d, 2 * s.F, s.F, G, s.F};
     Fp8Args a2 = {h, hs, nullptr, w2, w2s, y_perm, nullptr, offsets, ts2, s.T, s.k, s.F, s.d, s.d, G, s.F};
     hipError_t e;
-    if (p.bm1 == 256) e = launch_fp8<256, 256, 4, true, true>("linear1", grid_for(p.bm1, ntn1), a1, st);
+    // the 8-wave tiles address their A operand with 32-bit byte offsets
+    const bool a1_small = (long)s.T * s.d < (1L << 32), a2_small = rows * (long)s.F < (1L << 32);
+    if (p.bm1 == 256 && a1_small) e = launch_fp8_8<true>("linear1", grid_for(p.bm1, ntn1), a1, st);
+    else if (p.bm1 == 256) e = launch_fp8<256, 256, 4, true, true>("linear1", grid_for(p.bm1, ntn1), a1, st);
     else e = launch_fp8<128, 256, 4, true, true>("linear1", grid_for(p.bm1, ntn1), a1, st);
     if (e != hipSuccess) return e;
-    if (p.bm2 == 256 && p.bn2 == 256) e = launch_fp8<256, 256, 2, false, false>("linear2", grid_for(p.bm2, ntn2), a2, st);
+    if (p.bm2 == 256 && p.bn2 == 256 && a2_small) e = launch_fp8_8<false>("linear2", grid_for(p.bm2, ntn2), a2, st);
+    else if (p.bm2 == 256 && p.bn2 == 256) e = launch_fp8<256, 256, 2, false, false>("linear2", grid_for(p.bm2, ntn2), a2, st);
     else if (p.bn2 == 256) e = launch_fp8<128, 256, 2, false, false>("linear2", grid_for(p.bm2, ntn2), a2, st);
     else if (p.bm2 == 256) e = launch_fp8<256, 128, 2, false, false>("linear2", grid_for(p.bm2, ntn2), a2, st);
     else e = launch_fp8<128, 128, 2, false, false>("linear2", grid_for(p.bm2, ntn2), a2, st);

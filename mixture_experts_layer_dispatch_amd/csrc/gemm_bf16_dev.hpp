@@ -243,9 +243,13 @@ __device__ __forceinline__ void bf16_tile(const GemmArgs &a, int tile, uint8_t *
 // One tile per call; lds holds bf16_tile8_lds() bytes; same caller contract as bf16_tile.
 constexpr size_t bf16_tile8_lds() { return 5 * (size_t)(256 + 256) * 64; }
 
-template <bool SWIGLU, bool GATHER>
-__device__ __forceinline__ void bf16_tile8(const GemmArgs &a, int tile, uint8_t *lds) {
+// The core takes the tile's rows and N tile (ti), the row stride of A and B in elements
+// (lda), and the K range [k0, k0 + 32 nk).  F32OUT (not with SWIGLU) writes fp32 C.
+template <bool SWIGLU, bool GATHER, bool F32OUT>
+__device__ __forceinline__ void bf16_tile8_core(const GemmArgs &a, const TileInfo &ti, long lda, int k0, int nk,
+                                                uint8_t *lds) {
     constexpr int BM = 256, BN = 256, BK = 32, NS = 5;
+    static_assert(!(SWIGLU && F32OUT), "SwiGLU writes bf16 h");
     constexpr int TM = 4, TN = 2;                          // wave block 128 x 64
     constexpr int CPR = BK / 8, RPI = 64 / CPR;            // 16 rows per DMA instruction
     constexpr int IA = BM / (8 * RPI), IB = BN / (8 * RPI);  // 2 + 2 DMA instructions per wave and stage
@@ -254,7 +258,6 @@ __device__ __forceinline__ void bf16_tile8(const GemmArgs &a, int tile, uint8_t 
     constexpr int STAGE = (BM + BN) * ROWB;
     static_assert(IA == 2 && IB == 2, "interleave pattern assumes two A and two B instructions");
 
-    const TileInfo ti = decode_tile(tile, a.tile_start, a.offsets, a.G, BM);
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;
     const int lrow = lane / CPR, lphys = lane % CPR;
@@ -265,7 +268,7 @@ __device__ __forceinline__ void bf16_tile8(const GemmArgs &a, int tile, uint8_t 
         const int r = RPI * (wave * IA + q) + lrow;
         const long grow = ti.row0 + (r < ti.nrows ? r : 0);
         const long src = GATHER ? row_token(grow, a.row_to_slot, a.T, a.k) : grow;
-        pa[q] = a.A + src * a.K + ((lphys ^ swz_key<BK>(r)) * 8);
+        pa[q] = a.A + src * lda + k0 + ((lphys ^ swz_key<BK>(r)) * 8);
     }
     const int f0 = ti.nt * (BN / 2), n0 = ti.nt * BN;
     const uint16_t *pb[IB];
@@ -273,7 +276,7 @@ __device__ __forceinline__ void bf16_tile8(const GemmArgs &a, int tile, uint8_t 
     for (int q = 0; q < IB; ++q) {
         const int r = RPI * (wave * IB + q) + lrow;
         const long wrow = SWIGLU ? (r < BN / 2 ? f0 + r : a.F + f0 + r - BN / 2) : n0 + r;
-        pb[q] = a.B + ((long)ti.g * a.Ntot + wrow) * a.K + ((lphys ^ swz_key<BK>(r)) * 8);
+        pb[q] = a.B + ((long)ti.g * a.Ntot + wrow) * lda + k0 + ((lphys ^ swz_key<BK>(r)) * 8);
     }
 
     f32x16 acc[TM][TN];
@@ -294,7 +297,6 @@ __device__ __forceinline__ void bf16_tile8(const GemmArgs &a, int tile, uint8_t 
             boff[h][j] = BM * ROWB + swz_off<BK>(base + (lane & 31), h * 2 + khalf);
         }
     }
-    const int nk = a.K / BK;
 
 #define MOE_BARRIER()                          \
     do {                                       \
@@ -393,12 +395,22 @@ __device__ __forceinline__ void bf16_tile8(const GemmArgs &a, int tile, uint8_t 
                 const float gv = acc[i][0][r], uv = acc[i][1][r];
                 const float h = gv / (1.0f + __expf(-gv)) * uv;
                 a.C[grow * a.F + f0 + wn * 32 + (lane & 31)] = f32_to_bf16(h);
+            } else if (F32OUT) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    ((float *)a.C)[grow * a.ldc + n0 + wn * 64 + j * 32 + (lane & 31)] = acc[i][j][r];
             } else {
 #pragma unroll
                 for (int j = 0; j < TN; ++j) a.C[grow * a.ldc + n0 + wn * 64 + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][r]);
             }
         }
     }
+}
+
+template <bool SWIGLU, bool GATHER>
+__device__ __forceinline__ void bf16_tile8(const GemmArgs &a, int tile, uint8_t *lds) {
+    const TileInfo ti = decode_tile(tile, a.tile_start, a.offsets, a.G, 256);
+    bf16_tile8_core<SWIGLU, GATHER, false>(a, ti, a.K, 0, a.K / 32, lds);
 }
 
 // ---- fp32 path: one lane per output element ------------------------------------

@@ -320,6 +320,361 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args &a, int tile, uint8_t *ld
     }
 }
 
+// ---- 8 waves on a 256 x 256 tile ------------------------------------------------------
+//
+// Two waves per SIMD (512 threads), so one wave's MFMAs cover the other's LDS and barrier
+// waits.  linear1: each wave owns 32 rows x (128 gate + 128 up) columns, which keeps the
+// SwiGLU and h-quantisation epilogue inside the wave; linear2: 64 rows x 128 columns.
+// K advances 128 per stage (two k64 MFMA steps); NS = 3 stages of 50 KB (A codes 256 x 128,
+// B codes 256 x 64, A scales, B scale dwords).  Each pass multiplies k64 step 0 of stage kt
+// while reading step 1's fragments, passes the one barrier (stage kt + 1 published, every
+// wave done with stage kt), then multiplies step 1 while reading step 0 of stage kt + 1.
+// Loads are split as in the bf16 8-wave tile: stage s's B codes and scale dword go out in
+// the first half of pass s - NS + 1, its A codes in the second half of pass s - NS, both
+// into the buffer freed by the barrier of pass s - NS, interleaved one by one with MFMAs.
+// With one 32-row block per wave (linear1) each B fragment feeds one MFMA per k64 step and
+// is refilled right after it, which keeps the wave within 256 VGPRs without spilling.  The
+// k accumulation order is that of fp8_tile, so results are identical bit for bit.
+//
+// A codes are addressed by 32-bit byte offsets: callers keep A below 4 GiB.  One tile per
+// call; lds holds fp8_tile8_lds() bytes; same caller contract as fp8_tile.
+constexpr size_t fp8_tile8_lds() { return 3 * (size_t)(256 * 128 + 256 * 64 + 256 * 4 + 256 * 4); }
+
+// TM x TN blocks of 32x32 per wave; linear1 (SWIGLU): TM = 1, TN = 8 (32 rows, 128 gate + 128 up
+// columns); linear2: TM = 2, TN = 4 (64 rows x 128 columns).
+template <int TM, int TN, bool SWIGLU, bool GATHER>
+__device__ __forceinline__ void fp8_tile8(const Fp8Args &a, int tile, uint8_t *lds) {
+    constexpr int BM = 256, BN = 256, NS = 3;
+    constexpr int WMW = BM / (32 * TM), WNW = 8 / WMW;
+    static_assert(WNW * TN * 32 == BN, "wave grid");
+    static_assert(!SWIGLU || (TM == 1 && TN == 8), "SwiGLU needs 128 gate + 128 up columns per wave");
+    constexpr int PA = 4, PB = 2;                       // A / B code DMA instructions per wave and stage
+    constexpr int PER = PA + PB + 1;                    // + one scale instruction
+    constexpr int OFF_B = BM * 128, OFF_SA = OFF_B + BN * 64, OFF_SB = OFF_SA + BM * 4;
+    constexpr int STAGE = OFF_SB + BN * 4;
+
+    int g, row0, nrows, nt;
+    {
+        int lo = 0, hi = a.G - 1;
+        while (lo < hi) {
+            int mid = (lo + hi + 1) >> 1;
+            if (a.tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
+        }
+        g = lo;
+        const int rb = a.offsets[g], cnt = a.offsets[g + 1] - rb;
+        const int mtiles = (cnt + BM - 1) / BM, local = tile - a.tile_start[g];
+        const int mt = local % mtiles;
+        nt = local / mtiles;
+        row0 = rb + mt * BM;
+        nrows = min(BM, cnt - mt * BM);
+    }
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int wm = wave % WMW, wn = wave / WMW;
+    const int KB = a.K / 128;
+
+    uint32_t pa_off[PA];  // A is at most 4 GiB: byte offsets from the uniform base
+#pragma unroll
+    for (int q = 0; q < PA; ++q) {
+        const int r = 8 * (wave * PA + q) + (lane >> 3);
+        const long grow = row0 + (r < nrows ? r : 0);
+        const long src = GATHER ? row_token(grow, a.row_to_slot, a.T, a.k) : grow;
+        pa_off[q] = (uint32_t)(src * a.K + (((lane & 7) ^ ((r >> 1) & 7)) << 4));
+    }
+#define pa_at(q, kt) (a.A + pa_off[q] + (uint32_t)(kt) * 128u)
+    const int f0 = nt * (BN / 2), n0 = nt * BN;
+    auto wrow_of = [&](int r) -> long { return SWIGLU ? (r < BN / 2 ? f0 + r : a.F + f0 + r - BN / 2) : n0 + r; };
+    const uint8_t *pb[PB];
+#pragma unroll
+    for (int q = 0; q < PB; ++q) {
+        const int r = 16 * (wave * PB + q) + (lane >> 2);
+        pb[q] = a.B + ((long)g * a.Ntot + wrow_of(r)) * (a.K / 2) + (((lane & 3) ^ ((r >> 2) & 3)) << 4);
+    }
+    // scales: waves 0-3 load the A scales of rows 64 w + lane, waves 4-7 the B scale dwords
+    const uint8_t *psc;
+    int sc_dst, sc_step;
+    if (wave < 4) {
+        const int r = 64 * wave + lane;
+        const long grow = row0 + (r < nrows ? r : 0);
+        const long src = GATHER ? row_token(grow, a.row_to_slot, a.T, a.k) : grow;
+        psc = (const uint8_t *)(a.As + src * KB);
+        sc_dst = OFF_SA + wave * 256;
+        sc_step = 4;
+    } else {
+        const int r = 64 * (wave - 4) + lane;
+        psc = a.Bs + ((long)g * a.Ntot + wrow_of(r)) * (a.K / 32);
+        sc_dst = OFF_SB + (wave - 4) * 256;
+        sc_step = 4;
+    }
+
+    const int khalf = lane >> 5;
+    int aoff[2][TM][2], boff[2][TN], arow[TM], brow[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) arow[i] = wm * (32 * TM) + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int base = SWIGLU ? (j < TN / 2 ? j * 32 : BN / 2 + (j - TN / 2) * 32) : wn * (32 * TN) + j * 32;
+        brow[j] = base + (lane & 31);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            aoff[h][i][0] = sw128(arow[i], h * 4 + khalf);
+            aoff[h][i][1] = sw128(arow[i], h * 4 + 2 + khalf);
+        }
+        // the swizzle key of row 32 j + l does not depend on j: block j sits 2048 bytes further
+#pragma unroll
+        for (int j = 0; j < TN; ++j) boff[h][j] = OFF_B + sw64(brow[0], h * 2 + khalf) + (brow[j] - brow[0]) * 64;
+    }
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){};
+
+#define F8_BARRIER()                           \
+    do {                                       \
+        asm volatile("" ::: "memory");         \
+        __builtin_amdgcn_s_barrier();          \
+        asm volatile("" ::: "memory");         \
+    } while (0)
+    // part 1 of stage s: B codes and the scale dword; part 2: A codes
+#define F8_DMA1(s)                                                                                  \
+    do {                                                                                            \
+        const int s_ = (s);                                                                         \
+        uint8_t *st_ = lds + (s_ % NS) * STAGE;                                                     \
+        const int kt_ = s_ < KB ? s_ : KB - 1;                                                      \
+        _Pragma("unroll") for (int q = 0; q < PB; ++q)                                              \
+            lds_dma16(pb[q] + kt_ * 64, st_ + OFF_B + (wave * PB + q) * 1024);                      \
+        lds_dma4(psc + kt_ * sc_step, st_ + sc_dst);                                                \
+    } while (0)
+#define F8_DMA2(s)                                                                                  \
+    do {                                                                                            \
+        const int s_ = (s);                                                                         \
+        uint8_t *st_ = lds + (s_ % NS) * STAGE;                                                     \
+        const int kt_ = s_ < KB ? s_ : KB - 1;                                                      \
+        _Pragma("unroll") for (int q = 0; q < PA; ++q)                                              \
+            lds_dma16(pa_at(q, kt_), st_ + (wave * PA + q) * 1024);                             \
+    } while (0)
+#define F8_READ(FA, FB, s, h)                                                                       \
+    do {                                                                                            \
+        const uint8_t *st_ = lds + ((s) % NS) * STAGE;                                              \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                            \
+            FA[i][0] = *(const i32x4 *)(st_ + aoff[h][i][0]);                                       \
+            FA[i][1] = *(const i32x4 *)(st_ + aoff[h][i][1]);                                       \
+        }                                                                                           \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j) FB[j] = *(const i32x4 *)(st_ + boff[h][j]); \
+    } while (0)
+#define F8_SCALES(SA, SB, s)                                                                        \
+    do {                                                                                            \
+        const uint8_t *st_ = lds + ((s) % NS) * STAGE;                                              \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i)                                              \
+            SA[i] = (int)((*(const uint32_t *)(st_ + OFF_SA + arow[i] * 4) >> 23) & 0xFF);          \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j) SB[j] = *(const int *)(st_ + OFF_SB + brow[j] * 4); \
+    } while (0)
+#define F8_MMA(FA, FB, SA, SB, h)                                                                   \
+    do {                                                                                            \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i)                                              \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                        \
+                i32x8 av_ = {FA[i][0][0], FA[i][0][1], FA[i][0][2], FA[i][0][3],                    \
+                             FA[i][1][0], FA[i][1][1], FA[i][1][2], FA[i][1][3]};                   \
+                i32x8 bv_ = {FB[j][0], FB[j][1], FB[j][2], FB[j][3], 0, 0, 0, 0};                   \
+                const int sb_ = (SB[j] >> (8 * ((h) * 2 + khalf))) & 0xFF;                          \
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av_, bv_, acc[i][j], 0, 4, 0, \
+                                                                            SA[i], 0, sb_);         \
+            }                                                                                       \
+    } while (0)
+#define F8_INTERLEAVE(NR, ND)                                                                       \
+    do {                                                                                            \
+        _Pragma("unroll") for (int m_ = 0; m_ < TM * TN; ++m_) {                                    \
+            if (m_ < (ND)) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                       \
+            __builtin_amdgcn_sched_group_barrier(0x100, ((NR) + TM * TN - 1) / (TM * TN), 0);       \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                      \
+        }                                                                                           \
+        __builtin_amdgcn_sched_barrier(0);                                                          \
+    } while (0)
+
+    if constexpr (TM == 1) {
+        // one 32-row block per wave: each B fragment feeds one MFMA per k64 step, so it is
+        // refilled right after that MFMA (register rotation); only the A fragment is doubled
+        i32x4 fa0[2], fa1[2], fb[TN];
+        int sa0, sb0[TN];
+#define F8_RA(FA, s, h)                                                                             \
+        do {                                                                                        \
+            const uint8_t *st_ = lds + ((s) % NS) * STAGE;                                          \
+            FA[0] = *(const i32x4 *)(st_ + aoff[h][0][0]);                                          \
+            FA[1] = *(const i32x4 *)(st_ + aoff[h][0][1]);                                          \
+        } while (0)
+#define F8_RB(j, s, h) fb[j] = *(const i32x4 *)(lds + ((s) % NS) * STAGE + boff[h][j])
+#define F8_M1(FA, j, h)                                                                             \
+        do {                                                                                        \
+            i32x8 av_ = {FA[0][0], FA[0][1], FA[0][2], FA[0][3], FA[1][0], FA[1][1], FA[1][2], FA[1][3]}; \
+            i32x8 bv_ = {fb[j][0], fb[j][1], fb[j][2], fb[j][3], 0, 0, 0, 0};                       \
+            const int sb_ = (sb0[j] >> (8 * ((h) * 2 + khalf))) & 0xFF;                             \
+            acc[0][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av_, bv_, acc[0][j], 0, 4, 0, sa0, 0, sb_); \
+        } while (0)
+#define F8_SC(s)                                                                                    \
+        do {                                                                                        \
+            const uint8_t *st_ = lds + ((s) % NS) * STAGE;                                          \
+            sa0 = (int)((*(const uint32_t *)(st_ + OFF_SA + arow[0] * 4) >> 23) & 0xFF);            \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j)                                          \
+                sb0[j] = *(const int *)(st_ + OFF_SB + brow[0] * 4 + (j < TN / 2 ? j : BN / 2 / 32 + j - TN / 2) * 128); \
+        } while (0)
+        // single DMA instructions: part 1 (q < PB: B codes, q == PB: scales), part 2 (A codes)
+#define F8_D1(s, q)                                                                                 \
+        do {                                                                                        \
+            const int s_ = (s);                                                                     \
+            uint8_t *st_ = lds + (s_ % NS) * STAGE;                                                 \
+            const int kt_ = s_ < KB ? s_ : KB - 1;                                                  \
+            if ((q) < PB) lds_dma16(pb[(q) < PB ? (q) : 0] + kt_ * 64, st_ + OFF_B + (wave * PB + (q)) * 1024); \
+            else lds_dma4(psc + kt_ * sc_step, st_ + sc_dst);                                       \
+        } while (0)
+#define F8_D2(s, q)                                                                                 \
+        do {                                                                                        \
+            const int s_ = (s);                                                                     \
+            uint8_t *st_ = lds + (s_ % NS) * STAGE;                                                 \
+            const int kt_ = s_ < KB ? s_ : KB - 1;                                                  \
+            lds_dma16(pa_at(q, kt_), st_ + (wave * PA + (q)) * 1024);                           \
+        } while (0)
+#pragma unroll
+        for (int s0 = 0; s0 < NS - 1; ++s0) {
+            F8_DMA2(s0);
+            F8_DMA1(s0);
+        }
+        F8_DMA2(NS - 1);
+        wait_vmcnt<(NS - 2) * PER + PA>();
+        F8_BARRIER();
+        F8_RA(fa0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) F8_RB(j, 0, 0);
+        F8_SC(0);
+        wait_lgkmcnt0();
+        for (int kt = 0; kt < KB; ++kt) {
+            const int nx = kt + 1 < KB ? kt + 1 : kt;
+            F8_RA(fa1, kt, 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                F8_M1(fa0, j, 0);
+                F8_RB(j, kt, 1);
+                if (j & 1) {
+                    if (j / 2 < PB + 1) F8_D1(kt + NS - 1, j / 2);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            wait_vmcnt<(NS - 2) * PER>();
+            wait_lgkmcnt0();
+            F8_BARRIER();
+            __builtin_amdgcn_sched_barrier(0);
+            F8_RA(fa0, nx, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                F8_M1(fa1, j, 1);
+                F8_RB(j, nx, 0);
+                if (!(j & 1)) F8_D2(kt + NS, j / 2);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            F8_SC(nx);  // after every MFMA of stage kt has taken its scales
+            wait_lgkmcnt0();
+        }
+#undef F8_RA
+#undef F8_RB
+#undef F8_M1
+#undef F8_SC
+#undef F8_D1
+#undef F8_D2
+    } else {
+    i32x4 fa0[TM][2], fb0[TN], fa1[TM][2], fb1[TN];
+        int sa0[TM], sb0[TN];
+        // prologue: stages 0 .. NS-2 whole and part 2 of stage NS-1; stage 0 published
+    #pragma unroll
+        for (int s0 = 0; s0 < NS - 1; ++s0) {
+            F8_DMA2(s0);
+            F8_DMA1(s0);
+        }
+        F8_DMA2(NS - 1);
+        wait_vmcnt<(NS - 2) * PER + PA>();
+        F8_BARRIER();
+        F8_READ(fa0, fb0, 0, 0);
+        F8_SCALES(sa0, sb0, 0);
+        wait_lgkmcnt0();
+        for (int kt = 0; kt < KB; ++kt) {
+            const int nx = kt + 1 < KB ? kt + 1 : kt;
+            F8_READ(fa1, fb1, kt, 1);
+            F8_DMA1(kt + NS - 1);
+            F8_MMA(fa0, fb0, sa0, sb0, 0);
+            F8_INTERLEAVE(2 * TM + TN, PB + 1);
+            wait_vmcnt<(NS - 2) * PER>();
+            wait_lgkmcnt0();
+            F8_BARRIER();
+            __builtin_amdgcn_sched_barrier(0);
+            F8_DMA2(kt + NS);
+            F8_READ(fa0, fb0, nx, 0);
+            F8_MMA(fa1, fb1, sa0, sb0, 1);
+            F8_INTERLEAVE(2 * TM + TN, PA);
+            F8_SCALES(sa0, sb0, nx);  // after every MFMA of stage kt has taken its scales
+            wait_lgkmcnt0();
+        }
+    }
+    wait_vmcnt<0>();
+#undef pa_at
+#undef F8_BARRIER
+#undef F8_DMA1
+#undef F8_DMA2
+#undef F8_READ
+#undef F8_SCALES
+#undef F8_MMA
+#undef F8_INTERLEAVE
+
+    if (SWIGLU) {
+        uint8_t *hq = (uint8_t *)a.C;
+        constexpr int TNh = TN / 2;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * (32 * TM) + i * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+                float hv[TNh];
+                float amax = 0.0f;
+#pragma unroll
+                for (int j = 0; j < TNh; ++j) {
+                    const float gv = acc[i][j][r], uv = acc[i][j + TNh][r];
+                    hv[j] = gv / (1.0f + __expf(-gv)) * uv;
+                    amax = fmaxf(amax, fabsf(hv[j]));
+                }
+#pragma unroll
+                for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+                if (row < nrows) {
+                    const int e = e4m3_block_exponent(amax);
+                    const float inv = ldexpf(1.0f, -e);
+                    const long grow = row0 + row;
+#pragma unroll
+                    for (int j = 0; j < TNh; ++j) {
+                        const uint32_t c = cvt_e4m3x2(hv[j] * inv, 0.0f) & 0xFFu;
+                        hq[grow * a.F + f0 + j * 32 + (lane & 31)] = (uint8_t)c;
+                    }
+                    if ((lane & 31) == 0) a.Cs[grow * (a.F / 128) + f0 / 128] = ldexpf(1.0f, e);
+                }
+            }
+        }
+    } else {
+        uint16_t *y = (uint16_t *)a.C;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * (32 * TM) + i * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+                if (row >= nrows) continue;
+                const long grow = row0 + row;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) y[grow * a.ldc + n0 + wn * (32 * TN) + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][r]);
+            }
+        }
+    }
+}
+
 // ---- decode path: few rows per group ----------------------------------------------------
 //
 // With a handful of rows per expert the layer is weight streaming (HBM bound).  Each

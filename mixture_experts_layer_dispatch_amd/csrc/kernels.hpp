@@ -29,8 +29,10 @@ struct Shape {
 };
 
 // router: logits, keys, top-k, gates.  part: fp32 scratch of route_splitk_slices(s) * T * E
-// partial logits (split-K path), or nullptr to always use the one-pass kernels.
+// partial logits (split-K and tiled paths), or nullptr to always use the one-pass kernels.
+// route_tile_slices(s) > 0: the unfused router runs as a tiled GEMM over that many slices.
 int route_splitk_slices(const Shape &s);
+int route_tile_slices(const Shape &s);
 long route_splitk_waves(const Shape &s, int nks);
 hipError_t launch_route(const Shape &s, const void *x, const void *wr, const float *bias, int32_t *idx,
                         float *gate, float *logits, float *keys, int32_t *err, float *part, hipStream_t st);
