@@ -245,18 +245,24 @@ constexpr size_t bf16_tile8_lds() { return 5 * (size_t)(256 + 256) * 64; }
 
 // The core takes the tile's rows and N tile (ti), the row stride of A and B in elements
 // (lda), and the K range [k0, k0 + 32 nk).  F32OUT (not with SWIGLU) writes fp32 C.
-template <bool SWIGLU, bool GATHER, bool F32OUT>
+//
+// TM = 32-row blocks per wave: 4 for tiles of up to 256 rows; a group's last, partial
+// tile runs with TM = 2 (up to 128 rows) or 1 (up to 64), which keeps the wave grid and
+// the LDS layout, loads only the first 128 A rows and multiplies only TM blocks: MFMA work
+// shrinks with the rows present and stays balanced over the SIMDs.
+template <bool SWIGLU, bool GATHER, bool F32OUT, int TM>
 __device__ __forceinline__ void bf16_tile8_core(const GemmArgs &a, const TileInfo &ti, long lda, int k0, int nk,
                                                 uint8_t *lds) {
     constexpr int BM = 256, BN = 256, BK = 32, NS = 5;
     static_assert(!(SWIGLU && F32OUT), "SwiGLU writes bf16 h");
-    constexpr int TM = 4, TN = 2;                          // wave block 128 x 64
+    static_assert(TM == 4 || TM == 2 || TM == 1, "row blocks per wave");
+    constexpr int TN = 2;                                  // wave block (32 TM) x 64
     constexpr int CPR = BK / 8, RPI = 64 / CPR;            // 16 rows per DMA instruction
-    constexpr int IA = BM / (8 * RPI), IB = BN / (8 * RPI);  // 2 + 2 DMA instructions per wave and stage
+    constexpr int IA = TM == 4 ? 2 : 1, IB = BN / (8 * RPI);  // A and B DMA instructions per wave and stage
     constexpr int PER = IA + IB;
     constexpr int ROWB = BK * 2;
     constexpr int STAGE = (BM + BN) * ROWB;
-    static_assert(IA == 2 && IB == 2, "interleave pattern assumes two A and two B instructions");
+    static_assert(IB == 2, "interleave pattern assumes two B instructions");
 
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;
@@ -290,7 +296,7 @@ __device__ __forceinline__ void bf16_tile8_core(const GemmArgs &a, const TileInf
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) aoff[h][i] = swz_off<BK>(wm * 128 + i * 32 + (lane & 31), h * 2 + khalf);
+        for (int i = 0; i < TM; ++i) aoff[h][i] = swz_off<BK>(wm * (32 * TM) + i * 32 + (lane & 31), h * 2 + khalf);
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int base = SWIGLU ? (j == 0 ? wn * 32 : BN / 2 + wn * 32) : wn * 64 + j * 32;
@@ -335,16 +341,25 @@ __device__ __forceinline__ void bf16_tile8_core(const GemmArgs &a, const TileInf
             _Pragma("unroll") for (int j = 0; j < TN; ++j)                                       \
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[i], F[TM + j], acc[i][j], 0, 0, 0); \
     } while (0)
-    // per half pass: 8 MFMAs, 6 fragment reads and 2 DMA instructions, interleaved
-#define MOE_INTERLEAVE()                                                                         \
+    // per half pass with TM = 4: 8 MFMAs, 6 fragment reads and 2 DMA instructions, as
+    // {3 x (read, MFMA), (DMA, MFMA)} twice; smaller TM: (DMA?, reads, MFMA) per MFMA
+#define MOE_INTERLEAVE(ND)                                                                       \
     do {                                                                                         \
-        _Pragma("unroll") for (int r_ = 0; r_ < 2; ++r_) {                                       \
-            _Pragma("unroll") for (int q_ = 0; q_ < 3; ++q_) {                                   \
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                               \
+        if constexpr (TM == 4) {                                                                 \
+            _Pragma("unroll") for (int r_ = 0; r_ < 2; ++r_) {                                   \
+                _Pragma("unroll") for (int q_ = 0; q_ < 3; ++q_) {                               \
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                           \
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                           \
+                }                                                                                \
+                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                               \
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                               \
             }                                                                                    \
-            __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                   \
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   \
+        } else {                                                                                 \
+            _Pragma("unroll") for (int m_ = 0; m_ < TM * TN; ++m_) {                             \
+                if (m_ < (ND)) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                \
+                __builtin_amdgcn_sched_group_barrier(0x100, (TM + TN + TM * TN - 1) / (TM * TN), 0); \
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                               \
+            }                                                                                    \
         }                                                                                        \
         __builtin_amdgcn_sched_barrier(0);                                                       \
     } while (0)
@@ -365,7 +380,7 @@ __device__ __forceinline__ void bf16_tile8_core(const GemmArgs &a, const TileInf
         MOE_READ(F1, kt, 1);
         MOE_DMA_B(kt + NS - 1);
         MOE_MMA(F0);
-        MOE_INTERLEAVE();
+        MOE_INTERLEAVE(IB);
         wait_vmcnt<(NS - 2) * PER>();  // own loads of stage kt+1 landed (kt+2 .. kt+NS-1 may fly)
         wait_lgkmcnt0();
         MOE_BARRIER();
@@ -373,7 +388,7 @@ __device__ __forceinline__ void bf16_tile8_core(const GemmArgs &a, const TileInf
         MOE_DMA_A(kt + NS);
         MOE_READ(F0, (kt + 1 < nk ? kt + 1 : kt), 0);  // the last pass re-reads a published stage
         MOE_MMA(F1);
-        MOE_INTERLEAVE();
+        MOE_INTERLEAVE(IA);
         wait_lgkmcnt0();
     }
     wait_vmcnt<0>();
@@ -388,7 +403,7 @@ __device__ __forceinline__ void bf16_tile8_core(const GemmArgs &a, const TileInf
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+            const int row = wm * (32 * TM) + i * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
             if (row >= ti.nrows) continue;
             const long grow = ti.row0 + row;
             if (SWIGLU) {
@@ -407,10 +422,19 @@ __device__ __forceinline__ void bf16_tile8_core(const GemmArgs &a, const TileInf
     }
 }
 
+// the core sized to the tile's rows
+template <bool SWIGLU, bool GATHER, bool F32OUT>
+__device__ __forceinline__ void bf16_tile8_rows(const GemmArgs &a, const TileInfo &ti, long lda, int k0, int nk,
+                                                uint8_t *lds) {
+    if (ti.nrows > 128) bf16_tile8_core<SWIGLU, GATHER, F32OUT, 4>(a, ti, lda, k0, nk, lds);
+    else if (ti.nrows > 64) bf16_tile8_core<SWIGLU, GATHER, F32OUT, 2>(a, ti, lda, k0, nk, lds);
+    else bf16_tile8_core<SWIGLU, GATHER, F32OUT, 1>(a, ti, lda, k0, nk, lds);
+}
+
 template <bool SWIGLU, bool GATHER>
 __device__ __forceinline__ void bf16_tile8(const GemmArgs &a, int tile, uint8_t *lds) {
     const TileInfo ti = decode_tile(tile, a.tile_start, a.offsets, a.G, 256);
-    bf16_tile8_core<SWIGLU, GATHER, false>(a, ti, a.K, 0, a.K / 32, lds);
+    bf16_tile8_rows<SWIGLU, GATHER, false>(a, ti, a.K, 0, a.K / 32, lds);
 }
 
 // ---- fp32 path: one lane per output element ------------------------------------

@@ -333,8 +333,11 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args &a, int tile, uint8_t *ld
 // the first half of pass s - NS + 1, its A codes in the second half of pass s - NS, both
 // into the buffer freed by the barrier of pass s - NS, interleaved one by one with MFMAs.
 // With one 32-row block per wave (linear1) each B fragment feeds one MFMA per k64 step and
-// is refilled right after it, which keeps the wave within 256 VGPRs without spilling.  The
-// k accumulation order is that of fp8_tile, so results are identical bit for bit.
+// is refilled right after it, which keeps the wave within 256 VGPRs without spilling.  A
+// wave whose rows all lie past a group's last, partial tile skips its fragment reads and
+// MFMAs (it still loads its share and keeps the barriers), and the row groups are laid out
+// so that the first 128 rows take one wave per SIMD.  The k accumulation order is that of
+// fp8_tile, so results are identical bit for bit.
 //
 // A codes are addressed by 32-bit byte offsets: callers keep A below 4 GiB.  One tile per
 // call; lds holds fp8_tile8_lds() bytes; same caller contract as fp8_tile.
@@ -369,7 +372,9 @@ __device__ __forceinline__ void fp8_tile8(const Fp8Args &a, int tile, uint8_t *l
         nrows = min(BM, cnt - mt * BM);
     }
     const int lane = lane_id(), wave = threadIdx.x >> 6;
-    const int wm = wave % WMW, wn = wave / WMW;
+    // linear2: waves 0-3 (one per SIMD) cover rows 0-127, so a short tile keeps every SIMD busy
+    const int wm = TM == 1 ? wave : (wave & 1) + 2 * (wave >> 2), wn = TM == 1 ? 0 : (wave >> 1) & 1;
+    static_assert(TM == 1 || (WMW == 4 && WNW == 2), "wave grid");
     const int KB = a.K / 128;
 
     uint32_t pa_off[PA];  // A is at most 4 GiB: byte offsets from the uniform base
@@ -550,35 +555,43 @@ __device__ __forceinline__ void fp8_tile8(const Fp8Args &a, int tile, uint8_t *l
         for (int j = 0; j < TN; ++j) F8_RB(j, 0, 0);
         F8_SC(0);
         wait_lgkmcnt0();
-        for (int kt = 0; kt < KB; ++kt) {
-            const int nx = kt + 1 < KB ? kt + 1 : kt;
-            F8_RA(fa1, kt, 1);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                F8_M1(fa0, j, 0);
-                F8_RB(j, kt, 1);
-                if (j & 1) {
-                    if (j / 2 < PB + 1) F8_D1(kt + NS - 1, j / 2);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            wait_vmcnt<(NS - 2) * PER>();
-            wait_lgkmcnt0();
-            F8_BARRIER();
-            __builtin_amdgcn_sched_barrier(0);
-            F8_RA(fa0, nx, 0);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                F8_M1(fa1, j, 1);
-                F8_RB(j, nx, 0);
-                if (!(j & 1)) F8_D2(kt + NS, j / 2);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            F8_SC(nx);  // after every MFMA of stage kt has taken its scales
-            wait_lgkmcnt0();
+        // a wave whose 32 rows lie past the tile's rows only loads and keeps the barriers
+#define F8_LOOP1(ACT)                                                                               \
+        for (int kt = 0; kt < KB; ++kt) {                                                           \
+            const int nx = kt + 1 < KB ? kt + 1 : kt;                                               \
+            if (ACT) F8_RA(fa1, kt, 1);                                                             \
+            __builtin_amdgcn_sched_barrier(0);                                                      \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                        \
+                if (ACT) {                                                                          \
+                    F8_M1(fa0, j, 0);                                                               \
+                    F8_RB(j, kt, 1);                                                                \
+                }                                                                                   \
+                if ((j & 1) && j / 2 < PB + 1) F8_D1(kt + NS - 1, j / 2);                           \
+                __builtin_amdgcn_sched_barrier(0);                                                  \
+            }                                                                                       \
+            wait_vmcnt<(NS - 2) * PER>();                                                           \
+            wait_lgkmcnt0();                                                                        \
+            F8_BARRIER();                                                                           \
+            __builtin_amdgcn_sched_barrier(0);                                                      \
+            if (ACT) F8_RA(fa0, nx, 0);                                                             \
+            __builtin_amdgcn_sched_barrier(0);                                                      \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                        \
+                if (ACT) {                                                                          \
+                    F8_M1(fa1, j, 1);                                                               \
+                    F8_RB(j, nx, 0);                                                                \
+                }                                                                                   \
+                if (!(j & 1)) F8_D2(kt + NS, j / 2);                                                \
+                __builtin_amdgcn_sched_barrier(0);                                                  \
+            }                                                                                       \
+            if (ACT) F8_SC(nx); /* after every MFMA of stage kt has taken its scales */             \
+            wait_lgkmcnt0();                                                                        \
         }
+        if (wave * 32 < nrows) {
+            F8_LOOP1(true)
+        } else {
+            F8_LOOP1(false)
+        }
+#undef F8_LOOP1
 #undef F8_RA
 #undef F8_RB
 #undef F8_M1
@@ -600,23 +613,35 @@ __device__ __forceinline__ void fp8_tile8(const Fp8Args &a, int tile, uint8_t *l
         F8_READ(fa0, fb0, 0, 0);
         F8_SCALES(sa0, sb0, 0);
         wait_lgkmcnt0();
-        for (int kt = 0; kt < KB; ++kt) {
-            const int nx = kt + 1 < KB ? kt + 1 : kt;
-            F8_READ(fa1, fb1, kt, 1);
-            F8_DMA1(kt + NS - 1);
-            F8_MMA(fa0, fb0, sa0, sb0, 0);
-            F8_INTERLEAVE(2 * TM + TN, PB + 1);
-            wait_vmcnt<(NS - 2) * PER>();
-            wait_lgkmcnt0();
-            F8_BARRIER();
-            __builtin_amdgcn_sched_barrier(0);
-            F8_DMA2(kt + NS);
-            F8_READ(fa0, fb0, nx, 0);
-            F8_MMA(fa1, fb1, sa0, sb0, 1);
-            F8_INTERLEAVE(2 * TM + TN, PA);
-            F8_SCALES(sa0, sb0, nx);  // after every MFMA of stage kt has taken its scales
-            wait_lgkmcnt0();
+        // a wave whose rows lie past the tile's rows only loads and keeps the barriers
+#define F8_LOOP2(ACT)                                                                               \
+        for (int kt = 0; kt < KB; ++kt) {                                                           \
+            const int nx = kt + 1 < KB ? kt + 1 : kt;                                               \
+            if (ACT) F8_READ(fa1, fb1, kt, 1);                                                      \
+            F8_DMA1(kt + NS - 1);                                                                   \
+            if (ACT) {                                                                              \
+                F8_MMA(fa0, fb0, sa0, sb0, 0);                                                      \
+                F8_INTERLEAVE(2 * TM + TN, PB + 1);                                                 \
+            }                                                                                       \
+            wait_vmcnt<(NS - 2) * PER>();                                                           \
+            wait_lgkmcnt0();                                                                        \
+            F8_BARRIER();                                                                           \
+            __builtin_amdgcn_sched_barrier(0);                                                      \
+            F8_DMA2(kt + NS);                                                                       \
+            if (ACT) {                                                                              \
+                F8_READ(fa0, fb0, nx, 0);                                                           \
+                F8_MMA(fa1, fb1, sa0, sb0, 1);                                                      \
+                F8_INTERLEAVE(2 * TM + TN, PA);                                                     \
+                F8_SCALES(sa0, sb0, nx); /* after every MFMA of stage kt has taken its scales */    \
+            }                                                                                       \
+            wait_lgkmcnt0();                                                                        \
         }
+        if (wm * 32 * TM < nrows) {
+            F8_LOOP2(true)
+        } else {
+            F8_LOOP2(false)
+        }
+#undef F8_LOOP2
     }
     wait_vmcnt<0>();
 #undef pa_at

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(512) void route_tile_kernel(const uint16_t *__restr
     ti.nrows = min(256, T - ti.row0);
     GemmArgs a = {x, nullptr, wr, (uint16_t *)(part + (long)ks * T * E), nullptr, nullptr, T, 1, d, E, E, 1, 0};
     const int kchunk = d / nks;
-    bf16_tile8_core<false, false, true>(a, ti, d, ks * kchunk, kchunk / 32, lds);
+    bf16_tile8_rows<false, false, true>(a, ti, d, ks * kchunk, kchunk / 32, lds);
 }
 
 // one workgroup per token
