@@ -205,10 +205,10 @@ moe_status moe_dispatch(const moe_cfg *cfg, const int32_t *topk_idx, const void 
     MOE_TRY(arch_check());
     const Layout L = layout_of(cfg);
     const Shape s = shape_of(cfg);
-    hipError_t e = launch_dispatch(s, topk_idx, at<int32_t>(ws, L.blockcounts), counts, offsets, slot_to_row,
-                                   row_to_slot, at<int32_t>(ws, L.err), stream);
-    if (e == hipSuccess && fp8) e = launch_quant_x(s, (const uint16_t *)x, xq, xq_scale, stream);
-    return launched(e);
+    // FP8 mode: the activations are quantised by the same launch (an independent job)
+    return launched(launch_dispatch(s, topk_idx, at<int32_t>(ws, L.blockcounts), counts, offsets, slot_to_row,
+                                    row_to_slot, at<int32_t>(ws, L.err), fp8 ? (const uint16_t *)x : nullptr,
+                                    fp8 ? xq : nullptr, fp8 ? xq_scale : nullptr, stream));
 }
 
 moe_status moe_ffn(const moe_cfg *cfg, const moe_weights *w, const void *x, const uint8_t *xq, const float *xq_scale,

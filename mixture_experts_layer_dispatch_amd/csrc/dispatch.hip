@@ -28,32 +28,71 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t *__
     scatter_block<false>(idx, T, k, E, blockIdx.x, bases, slot_to_row, row_to_slot, masks);
 }
 
+// One dispatch block (T <= 256 tokens): workgroup 0 runs histogram, scan and scatter in
+// one pass (device-coherent accesses, as its own stores are read back), the others
+// quantise x to e4m3 (an independent job; none when xq is null).
+__global__ __launch_bounds__(256) void dispatch_one_kernel(const int32_t *__restrict__ idx, int T, int k, int E,
+                                                          int S, int32_t *__restrict__ blockcounts,
+                                                          int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                                                          int32_t *__restrict__ slot_to_row,
+                                                          int32_t *__restrict__ row_to_slot, int32_t *err,
+                                                          const uint16_t *__restrict__ x, long nq,
+                                                          uint8_t *__restrict__ xq, float *__restrict__ xs) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    if (blockIdx.x > 0) {
+        for (long gid = (long)(blockIdx.x - 1) * blockDim.x + threadIdx.x; gid < nq * 16;
+             gid += (long)(gridDim.x - 1) * blockDim.x)
+            quant_x_lane<false>(x, nq, xq, xs, gid);
+        return;
+    }
+    count_block<true>(idx, T, k, E, 0, (unsigned long long *)lds, blockcounts, err);
+    wait_vmcnt<0>();
+    __syncthreads();
+    dispatch_scan_block<true>(blockcounts, 1, T, E, S, counts, offsets, (int32_t *)lds);
+    wait_vmcnt<0>();
+    __syncthreads();
+    scatter_block<true>(idx, T, k, E, 0, blockcounts, slot_to_row, row_to_slot, (unsigned long long *)lds);
+}
+
+// Histogram of one dispatch block per workgroup; workgroups past nblk quantise x.
+__global__ __launch_bounds__(256) void dispatch_count_quant_kernel(const int32_t *__restrict__ idx, int T, int k,
+                                                                  int E, int nblk, int32_t *__restrict__ blockcounts,
+                                                                  int32_t *err, const uint16_t *__restrict__ x,
+                                                                  long nq, uint8_t *__restrict__ xq,
+                                                                  float *__restrict__ xs) {
+    extern __shared__ unsigned long long masks[];  // [4][E]
+    if ((int)blockIdx.x >= nblk) {
+        const long nqg = gridDim.x - nblk;
+        for (long gid = (long)(blockIdx.x - nblk) * blockDim.x + threadIdx.x; gid < nq * 16; gid += nqg * blockDim.x)
+            quant_x_lane<false>(x, nq, xq, xs, gid);
+        return;
+    }
+    count_block<false>(idx, T, k, E, blockIdx.x, masks, blockcounts, err);
+}
+
+// x, xq, xs: the activations and their e4m3 codes and block scales, quantised alongside
+// (FP8 mode), or null.
 hipError_t launch_dispatch(const Shape &s, const int32_t *idx, int32_t *blockcounts, int32_t *counts,
                            int32_t *offsets, int32_t *slot_to_row, int32_t *row_to_slot, int32_t *err,
-                           hipStream_t st) {
+                           const uint16_t *x, uint8_t *xq, float *xs, hipStream_t st) {
     if (s.T == 0) return hipSuccess;
     const int nblk = dispatch_blocks(s.T);
     const size_t lds = (size_t)4 * s.E * sizeof(unsigned long long);
-    MOE_LAUNCH("dispatch_count", dispatch_count_kernel, dim3(nblk), dim3(256), lds, st, idx, s.T, s.k, s.E,
-               blockcounts, err);
+    const long nq = xq ? (long)s.T * s.d / 128 : 0;
+    // quantisation workgroups: 16 lanes per 128-wide block, up to 4 blocks' worth per lane
+    const long qwg = nq ? (nq * 16 + 1023) / 1024 : 0;
+    if (nblk == 1) {
+        const size_t l1 = lds > (size_t)(1024 + 256) * 4 ? lds : (size_t)(1024 + 256) * 4;
+        MOE_LAUNCH("dispatch", dispatch_one_kernel, dim3((unsigned)(1 + qwg)), dim3(256), l1, st, idx, s.T, s.k, s.E,
+                   s.S, blockcounts, counts, offsets, slot_to_row, row_to_slot, err, x, nq, xq, xs);
+        return hipGetLastError();
+    }
+    MOE_LAUNCH("dispatch_count", dispatch_count_quant_kernel, dim3((unsigned)(nblk + qwg)), dim3(256), lds, st, idx,
+               s.T, s.k, s.E, nblk, blockcounts, err, x, nq, xq, xs);
     MOE_LAUNCH("dispatch_scan", dispatch_scan_kernel, dim3(1), dim3(256), 0, st, blockcounts, nblk, s.T, s.E, s.S,
                counts, offsets);
     MOE_LAUNCH("dispatch_scatter", dispatch_scatter_kernel, dim3(nblk), dim3(256), lds, st, idx, s.T, s.k, s.E,
                (const int32_t *)blockcounts, slot_to_row, row_to_slot);
-    return hipGetLastError();
-}
-
-__global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t *__restrict__ x, long nblocks,
-                                                     uint8_t *__restrict__ xq, float *__restrict__ xs) {
-    quant_x_lane<false>(x, nblocks, xq, xs, (long)blockIdx.x * blockDim.x + threadIdx.x);
-}
-
-hipError_t launch_quant_x(const Shape &s, const uint16_t *x, uint8_t *xq, float *xs, hipStream_t st) {
-    const long nblocks = (long)s.T * s.d / 128;
-    if (nblocks == 0) return hipSuccess;
-    const long threads = nblocks * 16;
-    MOE_LAUNCH("quant_x", quant_x_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, x, nblocks, xq,
-               xs);
     return hipGetLastError();
 }
 

@@ -47,27 +47,21 @@ FfnPlan ffn_plan(const Shape &s) {
     FfnPlan p;
     const long rows = s.rows();
     const double per_group = (double)rows / s.G();
-    const long G = s.G();
     // weight streaming only below one row per group: from there on the tiled kernels, which
     // stream each weight tile through LDS for several rows, are faster (measured at 2.2 rows
     // per group: 1.52 against 1.61 ms; at 18: 2.12 against 2.83 ms)
     p.decode = s.mode == MODE_FP8 && per_group < 1.0 && rows * (s.d > 2 * s.F ? s.d : 2 * s.F) < (1L << 31);
     if (p.decode) {
         // One 64-lane wave per (group, 32-row tile, 32 output columns, K slice).  linear1's
-        // K slices (whole 256-wide chunks) minimise rounds over the resident waves (256 CUs
-        // x 16) times the K per wave plus a fixed cost per tile worth 1024 of K, counting
-        // the row tiles one per touched group.
-        constexpr long kWaves = 4096;
-        const long mt = rows <= G ? rows : rows / 32 + G;
-        const long per_ks = mt * (2L * s.F / 32);
+        // K slices are whole 256-wide chunks, the fewest that keep a slice within 1024: the
+        // unfused kernel stages a slice of each activation row in LDS, and 4-wave groups
+        // of these waves then stream every weight tile with four blocks in flight.  If d is
+        // no multiple of 256, one slice.
         const int chunks = s.d % 256 == 0 ? s.d / 256 : 1;
-        long best_cost = -1;
         p.ks = 1;
-        for (int q = 1; q <= chunks && q <= 32; ++q) {
-            if (chunks % q) continue;
-            const long cost = (per_ks * q + kWaves - 1) / kWaves * (s.d / q + 1024);
-            if (best_cost < 0 || cost < best_cost) { best_cost = cost; p.ks = q; }
-        }
+        if (s.d % 256 == 0)
+            for (int q = 1; q <= chunks; ++q)
+                if (chunks % q == 0 && s.d / q <= 1024) { p.ks = q; break; }
         p.bm1 = p.bm2 = 32;
         p.bn1 = p.bn2 = 32;
         p.ntn1 = (2 * s.F / 32) * p.ks;
@@ -139,8 +133,9 @@ hipError_t launch_ffn(const Shape &s, const FfnPlan &p, const void *w1, const vo
     }
     int32_t *ts1 = tile_start, *ts2 = tile_start + (G + 1);
     const int ntn1 = p.ntn1, ntn2 = p.ntn2;
-    MOE_LAUNCH("tile_plan", tile_plan_kernel, dim3(1), dim3(256), 0, st, offsets, G, p.bm1, ntn1, p.bm2, ntn2, ts1,
-               ts2);
+    if (!(s.mode == MODE_FP8 && fp8_gemv_ok(s, p)))
+        MOE_LAUNCH("tile_plan", tile_plan_kernel, dim3(1), dim3(256), 0, st, offsets, G, p.bm1, ntn1, p.bm2, ntn2, ts1,
+                   ts2);
     if (s.mode == MODE_FP8)
         return launch_fp8_ffn(s, p, (const uint8_t *)w1, (const uint8_t *)w1s, (const uint8_t *)w2,
                               (const uint8_t *)w2s, xq, xs, offsets, row_to_slot, (uint8_t *)h, hs, y_perm, ts1, ts2,

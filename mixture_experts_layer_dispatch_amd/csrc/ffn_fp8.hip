@@ -1,6 +1,7 @@
 // FP8 e4m3 x MXFP4 FFN kernels (S8-S9, S12) and their launchers; the work items live in
 // gemm_fp8_dev.hpp.
 #include "common.hpp"
+#include "dispatch_dev.hpp"
 #include "gemm_fp8_dev.hpp"
 #include "kernels.hpp"
 
@@ -56,7 +57,29 @@ constexpr long kDecodeMaxWaves = 1L << 20;  // grid cap; the kernels stride over
 template <bool LIN1>
 __global__ __launch_bounds__(64) void fp8_decode_kernel(DecArgs a) {
     const int total = a.tile_start[a.G];
-    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) fp8_decode_tile<LIN1, false>(a, tile, a.tile_start, a.offsets);
+    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) fp8_decode_tile<LIN1, false, true>(a, tile, a.tile_start, a.offsets);
+}
+
+// workgroup tiles: ts[G] / 4 of them
+// ntn: 32-column tiles per row tile and group (the K slices included).  The tile plan --
+// the prefix over groups of ceil(rows / 32) * ntn -- is built in LDS from the offsets.
+template <bool LIN1, int QC>
+__global__ __launch_bounds__(256) void fp8_gemv_kernel(DecArgs a, int rmax, int ntn) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    int32_t *plan = (int32_t *)lds;  // tile starts, then group offsets
+    for (int i = threadIdx.x; i <= a.G; i += blockDim.x) plan[a.G + 1 + i] = a.offsets[i];
+    __syncthreads();
+    for (int g = threadIdx.x; g < a.G; g += blockDim.x)
+        plan[g] = (plan[a.G + 2 + g] - plan[a.G + 1 + g] + 31) / 32 * ntn;
+    __syncthreads();
+    const int tot = block_exclusive_scan(plan, a.G, plan + 2 * (a.G + 1));
+    if (threadIdx.x == 0) plan[a.G] = tot;
+    __syncthreads();
+    const int total = plan[a.G] / (4 * QC);
+    for (int wt = blockIdx.x; wt < total; wt += gridDim.x) {
+        fp8_gemv_tile<LIN1, QC>(a, wt, rmax, plan, lds);
+        __syncthreads();  // the next tile restages the LDS rows
+    }
 }
 
 __global__ __launch_bounds__(256) void fp8_decode_swiglu_kernel(const float *__restrict__ part, long rows, int F,
@@ -64,6 +87,17 @@ __global__ __launch_bounds__(256) void fp8_decode_swiglu_kernel(const float *__r
                                                                float *__restrict__ hs) {
     const long wid = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (wid < rows * (F / 128)) decode_swiglu_wave<false>(part, rows, F, ks, hq, hs, wid);
+}
+
+// The workgroup decode kernels apply: K slices of whole 1024-wide blocks (at most 2048),
+// column tiles in fours, and the staged rows (at most min(32, T) per tile) and the plan
+// within 64 KB of LDS.  They build their own tile plan.
+bool fp8_gemv_ok(const Shape &s, const FfnPlan &p) {
+    if (!p.decode) return false;
+    const int rmax = s.T < 32 ? s.T : 32, G = s.G();
+    const int kc1 = s.d / p.ks, kc2 = s.F;
+    return kc1 % 1024 == 0 && kc2 % 1024 == 0 && kc1 <= 2048 && kc2 <= 2048 && p.ntn1 % 4 == 0 &&
+           p.ntn2 % 4 == 0 && fp8_gemv_lds_total(G, rmax, kc1) <= 65536 && fp8_gemv_lds_total(G, rmax, kc2) <= 65536;
 }
 
 static hipError_t launch_fp8_decode(const Shape &s, const FfnPlan &p, const uint8_t *w1, const uint8_t *w1s,
@@ -79,11 +113,58 @@ static hipError_t launch_fp8_decode(const Shape &s, const FfnPlan &p, const uint
         return dim3((unsigned)(ub < kDecodeMaxWaves ? ub : kDecodeMaxWaves));
     };
     DecArgs a1 = {xq, xs, row_to_slot, offsets, ts1, w1, w1s, upart, nullptr, rows, s.T, s.k, s.d, 2 * s.F, G, p.ks};
-    MOE_LAUNCH("linear1", fp8_decode_kernel<true>, grid_for(p.ntn1), dim3(64), 0, st, a1);
+    DecArgs a2 = {h, hs, nullptr, offsets, ts2, w2, w2s, nullptr, (uint16_t *)y_perm, rows, s.T, s.k, s.F, s.d, G, 1};
+    const int rmax = s.T < 32 ? s.T : 32;
+    const int kc1 = s.d / p.ks, kc2 = s.F;
+    const size_t l1 = fp8_gemv_lds_total(G, rmax, kc1), l2 = fp8_gemv_lds_total(G, rmax, kc2);
+    const bool wg = fp8_gemv_ok(s, p);
     const long waves = rows * (s.F / 128);
+    if (wg) {
+        static bool attr = false;
+        if (!attr) {
+            const void *fns[] = {(const void *)fp8_gemv_kernel<true, 1>, (const void *)fp8_gemv_kernel<true, 2>,
+                                 (const void *)fp8_gemv_kernel<true, 4>, (const void *)fp8_gemv_kernel<false, 1>,
+                                 (const void *)fp8_gemv_kernel<false, 2>, (const void *)fp8_gemv_kernel<false, 4>};
+            for (const void *f : fns) {
+                hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 65536);
+                if (e != hipSuccess) return e;
+            }
+            attr = true;
+        }
+        // column quads per workgroup tile: longer weight streams per wave, while keeping about
+        // two workgroup tiles per CU (measured, 9 experts x 4096 x 7168: 42.6 us with one
+        // quad, 36 with two, 32.5 with four); every group's quad count (ntn / 4) is a
+        // multiple of the choice
+        auto qc_for = [&](int ntn) {
+            const long quads = (long)(grid_for(ntn).x) / 4;
+            int qc = quads >= 1536 ? 4 : quads >= 768 ? 2 : 1;
+            while ((ntn / 4) % qc) qc /= 2;
+            return qc;
+        };
+        auto launch = [&](bool lin1, int ntn, const DecArgs &args, size_t lds) {
+            const int qc = qc_for(ntn);
+            const unsigned tiles = (unsigned)((grid_for(ntn).x / 4 + qc - 1) / qc), cap = 256 * 4;
+            const dim3 grid(tiles < cap ? tiles : cap);
+            const char *name = lin1 ? "linear1" : "linear2";
+            if (lin1) {
+                if (qc == 4) MOE_LAUNCH(name, (fp8_gemv_kernel<true, 4>), grid, dim3(256), lds, st, args, rmax, ntn);
+                else if (qc == 2) MOE_LAUNCH(name, (fp8_gemv_kernel<true, 2>), grid, dim3(256), lds, st, args, rmax, ntn);
+                else MOE_LAUNCH(name, (fp8_gemv_kernel<true, 1>), grid, dim3(256), lds, st, args, rmax, ntn);
+            } else {
+                if (qc == 4) MOE_LAUNCH(name, (fp8_gemv_kernel<false, 4>), grid, dim3(256), lds, st, args, rmax, ntn);
+                else if (qc == 2) MOE_LAUNCH(name, (fp8_gemv_kernel<false, 2>), grid, dim3(256), lds, st, args, rmax, ntn);
+                else MOE_LAUNCH(name, (fp8_gemv_kernel<false, 1>), grid, dim3(256), lds, st, args, rmax, ntn);
+            }
+        };
+        launch(true, p.ntn1, a1, l1);
+        MOE_LAUNCH("swiglu_quant", fp8_decode_swiglu_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st,
+                   (const float *)upart, rows, s.F, p.ks, h, hs);
+        launch(false, p.ntn2, a2, l2);
+        return hipGetLastError();
+    }
+    MOE_LAUNCH("linear1", fp8_decode_kernel<true>, grid_for(p.ntn1), dim3(64), 0, st, a1);
     MOE_LAUNCH("swiglu_quant", fp8_decode_swiglu_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st,
                (const float *)upart, rows, s.F, p.ks, h, hs);
-    DecArgs a2 = {h, hs, nullptr, offsets, ts2, w2, w2s, nullptr, (uint16_t *)y_perm, rows, s.T, s.k, s.F, s.d, G, 1};
     MOE_LAUNCH("linear2", fp8_decode_kernel<false>, grid_for(p.ntn2), dim3(64), 0, st, a2);
     return hipGetLastError();
 }

@@ -730,7 +730,9 @@ struct DecArgs {
 // hold rows of two row tiles, finished by different waves).  Every other input is read
 // through the caches: each of its lines has a single writer, which finished before any
 // reader was let in, so no cache can hold an older copy.
-template <bool LIN1, bool COH>
+// PF: the next block's loads are issued before this block's MFMAs (two blocks in flight
+// per wave, about 220 VGPRs); without PF one block at a time, for register-capped callers.
+template <bool LIN1, bool COH, bool PF = false>
 __device__ __forceinline__ void fp8_decode_tile(const DecArgs &a, int tile, const int32_t *ts, const int32_t *offs) {
     int lo = 0, hi = a.G - 1;
     while (lo < hi) {
@@ -758,27 +760,60 @@ __device__ __forceinline__ void fp8_decode_tile(const DecArgs &a, int tile, cons
 
     f32x16 acc = (f32x16){};
     int k0 = kbeg;
-    for (; k0 + 256 <= kend; k0 += 256) {
+    // 256 of K per block (four MFMAs)
+    struct Blk {
         i32x4 alo[4], ahi[4], bq[4];
+        uint32_t sb01, sb23;
+        float sa01, sa23;
+    };
+    auto load = [&](Blk &b, int kb) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int kk = k0 + 64 * u;
+            const int kk = kb + 64 * u;
             // fp8 A operand: K {16 kh..+15} and {32 + 16 kh..+15} of the 64-wide step
-            alo[u] = *(const i32x4 *)(a.A + arow + kk + 16 * kh);
-            ahi[u] = *(const i32x4 *)(a.A + arow + kk + 32 + 16 * kh);
+            b.alo[u] = *(const i32x4 *)(a.A + arow + kk + 16 * kh);
+            b.ahi[u] = *(const i32x4 *)(a.A + arow + kk + 32 + 16 * kh);
             // fp4 B operand: 32 consecutive K from 32 kh, one e8m0 block
-            bq[u] = *(const i32x4 *)(pb + (kk + 32 * kh) / 2);
+            b.bq[u] = *(const i32x4 *)(pb + (kk + 32 * kh) / 2);
         }
-        const uint32_t sb01 = *(const uint32_t *)(psb + k0 / 32), sb23 = *(const uint32_t *)(psb + k0 / 32 + 4);
-        const float sa01 = ldc<COH && !LIN1>(psa + k0 / 128), sa23 = ldc<COH && !LIN1>(psa + k0 / 128 + 1);
+        b.sb01 = *(const uint32_t *)(psb + kb / 32);
+        b.sb23 = *(const uint32_t *)(psb + kb / 32 + 4);
+        b.sa01 = ldc<COH && !LIN1>(psa + kb / 128);
+        b.sa23 = ldc<COH && !LIN1>(psa + kb / 128 + 1);
+    };
+    auto mma = [&](const Blk &b) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            i32x8 av = {alo[u][0], alo[u][1], alo[u][2], alo[u][3], ahi[u][0], ahi[u][1], ahi[u][2], ahi[u][3]};
-            i32x8 bv = {bq[u][0], bq[u][1], bq[u][2], bq[u][3], 0, 0, 0, 0};
-            const uint32_t sbw = u < 2 ? sb01 : sb23;
+            i32x8 av = {b.alo[u][0], b.alo[u][1], b.alo[u][2], b.alo[u][3],
+                        b.ahi[u][0], b.ahi[u][1], b.ahi[u][2], b.ahi[u][3]};
+            i32x8 bv = {b.bq[u][0], b.bq[u][1], b.bq[u][2], b.bq[u][3], 0, 0, 0, 0};
+            const uint32_t sbw = u < 2 ? b.sb01 : b.sb23;
             const int sb = (int)((sbw >> (8 * (2 * (u & 1) + kh))) & 0xFF);
-            const int sa = (int)((__float_as_uint(u < 2 ? sa01 : sa23) >> 23) & 0xFF);
+            const int sa = (int)((__float_as_uint(u < 2 ? b.sa01 : b.sa23) >> 23) & 0xFF);
             acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 4, 0, sa, 0, sb);
+        }
+    };
+    const int nblk = (kend - kbeg) / 256;
+    if (!PF) {
+        for (int i = 0; i < nblk; ++i, k0 += 256) {
+            Blk b0;
+            load(b0, k0);
+            mma(b0);
+        }
+    } else if (nblk > 0) {
+        Blk b0, b1;
+        load(b0, k0);
+        int i = 0;
+        for (; i + 2 <= nblk; i += 2) {
+            if (i + 1 < nblk) load(b1, k0 + 256);
+            mma(b0);
+            if (i + 2 < nblk) load(b0, k0 + 512);
+            mma(b1);
+            k0 += 512;
+        }
+        if (i < nblk) {  // odd count: b0 holds the last block
+            mma(b0);
+            k0 += 256;
         }
     }
     for (; k0 < kend; k0 += 64) {
@@ -798,6 +833,135 @@ __device__ __forceinline__ void fp8_decode_tile(const DecArgs &a, int tile, cons
         const long orow = row0 + row;
         if (LIN1) stc<COH>(a.part + ((long)ksl * a.rows + orow) * a.N + n, acc[q]);
         else stc16<COH>(a.Y, (size_t)(orow * a.N + n), f32_to_bf16(acc[q]));
+    }
+}
+
+// Workgroup form of the decode tile (unfused path): four waves share one (group, 32-row
+// tile, K slice) and take four neighbouring 32-column tiles, so workgroup tile w covers
+// wave tiles whose order matches fp8_decode_tile's (row tile fastest, then K slice, then
+// column tile) -- every group has a multiple of 4 column tiles, so the group's first
+// workgroup tile is ts[g] / 4.  The group's activation rows for the K slice (at most rmax
+// rows: a group never holds more rows than there are tokens) are copied into LDS by DMA,
+// issued together with the column's e8m0 scales for the slice and the first weight blocks,
+// so their latencies overlap; the weights then are the only global loads, D = 4 blocks of
+// 256 K ahead through a register ring (about 16 KB in flight per wave), running across the
+// QC column quads of the tile.  The tile plan
+// (tile starts and group offsets) sits in LDS, built once per workgroup.  The MFMA
+// operands and their order per K slice are those of fp8_decode_tile: results are identical
+// bit for bit.  K / ks is a multiple of 1024 and at most 2048.
+__host__ __device__ constexpr size_t fp8_gemv_lds(int G, int rmax, int kc) {
+    return (size_t)2 * (G + 1) * 4 + (size_t)rmax * (kc + 16) + (size_t)rmax * (kc / 128) * 4;
+}
+// the tile plan is built in the same LDS before the rows are staged (scan scratch included)
+__host__ __device__ constexpr size_t fp8_gemv_lds_total(int G, int rmax, int kc) {
+    const size_t a = fp8_gemv_lds(G, rmax, kc), b = (size_t)2 * (G + 1) * 4 + 256 * 4;
+    return a > b ? a : b;
+}
+
+// lds: fp8_gemv_lds(G, rmax, K / ks) bytes; plan[] = tile starts then offsets, loaded.
+// QC column quads (4 x 32 columns each) per workgroup tile: the weight ring runs across
+// them, one accumulator per quad, and the stores come at the end.
+template <bool LIN1, int QC>
+__device__ __forceinline__ void fp8_gemv_tile(const DecArgs &a, int wt, int rmax, const int32_t *plan,
+                                              uint8_t *lds) {
+    constexpr int D = 4;
+    const int32_t *ts = plan, *offs = plan + a.G + 1;
+    int lo = 0, hi = a.G - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (ts[mid] / (4 * QC) <= wt) lo = mid; else hi = mid - 1;
+    }
+    const int g = lo;
+    const int rb = offs[g], cnt = offs[g + 1] - rb;
+    const int mtiles = (cnt + 31) / 32, local = wt - ts[g] / (4 * QC);
+    const int mt = local % mtiles, rest = local / mtiles;
+    const int ksl = rest % a.ks, qc = rest / a.ks;
+    const int row0 = rb + mt * 32;
+    int nrows = min(32, cnt - mt * 32);
+    nrows = nrows < rmax ? nrows : rmax;  // rmax >= nrows whenever the routing is valid
+    const int kc = a.K / a.ks, kbeg = ksl * kc, RS = kc + 16, nsc = kc / 128;
+    uint8_t *la = lds + (size_t)2 * (a.G + 1) * 4;
+    float *lsa = (float *)(la + (size_t)rmax * RS);
+    const int lane = lane_id(), kh = lane >> 5, r = lane & 31, wave = threadIdx.x >> 6;
+
+    // 1. activation rows of the slice: one 1 KB DMA per (row, chunk), rows dealt to waves
+    for (int rw = wave; rw < nrows; rw += 4) {
+        const long src = LIN1 ? row_token(row0 + rw, a.row_to_slot, a.T, a.k) : (long)row0 + rw;
+        for (int c = 0; c < kc / 1024; ++c)
+            lds_dma16(a.A + (size_t)src * a.K + kbeg + c * 1024 + lane * 16, la + rw * RS + c * 1024);
+    }
+    float sav = 0.0f;  // this thread's activation scale, if any
+    const int sidx = threadIdx.x;
+    if (sidx < nrows * nsc) {
+        const int rw = sidx / nsc, j = sidx % nsc;
+        const long src = LIN1 ? row_token(row0 + rw, a.row_to_slot, a.T, a.k) : (long)row0 + rw;
+        sav = a.As[src * (a.K / 128) + kbeg / 128 + j];
+    }
+    // 2. weight blocks (4 x 16 B codes and 2 scale dwords per lane) through the ring: block t
+    // of the tile is block t % nb of quad t / nb
+    const int nb = kc / 256, nbt = QC * nb;
+    const long n0 = (long)(4 * qc * QC + wave) * 32 + r;  // this lane's column in quad 0
+    i32x4 bq[D][4];
+    uint32_t sbw[D][2];
+#define GEMV_LOAD(slot, t_)                                                                         \
+    do {                                                                                            \
+        const int tt_ = (t_) < nbt ? (t_) : nbt - 1;                                                \
+        const int c_ = tt_ / nb, i_ = tt_ % nb;                                                     \
+        const long n_ = n0 + (long)c_ * 128;                                                        \
+        const uint8_t *pb_ = a.B + ((long)g * a.N + n_) * (a.K / 2) + kbeg / 2 + i_ * 128;          \
+        const uint8_t *ps_ = a.Bs + ((long)g * a.N + n_) * (a.K / 32) + kbeg / 32 + i_ * 8;         \
+        _Pragma("unroll") for (int u = 0; u < 4; ++u) bq[slot][u] = *(const i32x4 *)(pb_ + 32 * u + 16 * kh); \
+        sbw[slot][0] = *(const uint32_t *)(ps_);                                                    \
+        sbw[slot][1] = *(const uint32_t *)(ps_ + 4);                                                \
+    } while (0)
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j) GEMV_LOAD(j, j);
+    // everything but the weight blocks has landed (loads complete in order)
+    wait_vmcnt<(D - 1) * 6>();
+    if (sidx < nrows * nsc) lsa[sidx] = sav;
+    __syncthreads();
+
+    const int rr = r < nrows ? r : 0;
+    const uint8_t *arow = la + rr * RS;
+    const float *asr = lsa + rr * nsc;
+    f32x16 acc[QC];
+#pragma unroll
+    for (int c = 0; c < QC; ++c) acc[c] = (f32x16){};
+    // nb is a multiple of D, so block t sits in ring slot t % D = j
+#pragma unroll
+    for (int c = 0; c < QC; ++c) {
+        for (int i0 = 0; i0 < nb; i0 += D) {
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                const int i = i0 + j, t = c * nb + i;
+                GEMV_LOAD((j + D - 1) % D, t + D - 1);
+                wait_vmcnt<(D - 1) * 6>();  // block t landed: 6 loads per block, in order
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const i32x4 lo4 = *(const i32x4 *)(arow + i * 256 + 64 * u + 16 * kh);
+                    const i32x4 hi4 = *(const i32x4 *)(arow + i * 256 + 64 * u + 32 + 16 * kh);
+                    i32x8 av = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+                    i32x8 bv = {bq[j][u][0], bq[j][u][1], bq[j][u][2], bq[j][u][3], 0, 0, 0, 0};
+                    const int sb = (int)((sbw[j][u >> 1] >> (8 * (2 * (u & 1) + kh))) & 0xFF);
+                    const int sa = (int)((__float_as_uint(asr[2 * i + (u >> 1)]) >> 23) & 0xFF);
+                    acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[c], 0, 4, 0, sa, 0, sb);
+                }
+            }
+        }
+    }
+    wait_vmcnt<0>();
+#undef GEMV_LOAD
+#pragma unroll
+    for (int c = 0; c < QC; ++c) {
+        const long n = n0 + (long)c * 128;
+#pragma unroll
+        for (int qq = 0; qq < 16; ++qq) {
+            const int row = 8 * (qq >> 2) + 4 * kh + (qq & 3);
+            if (row >= nrows) continue;
+            const long orow = row0 + row;
+            if (LIN1) a.part[((long)ksl * a.rows + orow) * a.N + n] = acc[c][qq];
+            else a.Y[orow * a.N + n] = f32_to_bf16(acc[c][qq]);
+        }
     }
 }
 

@@ -40,8 +40,7 @@ hipError_t launch_route(const Shape &s, const void *x, const void *wr, const flo
 // dispatch: block histogram, scan, scatter; FP8 activation quantisation
 hipError_t launch_dispatch(const Shape &s, const int32_t *idx, int32_t *blockcounts, int32_t *counts,
                            int32_t *offsets, int32_t *slot_to_row, int32_t *row_to_slot, int32_t *err,
-                           hipStream_t st);
-hipError_t launch_quant_x(const Shape &s, const uint16_t *x, uint8_t *xq, float *xs, hipStream_t st);
+                           const uint16_t *x, uint8_t *xq, float *xs, hipStream_t st);
 int dispatch_blocks(int T);
 
 // expert FFN
@@ -53,6 +52,8 @@ struct FfnPlan {
 };
 FfnPlan ffn_plan(const Shape &s);
 size_t ffn_partial_bytes(const Shape &s);  // decode: fp32 linear1 partials [ks][rows][2F]
+// FP8 decode: the workgroup kernels run (and need no tile plan from tile_plan)
+bool fp8_gemv_ok(const Shape &s, const FfnPlan &p);
 hipError_t launch_ffn(const Shape &s, const FfnPlan &p, const void *w1, const void *w1s, const void *w2,
                       const void *w2s, const void *x, const uint8_t *xq, const float *xs, const int32_t *offsets,
                       const int32_t *row_to_slot, void *h, float *hs, void *y_perm, int32_t *tile_start,
