@@ -262,7 +262,11 @@ def main():
     kernels = {n: {"launches_per_step": c / args.steps, "mean_ms": t / c} for n, (c, t) in prof.items()}
     log("kernels: " + ", ".join(f"{n} {v['mean_ms']:.4f}ms" for n, v in kernels.items()))
 
-    counts_np = counts.cpu().numpy()
+    if "fused" in timed:
+        counts_np = counts.cpu().numpy()  # written by the persistent kernel's steps
+    else:  # one more (untimed) unfused step for the per-group row counts
+        _, routing = moe.layer_unfused(cfg, x, wr, w1, w2, w1s, w2s, bias, ws=ws)
+        counts_np = routing["counts"].cpu().numpy()
     f_exp, f_rt = flops_of(w)
     tflops = (f_exp + f_rt) / (ms * 1e-3) / 1e12
     tok_s = w.T / (ms * 1e-3)

@@ -134,23 +134,23 @@ __device__ __forceinline__ void route_valu_token(const void *__restrict__ xv, co
 #pragma unroll
                 for (int u = 0; u < V; ++u) xs[u] = bf16_to_f32(h[u]);
             }
+            // unconditional loads (rows past E re-read row E-1 into accumulators that are
+            // dropped), so that all CH loads of a step are in flight together
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
-                int e = e0 + c;
-                if (e < E) {
-                    float ws[V];
-                    if (F32) {
-                        float4 q = *(const float4 *)((const float *)wv + (long)e * d + i0);
-                        ws[0] = q.x; ws[1] = q.y; ws[2] = q.z; ws[3] = q.w;
-                    } else {
-                        uint4 q = *(const uint4 *)((const uint16_t *)wv + (long)e * d + i0);
-                        const uint16_t *h = (const uint16_t *)&q;
+                const int e = e0 + c < E ? e0 + c : E - 1;
+                float ws[V];
+                if (F32) {
+                    float4 q = *(const float4 *)((const float *)wv + (long)e * d + i0);
+                    ws[0] = q.x; ws[1] = q.y; ws[2] = q.z; ws[3] = q.w;
+                } else {
+                    uint4 q = *(const uint4 *)((const uint16_t *)wv + (long)e * d + i0);
+                    const uint16_t *h = (const uint16_t *)&q;
 #pragma unroll
-                        for (int u = 0; u < V; ++u) ws[u] = bf16_to_f32(h[u]);
-                    }
-#pragma unroll
-                    for (int u = 0; u < V; ++u) acc[c] = fmaf(xs[u], ws[u], acc[c]);
+                    for (int u = 0; u < V; ++u) ws[u] = bf16_to_f32(h[u]);
                 }
+#pragma unroll
+                for (int u = 0; u < V; ++u) acc[c] = fmaf(xs[u], ws[u], acc[c]);
             }
         }
 #pragma unroll
