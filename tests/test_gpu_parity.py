@@ -35,6 +35,14 @@ SMALL = {
     "fp8_decode_1": Workload("fp8_decode_1", 2008, "fp8_mxfp4", 1, 512, 64, 8, 256, 1, "softmax"),
     "fp8_decode_5": Workload("fp8_decode_5", 2009, "fp8_mxfp4", 5, 512, 64, 8, 256, 1, "softmax"),
     "bf16_decode_3": Workload("bf16_decode_3", 2010, "bf16", 3, 256, 32, 4, 256, 1, "sigmoid"),
+    # workgroup weight-streaming kernels (K slices of 1024): several rows per group, one to
+    # four 128-column groups per workgroup tile
+    "fp8_decode_wg_3": Workload("fp8_decode_wg_3", 2011, "fp8_mxfp4", 3, 2048, 64, 8, 1024, 1, "softmax"),
+    "fp8_decode_wg_7": Workload("fp8_decode_wg_7", 2012, "fp8_mxfp4", 7, 2048, 64, 8, 1024, 1, "sigmoid",
+                                zipf_alpha=0.25),
+    # the router as a tiled GEMM (E a multiple of 256, T >= 2048) with a ragged last token tile
+    "bf16_router_tiled": Workload("bf16_router_tiled", 2013, "bf16", 2100, 512, 256, 8, 128, 1, "sigmoid",
+                                  zipf_alpha=0.25),
 }
 
 
