@@ -213,6 +213,31 @@ __device__ __forceinline__ int pick_tile(int b, int total) {
     return (j < per && t < total) ? t : -1;
 }
 
+// Tail split of a launch of 256-row tiles.  Workgroups are dealt to the eight XCDs round
+// robin (block b runs on XCD b % 8) and pick_tile gives each XCD a contiguous chunk of the
+// tiles.  An XCD runs C such workgroups at a time (one per CU), so a chunk of n tiles takes
+// ceil(n / C) rounds and a last round of n % C tiles leaves CUs idle.  When that round has
+// at most C / 2 tiles, each of them runs as two 128-row halves instead: still one round,
+// but a shorter one.  Returns the tile, or -1, and sets half to -1 (the whole tile), 0 (its
+// rows 0..127) or 1 (its rows 128..255).  Blocks needed per XCD: at most ceil(total / 8) +
+// C / 2.
+__host__ __device__ __forceinline__ int pick_tile_split(int b, int total, int C, int &half) {
+    const int xcd = b & 7, j = b >> 3;
+    const int per = (total + 7) >> 3;
+    const int base = xcd * per, n = per < total - base ? per : total - base;
+    half = -1;
+    if (n <= 0) return -1;
+    const int r = n % C, full = n - r;
+    if (j < full) return base + j;
+    if (2 * r <= C) {
+        const int q = j - full;
+        if (q >= 2 * r) return -1;
+        half = q & 1;
+        return base + full + (q >> 1);
+    }
+    return j < n ? base + j : -1;
+}
+
 struct TileInfo {
     int g, row0, nrows, nt, mt;  // group, first row, valid rows, N tile, row tile within the group
 };

@@ -21,11 +21,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     if (tile >= 0) bf16_tile<BM, BN, SWIGLU, GATHER>(a, tile, lds);
 }
 
+// xcd_cus: CUs per XCD (one workgroup per CU), for the tail split
 template <bool SWIGLU, bool GATHER>
-__global__ __launch_bounds__(512) void gemm_bf16_kernel8(GemmArgs a) {
+__global__ __launch_bounds__(512) void gemm_bf16_kernel8(GemmArgs a, int xcd_cus) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int tile = pick_tile(blockIdx.x, a.tile_start[a.G]);
-    if (tile >= 0) bf16_tile8<SWIGLU, GATHER>(a, tile, lds);
+    int half;
+    const int tile = pick_tile_split(blockIdx.x, a.tile_start[a.G], xcd_cus, half);
+    if (tile >= 0) bf16_tile8<SWIGLU, GATHER>(a, tile, lds, half);
 }
 
 __global__ __launch_bounds__(256) void ffn1_f32_kernel(const float *__restrict__ x, const int32_t *__restrict__ r2s,
@@ -96,9 +98,23 @@ static hipError_t launch_gemm(const char *name, dim3 grid, const GemmArgs &a, hi
     return hipGetLastError();
 }
 
-// 256 x 256 tiles: the 8-wave kernel
+// CUs per XCD of the current device (eight XCDs)
+int xcd_cus() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (!cached[dev]) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cached[dev] = cus / 8 > 0 ? cus / 8 : 1;
+    }
+    return cached[dev];
+}
+
+// 256 x 256 tiles: the 8-wave kernel.  ub: an upper bound of the tile count; the grid adds
+// the blocks of the tail split.
 template <bool SWIGLU, bool GATHER>
-static hipError_t launch_gemm8(const char *name, dim3 grid, const GemmArgs &a, hipStream_t st) {
+static hipError_t launch_gemm8(const char *name, long ub, const GemmArgs &a, hipStream_t st) {
     constexpr size_t lds = bf16_tile8_lds();
     static bool attr = false;
     if (!attr) {
@@ -107,7 +123,10 @@ static hipError_t launch_gemm8(const char *name, dim3 grid, const GemmArgs &a, h
         if (e != hipSuccess) return e;
         attr = true;
     }
-    MOE_LAUNCH(name, (gemm_bf16_kernel8<SWIGLU, GATHER>), grid, dim3(512), lds, st, a);
+    const int C = xcd_cus();
+    if (C <= 0) return hipErrorInvalidDevice;
+    const dim3 grid((unsigned)(8 * ((ub + 7) / 8 + C / 2)));
+    MOE_LAUNCH(name, (gemm_bf16_kernel8<SWIGLU, GATHER>), grid, dim3(512), lds, st, a, C);
     return hipGetLastError();
 }
 
@@ -149,10 +168,11 @@ hipError_t launch_ffn(const Shape &s, const FfnPlan &p, const void *w1, const vo
     GemmArgs a2 = {(const uint16_t *)h, nullptr, (const uint16_t *)w2, (uint16_t *)y_perm, offsets, ts2,
                    s.T, s.k, s.F, s.d, s.d, G, s.F};
     hipError_t e;
-    if (p.bm1 == 256) e = launch_gemm8<true, true>("linear1", grid_for(p.bm1, ntn1), a1, st);
+    auto ub_for = [&](int bm, int ntn) { return ((rows + bm - 1) / bm + (G < rows ? G : rows)) * (long)ntn; };
+    if (p.bm1 == 256) e = launch_gemm8<true, true>("linear1", ub_for(p.bm1, ntn1), a1, st);
     else e = launch_gemm<128, 256, true, true>("linear1", grid_for(p.bm1, ntn1), a1, st);
     if (e != hipSuccess) return e;
-    if (p.bm2 == 256 && p.bn2 == 256) e = launch_gemm8<false, false>("linear2", grid_for(p.bm2, ntn2), a2, st);
+    if (p.bm2 == 256 && p.bn2 == 256) e = launch_gemm8<false, false>("linear2", ub_for(p.bm2, ntn2), a2, st);
     else if (p.bn2 == 256) e = launch_gemm<128, 256, false, false>("linear2", grid_for(p.bm2, ntn2), a2, st);
     else if (p.bm2 == 256) e = launch_gemm<256, 128, false, false>("linear2", grid_for(p.bm2, ntn2), a2, st);
     else e = launch_gemm<128, 128, false, false>("linear2", grid_for(p.bm2, ntn2), a2, st);

@@ -431,9 +431,16 @@ __device__ __forceinline__ void bf16_tile8_rows(const GemmArgs &a, const TileInf
     else bf16_tile8_core<SWIGLU, GATHER, F32OUT, 1>(a, ti, lda, k0, nk, lds);
 }
 
+// half: -1 the whole tile, 0 / 1 its rows 0..127 / 128..255 (an empty half returns at once);
+// every output element takes the same k order either way, so the bits do not change
 template <bool SWIGLU, bool GATHER>
-__device__ __forceinline__ void bf16_tile8(const GemmArgs &a, int tile, uint8_t *lds) {
-    const TileInfo ti = decode_tile(tile, a.tile_start, a.offsets, a.G, 256);
+__device__ __forceinline__ void bf16_tile8(const GemmArgs &a, int tile, uint8_t *lds, int half = -1) {
+    TileInfo ti = decode_tile(tile, a.tile_start, a.offsets, a.G, 256);
+    if (half >= 0) {
+        ti.row0 += 128 * half;
+        ti.nrows = half ? ti.nrows - 128 : min(ti.nrows, 128);
+        if (ti.nrows <= 0) return;
+    }
     bf16_tile8_rows<SWIGLU, GATHER, false>(a, ti, a.K, 0, a.K / 32, lds);
 }
 
