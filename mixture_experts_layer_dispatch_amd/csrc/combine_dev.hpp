@@ -26,8 +26,7 @@ __device__ __forceinline__ void combine_lane(const void *__restrict__ yp, const 
     float acc[V];
 #pragma unroll
     for (int u = 0; u < V; ++u) acc[u] = 0.0f;
-    auto add_row = [&](long r, float g, bool scale) {
-        const i32x4 q = ldc16<COH>(yp, (size_t)(r * d + c) * (F32 ? 4 : 2));
+    auto add_row = [&](const i32x4 &q, float g, bool scale) {
         if constexpr (F32) {
             float v[4] = {__int_as_float(q[0]), __int_as_float(q[1]), __int_as_float(q[2]), __int_as_float(q[3])};
 #pragma unroll
@@ -40,12 +39,32 @@ __device__ __forceinline__ void combine_lane(const void *__restrict__ yp, const 
             }
         }
     };
-    for (int j = 0; j < k; ++j) {
-        long r = ldc<COH>(s2r + t * k + j);
-        r = r < 0 ? 0 : (r >= tk ? tk - 1 : r);
-        add_row(r, ldc<COH>(gate + t * k + j), true);
+    // All loads of a chunk of choices are issued before any is used (clamped, unconditional:
+    // a load under a branch would be waited for before the branch joins), the shared row's
+    // with the first chunk; the additions keep the fixed order.
+    constexpr int CH = 8;
+    const size_t esz = F32 ? 4 : 2;
+    const i32x4 qs = S ? ldc16<COH>(yp, (size_t)((tk + t) * d + c) * esz) : (i32x4){0, 0, 0, 0};
+    for (int j0 = 0; j0 < k; j0 += CH) {
+        long r[CH];
+        float g[CH];
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const int j = j0 + u < k ? j0 + u : k - 1;
+            r[u] = ldc<COH>(s2r + t * k + j);
+            g[u] = ldc<COH>(gate + t * k + j);
+        }
+        i32x4 q[CH];
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const long rr = r[u] < 0 ? 0 : (r[u] >= tk ? tk - 1 : r[u]);
+            q[u] = ldc16<COH>(yp, (size_t)(rr * d + c) * esz);
+        }
+#pragma unroll
+        for (int u = 0; u < CH; ++u)
+            if (j0 + u < k) add_row(q[u], g[u], true);
     }
-    if (S) add_row(tk + t, 1.0f, false);
+    if (S) add_row(qs, 1.0f, false);
     if constexpr (F32) {
         *(float4 *)((float *)y + t * d + c) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     } else {

@@ -29,8 +29,8 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t *__
 }
 
 // One dispatch block (T <= 256 tokens): workgroup 0 runs histogram, scan and scatter in
-// one pass (device-coherent accesses, as its own stores are read back), the others
-// quantise x to e4m3 (an independent job; none when xq is null).
+// one pass through LDS, the others quantise x to e4m3 (an independent job; none when xq
+// is null).
 __global__ __launch_bounds__(256) void dispatch_one_kernel(const int32_t *__restrict__ idx, int T, int k, int E,
                                                           int S, int32_t *__restrict__ blockcounts,
                                                           int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
@@ -45,13 +45,7 @@ __global__ __launch_bounds__(256) void dispatch_one_kernel(const int32_t *__rest
             quant_x_lane<false>(x, nq, xq, xs, gid);
         return;
     }
-    count_block<true>(idx, T, k, E, 0, (unsigned long long *)lds, blockcounts, err);
-    wait_vmcnt<0>();
-    __syncthreads();
-    dispatch_scan_block<true>(blockcounts, 1, T, E, S, counts, offsets, (int32_t *)lds);
-    wait_vmcnt<0>();
-    __syncthreads();
-    scatter_block<true>(idx, T, k, E, 0, blockcounts, slot_to_row, row_to_slot, (unsigned long long *)lds);
+    dispatch_single_block<false>(idx, T, k, E, S, counts, offsets, slot_to_row, row_to_slot, err, lds);
 }
 
 // Histogram of one dispatch block per workgroup; workgroups past nblk quantise x.
@@ -82,7 +76,7 @@ hipError_t launch_dispatch(const Shape &s, const int32_t *idx, int32_t *blockcou
     // quantisation workgroups: 16 lanes per 128-wide block, up to 4 blocks' worth per lane
     const long qwg = nq ? (nq * 16 + 1023) / 1024 : 0;
     if (nblk == 1) {
-        const size_t l1 = lds > (size_t)(1024 + 256) * 4 ? lds : (size_t)(1024 + 256) * 4;
+        const size_t l1 = lds + (size_t)(s.E + 256) * 4;
         MOE_LAUNCH("dispatch", dispatch_one_kernel, dim3((unsigned)(1 + qwg)), dim3(256), l1, st, idx, s.T, s.k, s.E,
                    s.S, blockcounts, counts, offsets, slot_to_row, row_to_slot, err, x, nq, xq, xs);
         return hipGetLastError();

@@ -207,6 +207,67 @@ __device__ __forceinline__ void scatter_block(const int32_t *__restrict__ idx, i
     }
 }
 
+// One dispatch block (T <= 256) by one workgroup: histogram, scan and scatter with the
+// per-expert counts and bases kept in LDS, so the choices are loaded once (kept in
+// registers) and counts, offsets and both permutations are stored once -- no global
+// round trip between the steps.  Same results as count_block + dispatch_scan_block +
+// scatter_block on one block.  lds: 4 E words of masks, then E + 256 ints.
+template <bool COH>
+__device__ __forceinline__ void dispatch_single_block(const int32_t *__restrict__ idx, int T, int k, int E, int S,
+                                                      int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                                                      int32_t *__restrict__ slot_to_row,
+                                                      int32_t *__restrict__ row_to_slot, int32_t *err,
+                                                      uint8_t *lds) {
+    unsigned long long *masks = (unsigned long long *)lds;
+    int32_t *base = (int32_t *)(masks + 4 * E), *tmp = base + E;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+    const bool live = tid < T;
+    int ids[kMaxChoices];
+    uint32_t ok = 0;
+    if (live) {
+        bool bad, dup;
+        ok = load_choices<COH>(idx, tid, k, E, ids, bad, dup);
+        if (bad) set_error(err, DEVERR_INDEX);
+        if (dup) set_error(err, DEVERR_DUP);
+    }
+    for (int i = tid; i < 4 * E; i += blockDim.x) masks[i] = 0ull;
+    __syncthreads();
+    if (live) {
+#pragma unroll
+        for (int j = 0; j < kMaxChoices; ++j)
+            if (ok >> j & 1u) atomicOr(&masks[wave * E + ids[j]], 1ull << lane);
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += blockDim.x) {
+        const int c = __popcll(masks[e]) + __popcll(masks[E + e]) + __popcll(masks[2 * E + e]) +
+                      __popcll(masks[3 * E + e]);
+        base[e] = c;
+        stc<COH>(counts + e, c);
+    }
+    __syncthreads();
+    const int routed = block_exclusive_scan(base, E, tmp);  // base[e] = offsets[e] now
+    for (int e = tid; e < E; e += blockDim.x) stc<COH>(offsets + e, base[e]);
+    if (tid == 0) {
+        stc<COH>(offsets + E, routed);
+        if (S) {
+            stc<COH>(counts + E, T);
+            stc<COH>(offsets + E + 1, routed + T);
+        }
+    }
+    if (!live) return;
+    const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int j = 0; j < kMaxChoices; ++j) {
+        if (!(ok >> j & 1u)) continue;
+        const int e = ids[j];
+        int rank = __popcll(masks[wave * E + e] & below);
+        for (int w = 0; w < wave; ++w) rank += __popcll(masks[w * E + e]);
+        const int row = base[e] + rank;
+        stc<COH>(slot_to_row + (long)tid * k + j, row);
+        stc<COH>(row_to_slot + row, (int32_t)((long)tid * k + j));
+    }
+}
+
 // ---- FP8 activation stage: x (bf16) -> e4m3 codes + power-of-two scale per 1x128 ----
 //
 // 16 lanes own one 128-value block (8 values each, one 16-byte load); gid is the global

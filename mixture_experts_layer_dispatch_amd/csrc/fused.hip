@@ -50,7 +50,8 @@ int fused_row_tiles(const Shape &s, const FfnPlan &p) {
 size_t fused_lds_bytes(const Shape &s, const FfnPlan &p) {
     const int kind = router_kind(s, route_splitk_slices(s));
     size_t b = gemm_lds(s, p);
-    const size_t r = router_lds(s, kind), m = (size_t)4 * s.E * 8, plan = (2 * 1032 + 256) * 4;
+    const size_t r = router_lds(s, kind), m = (size_t)4 * s.E * 8 + (size_t)(s.E + 256) * 4,
+                 plan = (2 * 1032 + 256) * 4;
     const size_t cached = p.decode ? (size_t)3 * (s.G() + 1) * 4 : 0;  // the plan, kept in LDS
     for (size_t v : {r, m, plan, cached}) b = v > b ? v : b;
     return b;

@@ -213,24 +213,21 @@ __device__ __forceinline__ void front_item(const FusedArgs &a, long i, uint8_t *
                           a.err);
         wg_count(a.sync, CNT_COUNT, i - a.b_cnt);
     } else if (i == a.b_plan) {  // scan, tile plans, cleared row-tile counters
+        int32_t *sh = (int32_t *)lds;
         if (a.nblk == 1) {
-            // one dispatch block: histogram, scan, plan and scatter in this one item
+            // one dispatch block: histogram, scan and scatter through LDS, then the plan
             if (a.router == ROUTER_SPLITK) wg_counter_wait(a.sync, CNT_SELECT, a.T, a.err);
             else wg_counter_wait(a.sync, CNT_ROUTE, nr, a.err);
-            count_block<true>(a.idx, a.T, a.k, a.E, 0, (unsigned long long *)lds, a.blockcounts, a.err);
+            dispatch_single_block<true>(a.idx, a.T, a.k, a.E, a.S, a.counts, a.offsets, a.s2r, a.r2s, a.err, lds);
             wait_vmcnt<0>();
             __syncthreads();
         } else {
             wg_counter_wait(a.sync, CNT_COUNT, a.nblk, a.err);
+            dispatch_scan_block<true>(a.blockcounts, a.nblk, a.T, a.E, a.S, a.counts, a.offsets, sh);
         }
-        int32_t *sh = (int32_t *)lds;
-        dispatch_scan_block<true>(a.blockcounts, a.nblk, a.T, a.E, a.S, a.counts, a.offsets, sh);
         tile_plan_block<true>(a.offsets, a.G, a.bm, a.ntn1, a.bm, a.ntn2, a.ts1, a.ts2, sh);
         for (long m = threadIdx.x; m < (long)a.nm * kRowTileSlots; m += blockDim.x) stc<true>(a.done1 + m * kSlot, 0);
         if (a.nblk == 1) {
-            wait_vmcnt<0>();
-            __syncthreads();
-            scatter_block<true>(a.idx, a.T, a.k, a.E, 0, a.blockcounts, a.s2r, a.r2s, (unsigned long long *)lds);
             wg_counter_wait(a.sync, CNT_QUANT, (int)a.b_r, a.err);
             wg_flag_raise(a.sync, FLAG_FRONT);
         } else {

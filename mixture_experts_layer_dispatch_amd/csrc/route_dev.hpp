@@ -257,17 +257,35 @@ __device__ __forceinline__ void route_splitk_wave(const uint16_t *__restrict__ x
     const uint16_t *xa = x + trow * d + k0 + 8 * (lane >> 5);
     const uint16_t *wb = wr + (long)(et * 32 + (lane & 31)) * d + k0 + 8 * (lane >> 5);
     f32x16 acc = (f32x16){};
-    for (int kk = 0; kk < kchunk; kk += 64) {
-        u32x4 av[4], bv[4];
+    // the next 64-wide step's loads are issued before this step's MFMAs
+    u32x4 av[2][4], bv[2][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        av[0][u] = *(const u32x4 *)(xa + 16 * u);
+        bv[0][u] = *(const u32x4 *)(wb + 16 * u);
+    }
+    for (int kk = 0; kk < kchunk; kk += 128) {
+        const int k1 = kk + 64 < kchunk ? kk + 64 : kk;  // an odd last step re-reads (unused)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            av[u] = *(const u32x4 *)(xa + kk + 16 * u);
-            bv[u] = *(const u32x4 *)(wb + kk + 16 * u);
+            av[1][u] = *(const u32x4 *)(xa + k1 + 16 * u);
+            bv[1][u] = *(const u32x4 *)(wb + k1 + 16 * u);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[u]),
-                                                          __builtin_bit_cast(bf16x8, bv[u]), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[0][u]),
+                                                          __builtin_bit_cast(bf16x8, bv[0][u]), acc, 0, 0, 0);
+        if (kk + 64 >= kchunk) break;
+        const int k2 = kk + 128 < kchunk ? kk + 128 : kk;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            av[0][u] = *(const u32x4 *)(xa + k2 + 16 * u);
+            bv[0][u] = *(const u32x4 *)(wb + k2 + 16 * u);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[1][u]),
+                                                          __builtin_bit_cast(bf16x8, bv[1][u]), acc, 0, 0, 0);
     }
     // acc[r] = logit partial of token 8(r/4) + 4(lane/32) + r%4 of the tile, expert lane%32
 #pragma unroll
@@ -277,28 +295,32 @@ __device__ __forceinline__ void route_splitk_wave(const uint16_t *__restrict__ x
     }
 }
 
-// 256 threads, token t: thread e adds expert e's K slices in slice order, 16 loads in
-// flight at a time (unconditional, clamped loads: a load under a branch would be waited
-// for before the branch joins, serialising the slices); then wave 0 selects.  lg: E
-// floats of LDS.
+// Thread e's sum of expert e's K slices, in slice order, CH loads in flight at a time
+// (unconditional, clamped loads: a load under a branch would be waited for before the
+// branch joins, serialising the slices).
+template <bool COH, int CH>
+__device__ __forceinline__ float sum_slices(const float *__restrict__ part, int nks, int T, int E, long t, int e) {
+    float s = 0.0f;
+    for (int q0 = 0; q0 < nks; q0 += CH) {
+        float v[CH];
+#pragma unroll
+        for (int q = 0; q < CH; ++q) v[q] = ldc<COH>(part + ((long)min(q0 + q, nks - 1) * T + t) * E + e);
+#pragma unroll
+        for (int q = 0; q < CH; ++q)
+            if (q0 + q < nks) s += v[q];
+    }
+    return s;
+}
+
+// 256 threads, token t: thread e adds expert e's K slices (all of them in one round trip
+// when there are more than 16), then wave 0 selects.  lg: E floats of LDS.
 template <bool COH>
 __device__ __forceinline__ void route_sum_select(const float *__restrict__ part, int nks, int T, int E, int k,
                                                  int gating, const float *__restrict__ bias, long t, float *lg,
                                                  int32_t *idx, float *gate, float *logits, float *keys,
                                                  int32_t *err) {
-    constexpr int CH = 16;
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        float s = 0.0f;
-        for (int q0 = 0; q0 < nks; q0 += CH) {
-            float v[CH];
-#pragma unroll
-            for (int q = 0; q < CH; ++q) v[q] = ldc<COH>(part + ((long)min(q0 + q, nks - 1) * T + t) * E + e);
-#pragma unroll
-            for (int q = 0; q < CH; ++q)
-                if (q0 + q < nks) s += v[q];
-        }
-        lg[e] = s;
-    }
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        lg[e] = nks > 16 ? sum_slices<COH, 64>(part, nks, T, E, t, e) : sum_slices<COH, 16>(part, nks, T, E, t, e);
     __syncthreads();
     if (threadIdx.x < kWave) select_token<COH>(lg, E, k, gating, bias, t, idx, gate, logits, keys, err);
 }
