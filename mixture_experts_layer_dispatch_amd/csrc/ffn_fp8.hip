@@ -60,10 +60,15 @@ __global__ __launch_bounds__(64) void fp8_decode_kernel(DecArgs a) {
     for (int tile = blockIdx.x; tile < total; tile += gridDim.x) fp8_decode_tile<LIN1, false, true>(a, tile, a.tile_start, a.offsets);
 }
 
+// Weight ring depth (a divisor of the slice's blocks).  Measured on MI355X at decode shapes
+// (9 groups, T = 1): eight blocks in flight per wave instead of four did not stream faster
+// (linear2, 9 x 7168 x 2048: 19.4-22.9 us against 17.5-19.2 us), so four.
+constexpr int gemv_ring(int, int) { return 4; }
+
 // workgroup tiles: ts[G] / 4 of them
 // ntn: 32-column tiles per row tile and group (the K slices included).  The tile plan --
 // the prefix over groups of ceil(rows / 32) * ntn -- is built in LDS from the offsets.
-template <bool LIN1, int QC>
+template <bool LIN1, int QC, int NB>
 __global__ __launch_bounds__(256) void fp8_gemv_kernel(DecArgs a, int rmax, int ntn) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     int32_t *plan = (int32_t *)lds;  // tile starts, then group offsets
@@ -77,7 +82,7 @@ __global__ __launch_bounds__(256) void fp8_gemv_kernel(DecArgs a, int rmax, int 
     __syncthreads();
     const int total = plan[a.G] / (4 * QC);
     for (int wt = blockIdx.x; wt < total; wt += gridDim.x) {
-        fp8_gemv_tile<LIN1, QC>(a, wt, rmax, plan, lds);
+        fp8_gemv_tile<LIN1, QC, NB, gemv_ring(QC, NB)>(a, wt, rmax, plan, lds);
         __syncthreads();  // the next tile restages the LDS rows
     }
 }
@@ -100,6 +105,34 @@ bool fp8_gemv_ok(const Shape &s, const FfnPlan &p) {
            p.ntn2 % 4 == 0 && fp8_gemv_lds_total(G, rmax, kc1) <= 65536 && fp8_gemv_lds_total(G, rmax, kc2) <= 65536;
 }
 
+template <bool LIN1, int QC, int NB>
+static hipError_t launch_gemv(const char *name, dim3 grid, size_t lds, hipStream_t st, const DecArgs &a, int rmax,
+                              int ntn) {
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void *)fp8_gemv_kernel<LIN1, QC, NB>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 65536);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    MOE_LAUNCH(name, (fp8_gemv_kernel<LIN1, QC, NB>), grid, dim3(256), lds, st, a, rmax, ntn);
+    return hipGetLastError();
+}
+
+// qc column quads per workgroup tile (1, 2 or 4); nb 256-wide blocks per K slice (4 or 8)
+template <bool LIN1>
+static hipError_t launch_gemv_any(int qc, int nb, const char *name, dim3 grid, size_t lds, hipStream_t st,
+                                  const DecArgs &a, int rmax, int ntn) {
+    if (nb == 4) {
+        if (qc == 4) return launch_gemv<LIN1, 4, 4>(name, grid, lds, st, a, rmax, ntn);
+        if (qc == 2) return launch_gemv<LIN1, 2, 4>(name, grid, lds, st, a, rmax, ntn);
+        return launch_gemv<LIN1, 1, 4>(name, grid, lds, st, a, rmax, ntn);
+    }
+    if (qc == 4) return launch_gemv<LIN1, 4, 8>(name, grid, lds, st, a, rmax, ntn);
+    if (qc == 2) return launch_gemv<LIN1, 2, 8>(name, grid, lds, st, a, rmax, ntn);
+    return launch_gemv<LIN1, 1, 8>(name, grid, lds, st, a, rmax, ntn);
+}
+
 static hipError_t launch_fp8_decode(const Shape &s, const FfnPlan &p, const uint8_t *w1, const uint8_t *w1s,
                                     const uint8_t *w2, const uint8_t *w2s, const uint8_t *xq, const float *xs,
                                     const int32_t *offsets, const int32_t *row_to_slot, uint8_t *h, float *hs,
@@ -120,17 +153,6 @@ static hipError_t launch_fp8_decode(const Shape &s, const FfnPlan &p, const uint
     const bool wg = fp8_gemv_ok(s, p);
     const long waves = rows * (s.F / 128);
     if (wg) {
-        static bool attr = false;
-        if (!attr) {
-            const void *fns[] = {(const void *)fp8_gemv_kernel<true, 1>, (const void *)fp8_gemv_kernel<true, 2>,
-                                 (const void *)fp8_gemv_kernel<true, 4>, (const void *)fp8_gemv_kernel<false, 1>,
-                                 (const void *)fp8_gemv_kernel<false, 2>, (const void *)fp8_gemv_kernel<false, 4>};
-            for (const void *f : fns) {
-                hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 65536);
-                if (e != hipSuccess) return e;
-            }
-            attr = true;
-        }
         // column quads per workgroup tile: longer weight streams per wave, while keeping about
         // two workgroup tiles per CU (measured, 9 experts x 4096 x 7168: 42.6 us with one
         // quad, 36 with two, 32.5 with four); every group's quad count (ntn / 4) is a
@@ -142,25 +164,17 @@ static hipError_t launch_fp8_decode(const Shape &s, const FfnPlan &p, const uint
             return qc;
         };
         auto launch = [&](bool lin1, int ntn, const DecArgs &args, size_t lds) {
-            const int qc = qc_for(ntn);
+            const int qc = qc_for(ntn), nb = (lin1 ? kc1 : kc2) / 256;
             const unsigned tiles = (unsigned)((grid_for(ntn).x / 4 + qc - 1) / qc), cap = 256 * 4;
             const dim3 grid(tiles < cap ? tiles : cap);
-            const char *name = lin1 ? "linear1" : "linear2";
-            if (lin1) {
-                if (qc == 4) MOE_LAUNCH(name, (fp8_gemv_kernel<true, 4>), grid, dim3(256), lds, st, args, rmax, ntn);
-                else if (qc == 2) MOE_LAUNCH(name, (fp8_gemv_kernel<true, 2>), grid, dim3(256), lds, st, args, rmax, ntn);
-                else MOE_LAUNCH(name, (fp8_gemv_kernel<true, 1>), grid, dim3(256), lds, st, args, rmax, ntn);
-            } else {
-                if (qc == 4) MOE_LAUNCH(name, (fp8_gemv_kernel<false, 4>), grid, dim3(256), lds, st, args, rmax, ntn);
-                else if (qc == 2) MOE_LAUNCH(name, (fp8_gemv_kernel<false, 2>), grid, dim3(256), lds, st, args, rmax, ntn);
-                else MOE_LAUNCH(name, (fp8_gemv_kernel<false, 1>), grid, dim3(256), lds, st, args, rmax, ntn);
-            }
+            return lin1 ? launch_gemv_any<true>(qc, nb, "linear1", grid, lds, st, args, rmax, ntn)
+                        : launch_gemv_any<false>(qc, nb, "linear2", grid, lds, st, args, rmax, ntn);
         };
-        launch(true, p.ntn1, a1, l1);
+        hipError_t e = launch(true, p.ntn1, a1, l1);
+        if (e != hipSuccess) return e;
         MOE_LAUNCH("swiglu_quant", fp8_decode_swiglu_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st,
                    (const float *)upart, rows, s.F, p.ks, h, hs);
-        launch(false, p.ntn2, a2, l2);
-        return hipGetLastError();
+        return launch(false, p.ntn2, a2, l2);
     }
     MOE_LAUNCH("linear1", fp8_decode_kernel<true>, grid_for(p.ntn1), dim3(64), 0, st, a1);
     MOE_LAUNCH("swiglu_quant", fp8_decode_swiglu_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st,
