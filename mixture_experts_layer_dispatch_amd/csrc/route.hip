@@ -63,6 +63,32 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float *__restri
     route_sum_select<false>(part, nks, T, E, k, gating, bias, blockIdx.x, lg, idx, gate, logits, keys, err);
 }
 
+// one wave per token (few K slices): tokens 4 b .. 4 b + 3
+__global__ __launch_bounds__(256) void route_select_wave_kernel(const float *__restrict__ part, int nks, int T, int E,
+                                                               int k, int gating, const float *__restrict__ bias,
+                                                               int32_t *idx, float *gate, float *logits, float *keys,
+                                                               int32_t *err) {
+    extern __shared__ float lgw[];  // [4][E]
+    const int wave = threadIdx.x >> 6;
+    const long t = (long)blockIdx.x * 4 + wave;
+    if (t < T)
+        route_sum_select_wave<false>(part, nks, T, E, k, gating, bias, t, lgw + wave * E, idx, gate, logits, keys, err);
+}
+
+// Selection after the split-K router: a wave per token when the slices are few (at most 4,
+// E at most 256: all of a lane's loads in flight at once), else a workgroup per token.
+static hipError_t launch_route_select(const Shape &s, int nks, const float *part, const float *bias, int32_t *idx,
+                                      float *gate, float *logits, float *keys, int32_t *err, hipStream_t st) {
+    if (nks <= 4 && s.E <= 256)
+        MOE_LAUNCH("route_select", route_select_wave_kernel, dim3((unsigned)((s.T + 3) / 4)), dim3(256),
+                   (size_t)4 * s.E * sizeof(float), st, part, nks, s.T, s.E, s.k, s.gating, bias, idx, gate, logits,
+                   keys, err);
+    else
+        MOE_LAUNCH("route_select", route_select_kernel, dim3(s.T), dim3(256), (size_t)s.E * sizeof(float), st, part,
+                   nks, s.T, s.E, s.k, s.gating, bias, idx, gate, logits, keys, err);
+    return hipGetLastError();
+}
+
 // Router work layout: bf16 activations with E a multiple of 256 and many tokens use the
 // tiled GEMM above; otherwise, with E a multiple of 32, the split-K kernel at every T -- one wave per (32 tokens, 32 experts, K slice), with as many K slices (whole
 // multiples of 64) as keep the waves near 2048, so that even a few tokens spread W_r over
@@ -114,18 +140,14 @@ hipError_t launch_route(const Shape &s, const void *x, const void *wr, const flo
         const long tiles = (long)((s.T + 255) / 256) * (s.E / 256) * tks;
         MOE_LAUNCH("route", route_tile_kernel, dim3((unsigned)((tiles + 7) / 8 * 8)), dim3(512), bf16_tile8_lds(), st,
                    (const uint16_t *)x, (const uint16_t *)wr, s.T, s.d, s.E, tks, part);
-        MOE_LAUNCH("route_select", route_select_kernel, dim3(s.T), dim3(256), (size_t)s.E * sizeof(float), st,
-                   (const float *)part, tks, s.T, s.E, s.k, s.gating, bias, idx, gate, logits, keys, err);
-        return hipGetLastError();
+        return launch_route_select(s, tks, part, bias, idx, gate, logits, keys, err, st);
     }
     const int nks = part ? route_splitk_slices(s) : 0;
     if (nks > 0) {
         dim3 grid((unsigned)(route_splitk_waves(s, nks)));
         MOE_LAUNCH("route", route_splitk_kernel, grid, dim3(64), 0, st, (const uint16_t *)x, (const uint16_t *)wr,
                    s.T, s.d, s.E, nks, part);
-        MOE_LAUNCH("route_select", route_select_kernel, dim3(s.T), dim3(256), (size_t)s.E * sizeof(float),
-                   st, (const float *)part, nks, s.T, s.E, s.k, s.gating, bias, idx, gate, logits, keys, err);
-        return hipGetLastError();
+        return launch_route_select(s, nks, part, bias, idx, gate, logits, keys, err, st);
     }
     if (s.mode != MODE_F32 && s.E % 32 == 0) {
         dim3 grid((s.T + kRouteTok - 1) / kRouteTok);

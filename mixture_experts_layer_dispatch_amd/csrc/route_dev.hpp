@@ -29,14 +29,31 @@ __device__ __forceinline__ uint64_t pack_key(float key, int e) {
     return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)e;
 }
 
+// v moved across lanes by one DPP control (lanes the control leaves out, or whose source
+// is out of range, keep their own value)
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+    const uint32_t l2 = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWMASK, 0xF, false);
+    const uint32_t h2 = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWMASK, 0xF, false);
+    return ((uint64_t)h2 << 32) | l2;
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Wave-wide maximum, in every lane: within quads (quad_perm swaps), half rows
+// (row_half_mirror) and rows (row_mirror), then row 0 -> 1 and 2 -> 3 (row_bcast:15 into
+// rows 1 and 3), rows 0-1 -> 2-3 (row_bcast:31 into rows 2 and 3); lane 63 then holds the
+// maximum, read out as a uniform value.  The maximum is exact, so the order is free.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)v, m, kWave), hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
+    v = max_u64(v, dpp_u64<0xB1>(v));        // quad_perm [1, 0, 3, 2]
+    v = max_u64(v, dpp_u64<0x4E>(v));        // quad_perm [2, 3, 0, 1]
+    v = max_u64(v, dpp_u64<0x141>(v));       // row_half_mirror
+    v = max_u64(v, dpp_u64<0x140>(v));       // row_mirror
+    v = max_u64(v, dpp_u64<0x142, 0xA>(v));  // row_bcast:15
+    v = max_u64(v, dpp_u64<0x143, 0xC>(v));  // row_bcast:31
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // One wave selects the top-k of token t whose E logits sit in LDS (lg[0..E)); expert e
@@ -310,6 +327,40 @@ __device__ __forceinline__ float sum_slices(const float *__restrict__ part, int 
             if (q0 + q < nks) s += v[q];
     }
     return s;
+}
+
+// One wave, token t: lane l adds the K slices of experts l, l + 64, ... into lg (this
+// wave's E floats of LDS), then selects; used when the slices are few, so that all four
+// waves of a workgroup select (four tokens at a time).  Same sums, same order, same bits
+// as route_sum_select.
+template <bool COH>
+__device__ __forceinline__ void route_sum_select_wave(const float *__restrict__ part, int nks, int T, int E, int k,
+                                                      int gating, const float *__restrict__ bias, long t, float *lg,
+                                                      int32_t *idx, float *gate, float *logits, float *keys,
+                                                      int32_t *err) {
+    const int lane = lane_id();
+    if (nks <= 4 && E <= 4 * kWave) {
+        // every load of the lane (4 experts x 4 slices, clamped) in flight together
+        float v[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane + kWave * i < E ? lane + kWave * i : E - 1;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[i][q] = ldc<COH>(part + ((long)(q < nks ? q : nks - 1) * T + t) * E + e);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float sum = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (q < nks) sum += v[i][q];
+            if (lane + kWave * i < E) lg[lane + kWave * i] = sum;
+        }
+    } else {
+        for (int e = lane; e < E; e += kWave) lg[e] = sum_slices<COH, 16>(part, nks, T, E, t, e);
+    }
+    __builtin_amdgcn_wave_barrier();  // the wave reads back its own LDS stores
+    select_token<COH>(lg, E, k, gating, bias, t, idx, gate, logits, keys, err);
 }
 
 // 256 threads, token t: thread e adds expert e's K slices (all of them in one round trip
