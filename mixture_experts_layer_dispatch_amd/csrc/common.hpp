@@ -242,6 +242,42 @@ struct TileInfo {
     int g, row0, nrows, nt, mt;  // group, first row, valid rows, N tile, row tile within the group
 };
 
+constexpr int kTileGroup = 8;  // row tiles per run of the grouped tile order
+
+// Grouped order of a group's (row tile, N tile) pairs: runs of GM row tiles take every N
+// tile in turn (row tile fastest within a run), so the tiles an XCD runs together share a
+// few activation row tiles and a few weight column tiles, and each activation tile is
+// fetched about ntn / (tiles in flight / GM) times instead of ntn times.  A bijection on
+// [0, mtiles * ntn).
+template <int GM>
+__host__ __device__ __forceinline__ void grouped_tile(int local, int mtiles, int ntn, int &mt, int &nt) {
+    const int per = GM * ntn, grp = local / per, first = grp * GM;
+    const int gsz = mtiles - first < GM ? mtiles - first : GM;
+    const int in = local - grp * per;
+    mt = first + in % gsz;
+    nt = in / gsz;
+}
+
+// As decode_tile, with the grouped order within each group (ts[g + 1] - ts[g] = mtiles x
+// N tiles).
+template <int GM>
+__device__ __forceinline__ TileInfo decode_tile_grouped(int tile, const int32_t *__restrict__ ts,
+                                                        const int32_t *__restrict__ offsets, int G, int BM) {
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (ts[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    TileInfo ti;
+    ti.g = lo;
+    const int rb = offsets[lo], cnt = offsets[lo + 1] - rb;
+    const int mtiles = (cnt + BM - 1) / BM;
+    grouped_tile<GM>(tile - ts[lo], mtiles, (ts[lo + 1] - ts[lo]) / mtiles, ti.mt, ti.nt);
+    ti.row0 = rb + ti.mt * BM;
+    ti.nrows = min(BM, cnt - ti.mt * BM);
+    return ti;
+}
+
 __device__ __forceinline__ TileInfo decode_tile(int tile, const int32_t *__restrict__ ts, const int32_t *__restrict__ offsets,
                                                 int G, int BM) {
     int lo = 0, hi = G - 1;

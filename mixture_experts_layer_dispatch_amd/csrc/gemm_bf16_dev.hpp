@@ -435,7 +435,7 @@ __device__ __forceinline__ void bf16_tile8_rows(const GemmArgs &a, const TileInf
 // every output element takes the same k order either way, so the bits do not change
 template <bool SWIGLU, bool GATHER>
 __device__ __forceinline__ void bf16_tile8(const GemmArgs &a, int tile, uint8_t *lds, int half = -1) {
-    TileInfo ti = decode_tile(tile, a.tile_start, a.offsets, a.G, 256);
+    TileInfo ti = decode_tile_grouped<kTileGroup>(tile, a.tile_start, a.offsets, a.G, 256);
     if (half >= 0) {
         ti.row0 += 128 * half;
         ti.nrows = half ? ti.nrows - 128 : min(ti.nrows, 128);

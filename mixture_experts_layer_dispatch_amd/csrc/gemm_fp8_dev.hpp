@@ -366,8 +366,8 @@ __device__ __forceinline__ void fp8_tile8(const Fp8Args &a, int tile, uint8_t *l
         g = lo;
         const int rb = a.offsets[g], cnt = a.offsets[g + 1] - rb;
         const int mtiles = (cnt + BM - 1) / BM, local = tile - a.tile_start[g];
-        const int mt = local % mtiles;
-        nt = local / mtiles;
+        int mt;
+        grouped_tile<kTileGroup>(local, mtiles, (a.tile_start[g + 1] - a.tile_start[g]) / mtiles, mt, nt);
         row0 = rb + mt * BM;
         nrows = min(BM, cnt - mt * BM);
     }

@@ -1,6 +1,7 @@
-// Host check of the tail split of the 256-row GEMM launches: for every tile count and
-// every CU count per XCD, the blocks of the launch cover each tile exactly once, either
-// whole or as its two 128-row halves, and a split only ever happens in an XCD's last round.
+// Host checks of the GEMM tile scheduling: the tail split of the 256-row launches (for every
+// tile count and every CU count per XCD, the blocks of the launch cover each tile exactly
+// once, either whole or as its two 128-row halves, and a split only ever happens in an
+// XCD's last round), and the grouped tile order (a bijection on a group's tiles).
 #include "common.hpp"
 
 #include <cstdio>
@@ -39,6 +40,25 @@ int main() {
                 }
         }
     }
+    // the grouped tile order is a bijection on [0, mtiles * ntn)
+    for (int mtiles = 1; mtiles <= 40; ++mtiles)
+        for (int ntn = 1; ntn <= 20; ++ntn) {
+            std::vector<int> seen((size_t)mtiles * ntn, 0);
+            for (int l = 0; l < mtiles * ntn; ++l) {
+                int mt, nt;
+                moe::grouped_tile<moe::kTileGroup>(l, mtiles, ntn, mt, nt);
+                if (mt < 0 || mt >= mtiles || nt < 0 || nt >= ntn) {
+                    std::printf("grouped order: mtiles %d ntn %d index %d -> (%d, %d)\n", mtiles, ntn, l, mt, nt);
+                    return 1;
+                }
+                seen[(size_t)mt * ntn + nt] += 1;
+            }
+            for (int v : seen)
+                if (v != 1) {
+                    std::printf("grouped order: mtiles %d ntn %d not a bijection\n", mtiles, ntn);
+                    return 1;
+                }
+        }
     std::printf("ok\n");
     return 0;
 }

@@ -11,7 +11,7 @@ HIPCC = shutil.which("hipcc") or ("/opt/rocm/bin/hipcc" if os.path.exists("/opt/
 
 
 @pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
-def test_tail_split_covers_every_tile_once(tmp_path):
+def test_tile_schedules_cover_every_tile_once(tmp_path):
     exe = tmp_path / "tile_split"
     src = os.path.join(ROOT, "tests", "host", "tile_split.cpp")
     subprocess.run([HIPCC, "--cuda-host-only", "-O1", "-I", CSRC, "-o", str(exe), src], check=True)
