@@ -28,16 +28,19 @@ static hipError_t launch_fp8(const char *name, dim3 grid, const Fp8Args &a, hipS
     return hipGetLastError();
 }
 
+// xcd_cus: CUs per XCD (one workgroup per CU), for the tail split
 template <bool SWIGLU>
-__global__ __launch_bounds__(512) void gemm_fp8_kernel8(Fp8Args a) {
+__global__ __launch_bounds__(512) void gemm_fp8_kernel8(Fp8Args a, int xcd_cus) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int tile = pick_tile(blockIdx.x, a.tile_start[a.G]);
-    if (tile >= 0) fp8_tile8<SWIGLU ? 1 : 2, SWIGLU ? 8 : 4, SWIGLU, SWIGLU>(a, tile, lds);
+    int half;
+    const int tile = pick_tile_split(blockIdx.x, a.tile_start[a.G], xcd_cus, half);
+    if (tile >= 0) fp8_tile8<SWIGLU ? 1 : 2, SWIGLU ? 8 : 4, SWIGLU, SWIGLU>(a, tile, lds, half);
 }
 
-// 256 x 256 tiles: the 8-wave kernel (linear1 gathers its rows, linear2 does not)
+// 256 x 256 tiles: the 8-wave kernel (linear1 gathers its rows, linear2 does not).  ub: an
+// upper bound of the tile count; the grid adds the blocks of the tail split.
 template <bool SWIGLU>
-static hipError_t launch_fp8_8(const char *name, dim3 grid, const Fp8Args &a, hipStream_t st) {
+static hipError_t launch_fp8_8(const char *name, long ub, const Fp8Args &a, hipStream_t st) {
     constexpr size_t lds = fp8_tile8_lds();
     static bool attr = false;
     if (!attr) {
@@ -46,7 +49,10 @@ static hipError_t launch_fp8_8(const char *name, dim3 grid, const Fp8Args &a, hi
         if (e != hipSuccess) return e;
         attr = true;
     }
-    MOE_LAUNCH(name, gemm_fp8_kernel8<SWIGLU>, grid, dim3(512), lds, st, a);
+    const int C = xcd_cus();
+    if (C <= 0) return hipErrorInvalidDevice;
+    const dim3 grid((unsigned)(8 * ((ub + 7) / 8 + C / 2)));
+    MOE_LAUNCH(name, gemm_fp8_kernel8<SWIGLU>, grid, dim3(512), lds, st, a, C);
     return hipGetLastError();
 }
 
@@ -202,11 +208,12 @@ hipError_t launch_fp8_ffn(const Shape &s, const FfnPlan &p, const uint8_t *w1, c
     hipError_t e;
     // the 8-wave tiles address their A operand with 32-bit byte offsets
     const bool a1_small = (long)s.T * s.d < (1L << 32), a2_small = rows * (long)s.F < (1L << 32);
-    if (p.bm1 == 256 && a1_small) e = launch_fp8_8<true>("linear1", grid_for(p.bm1, ntn1), a1, st);
+    auto ub_for = [&](int bm, int ntn) { return ((rows + bm - 1) / bm + (G < rows ? G : rows)) * (long)ntn; };
+    if (p.bm1 == 256 && a1_small) e = launch_fp8_8<true>("linear1", ub_for(p.bm1, ntn1), a1, st);
     else if (p.bm1 == 256) e = launch_fp8<256, 256, 4, true, true>("linear1", grid_for(p.bm1, ntn1), a1, st);
     else e = launch_fp8<128, 256, 4, true, true>("linear1", grid_for(p.bm1, ntn1), a1, st);
     if (e != hipSuccess) return e;
-    if (p.bm2 == 256 && p.bn2 == 256 && a2_small) e = launch_fp8_8<false>("linear2", grid_for(p.bm2, ntn2), a2, st);
+    if (p.bm2 == 256 && p.bn2 == 256 && a2_small) e = launch_fp8_8<false>("linear2", ub_for(p.bm2, ntn2), a2, st);
     else if (p.bm2 == 256 && p.bn2 == 256) e = launch_fp8<256, 256, 2, false, false>("linear2", grid_for(p.bm2, ntn2), a2, st);
     else if (p.bn2 == 256) e = launch_fp8<128, 256, 2, false, false>("linear2", grid_for(p.bm2, ntn2), a2, st);
     else if (p.bm2 == 256) e = launch_fp8<256, 128, 2, false, false>("linear2", grid_for(p.bm2, ntn2), a2, st);

@@ -344,9 +344,11 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args &a, int tile, uint8_t *ld
 constexpr size_t fp8_tile8_lds() { return 3 * (size_t)(256 * 128 + 256 * 64 + 256 * 4 + 256 * 4); }
 
 // TM x TN blocks of 32x32 per wave; linear1 (SWIGLU): TM = 1, TN = 8 (32 rows, 128 gate + 128 up
-// columns); linear2: TM = 2, TN = 4 (64 rows x 128 columns).
+// columns); linear2: TM = 2, TN = 4 (64 rows x 128 columns).  half: -1 the whole tile, 0 / 1
+// its rows 0..127 / 128..255 (an empty half returns at once); the first 128 rows are one
+// wave per SIMD's, and every output element takes the same k order either way.
 template <int TM, int TN, bool SWIGLU, bool GATHER>
-__device__ __forceinline__ void fp8_tile8(const Fp8Args &a, int tile, uint8_t *lds) {
+__device__ __forceinline__ void fp8_tile8(const Fp8Args &a, int tile, uint8_t *lds, int half = -1) {
     constexpr int BM = 256, BN = 256, NS = 3;
     constexpr int WMW = BM / (32 * TM), WNW = 8 / WMW;
     static_assert(WNW * TN * 32 == BN, "wave grid");
@@ -370,7 +372,12 @@ __device__ __forceinline__ void fp8_tile8(const Fp8Args &a, int tile, uint8_t *l
         grouped_tile<kTileGroup>(local, mtiles, (a.tile_start[g + 1] - a.tile_start[g]) / mtiles, mt, nt);
         row0 = rb + mt * BM;
         nrows = min(BM, cnt - mt * BM);
+        if (half >= 0) {
+            row0 += 128 * half;
+            nrows = half ? nrows - 128 : min(nrows, 128);
+        }
     }
+    if (nrows <= 0) return;
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     // linear2: waves 0-3 (one per SIMD) cover rows 0-127, so a short tile keeps every SIMD busy
     const int wm = TM == 1 ? wave : (wave & 1) + 2 * (wave >> 2), wn = TM == 1 ? 0 : (wave >> 1) & 1;

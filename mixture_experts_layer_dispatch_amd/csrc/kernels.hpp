@@ -42,6 +42,7 @@ hipError_t launch_dispatch(const Shape &s, const int32_t *idx, int32_t *blockcou
                            int32_t *offsets, int32_t *slot_to_row, int32_t *row_to_slot, int32_t *err,
                            const uint16_t *x, uint8_t *xq, float *xs, hipStream_t st);
 int dispatch_blocks(int T);
+int xcd_cus();  // CUs per XCD of the current device
 
 // expert FFN
 struct FfnPlan {
