@@ -9,7 +9,8 @@
 // (expert, block), then a scatter whose in-block rank comes from 64-bit lane masks
 // (population counts), never from the order of atomics.
 //
-// Workgroup-level items assume 256 threads.
+// Workgroup-level items do the work of 256 threads; in a larger workgroup the threads past
+// 256 only take part in the barriers.
 #pragma once
 
 #include "common.hpp"
@@ -54,7 +55,7 @@ __device__ __forceinline__ void build_masks(const int32_t *__restrict__ idx, int
     for (int i = tid; i < 4 * E; i += blockDim.x) masks[i] = 0ull;
     __syncthreads();
     const long t = (long)blk * kDispTok + tid;
-    if (t < T) {
+    if (tid < kDispTok && t < T) {
         int ids[kMaxChoices];
         bool bad, dup;
         const uint32_t ok = load_choices<COH>(idx, t, k, E, ids, bad, dup);
@@ -83,26 +84,31 @@ __device__ __forceinline__ void count_block(const int32_t *__restrict__ idx, int
 // total.  tmp: 256 ints of LDS.
 __device__ __forceinline__ int block_exclusive_scan(int32_t *v, int n, int32_t *tmp) {
     const int tid = threadIdx.x;
+    const bool act = tid < 256;  // threads past 256 only meet the barriers
     const int C = (n + 255) / 256, b0 = tid * C;
     int loc = 0;
-    for (int i = 0; i < C; ++i)
-        if (b0 + i < n) loc += v[b0 + i];
-    tmp[tid] = loc;
+    if (act) {
+        for (int i = 0; i < C; ++i)
+            if (b0 + i < n) loc += v[b0 + i];
+        tmp[tid] = loc;
+    }
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {
-        int a = tid >= off ? tmp[tid - off] : 0;
+        int a = act && tid >= off ? tmp[tid - off] : 0;
         __syncthreads();
-        tmp[tid] += a;
+        if (act) tmp[tid] += a;
         __syncthreads();
     }
-    int run = tmp[tid] - loc;
     const int total = tmp[255];
-    for (int i = 0; i < C; ++i)
-        if (b0 + i < n) {
-            int c = v[b0 + i];
-            v[b0 + i] = run;
-            run += c;
-        }
+    if (act) {
+        int run = tmp[tid] - loc;
+        for (int i = 0; i < C; ++i)
+            if (b0 + i < n) {
+                int c = v[b0 + i];
+                v[b0 + i] = run;
+                run += c;
+            }
+    }
     __syncthreads();
     return total;
 }
@@ -190,7 +196,7 @@ __device__ __forceinline__ void scatter_block(const int32_t *__restrict__ idx, i
     build_masks<COH>(idx, T, k, E, blk, masks, nullptr);  // errors were reported by the count pass
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
     const long t = (long)blk * kDispTok + tid;
-    if (t >= T) return;
+    if (tid >= kDispTok || t >= T) return;
     const unsigned long long below = (1ull << lane) - 1ull;
     int ids[kMaxChoices];
     bool bad, dup;
@@ -221,7 +227,7 @@ __device__ __forceinline__ void dispatch_single_block(const int32_t *__restrict_
     unsigned long long *masks = (unsigned long long *)lds;
     int32_t *base = (int32_t *)(masks + 4 * E), *tmp = base + E;
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
-    const bool live = tid < T;
+    const bool live = tid < T && tid < kDispTok;
     int ids[kMaxChoices];
     uint32_t ok = 0;
     if (live) {

@@ -7,7 +7,8 @@
 namespace moe {
 
 hipError_t launch_fused_bf16(FusedArgs &a, int bm, int bn2, size_t lds, int cu_limit, hipStream_t st);
-hipError_t launch_fused_fp8(FusedArgs &a, bool decode, int bm, int bn2, size_t lds, int cu_limit, hipStream_t st);
+hipError_t launch_fused_fp8(FusedArgs &a, bool decode, int bm, int bn2, bool w8, size_t lds, int cu_limit,
+                            hipStream_t st);
 
 namespace {
 
@@ -19,15 +20,26 @@ int router_kind(const Shape &s, int nks) {
 
 size_t router_lds(const Shape &s, int kind) {
     switch (kind) {
-        case ROUTER_SPLITK: return (size_t)s.E * 4;
+        case ROUTER_SPLITK: return (size_t)4 * s.E * 4;
         case ROUTER_MFMA: return (size_t)kRouteTok * s.E * 4;
         default: return (size_t)4 * s.E * 4;
     }
 }
 
+// FP8 8-wave tiles: their A operands (x codes, h codes) addressed with 32-bit byte offsets
+bool fp8_w8(const Shape &s) { return (long)s.T * s.d < (1L << 32) && s.rows() * (long)s.F < (1L << 32); }
+
+// the 512-thread kernel with the 8-wave tiles runs
+bool fused_w8(const Shape &s, const FfnPlan &p) {
+    if (s.mode == MODE_F32 || p.decode || p.bm1 != 256 || p.bn2 != 256) return false;
+    return s.mode == MODE_BF16 || fp8_w8(s);
+}
+
 size_t gemm_lds(const Shape &s, const FfnPlan &p) {
     if (s.mode == MODE_F32 || p.decode) return 0;
     const bool b256 = p.bm1 == 256, n256 = p.bn2 == 256;
+    if (b256 && n256 && s.mode == MODE_BF16) return bf16_tile8_lds();
+    if (b256 && n256 && fp8_w8(s)) return fp8_tile8_lds();
     if (s.mode == MODE_BF16) {
         const size_t l1 = b256 ? bf16_tile_lds<256, 256>() : bf16_tile_lds<128, 256>();
         const size_t l2 = b256 ? (n256 ? bf16_tile_lds<256, 256>() : bf16_tile_lds<256, 128>())
@@ -47,11 +59,18 @@ int fused_row_tiles(const Shape &s, const FfnPlan &p) {
     return (int)((rows + p.bm1 - 1) / p.bm1 + (G < rows ? G : rows));
 }
 
+// router kind of the persistent kernel: the 512-thread kernel runs the stand-alone path's
+// tiled router (same slices, same sums) where that one does
+int fused_router_kind(const Shape &s, const FfnPlan &p) {
+    if (fused_w8(s, p) && route_tile_slices(s) > 0) return ROUTER_TILE;
+    return router_kind(s, route_splitk_slices(s));
+}
+
 size_t fused_lds_bytes(const Shape &s, const FfnPlan &p) {
-    const int kind = router_kind(s, route_splitk_slices(s));
+    const int kind = fused_router_kind(s, p);
     size_t b = gemm_lds(s, p);
-    const size_t r = router_lds(s, kind), m = (size_t)4 * s.E * 8 + (size_t)(s.E + 256) * 4,
-                 plan = (2 * 1032 + 256) * 4;
+    const size_t r = kind == ROUTER_TILE ? bf16_tile8_lds() : router_lds(s, kind);
+    const size_t m = (size_t)4 * s.E * 8 + (size_t)(s.E + 256) * 4, plan = (2 * 1032 + 256) * 4;
     const size_t cached = p.decode ? (size_t)3 * (s.G() + 1) * 4 : 0;  // the plan, kept in LDS
     for (size_t v : {r, m, plan, cached}) b = v > b ? v : b;
     return b;
@@ -60,7 +79,7 @@ size_t fused_lds_bytes(const Shape &s, const FfnPlan &p) {
 hipError_t launch_layer_fused(const Shape &s, const FfnPlan &p, FusedArgs &a, int cu_limit, hipStream_t st) {
     a.T = s.T; a.d = s.d; a.E = s.E; a.k = s.k; a.F = s.F; a.S = s.S; a.G = s.G(); a.gating = s.gating;
     a.nks = route_splitk_slices(s);
-    a.router = router_kind(s, a.nks);
+    a.router = fused_router_kind(s, p);
     a.nblk = dispatch_blocks(s.T);
     a.bm = p.bm1;
     a.ntn1 = p.ntn1;
@@ -73,10 +92,12 @@ hipError_t launch_layer_fused(const Shape &s, const FfnPlan &p, FusedArgs &a, in
     long nr;
     switch (a.router) {
         case ROUTER_SPLITK: nr = (route_splitk_waves(s, a.nks) + 3) / 4; break;
+        case ROUTER_TILE: nr = (long)((s.T + 255) / 256) * (s.E / 256) * a.nks; break;
         case ROUTER_MFMA: nr = (s.T + kRouteTok - 1) / kRouteTok; break;
         default: nr = (s.T + 3) / 4; break;
     }
-    const long nsel = a.router == ROUTER_SPLITK ? s.T : 0;
+    a.sel4 = router_in_slices(a.router) && route_select_by_wave(s.E, a.nks);
+    const long nsel = !router_in_slices(a.router) ? 0 : a.sel4 ? (s.T + 3) / 4 : s.T;
     a.b_r = nq;
     a.b_sel = a.b_r + nr;
     a.b_cnt = a.b_sel + nsel;
@@ -92,7 +113,7 @@ hipError_t launch_layer_fused(const Shape &s, const FfnPlan &p, FusedArgs &a, in
     const size_t lds = fused_lds_bytes(s, p);
     if (s.mode == MODE_F32) return launch_fused_kernel<MODE_F32, 128, 128>(a, lds, cu_limit, st);
     if (s.mode == MODE_BF16) return launch_fused_bf16(a, p.bm1, p.bn2, lds, cu_limit, st);
-    return launch_fused_fp8(a, p.decode, p.bm1, p.bn2, lds, cu_limit, st);
+    return launch_fused_fp8(a, p.decode, p.bm1, p.bn2, fp8_w8(s), lds, cu_limit, st);
 }
 
 }  // namespace moe

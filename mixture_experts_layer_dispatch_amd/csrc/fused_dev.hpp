@@ -170,23 +170,39 @@ __device__ __forceinline__ void wg_counter_wait_acquire(int32_t *sync, int c, in
 
 __device__ __forceinline__ long round8(long n) { return (n + 7) / 8 * 8; }
 
-// ---- items of the steps before the GEMMs (workgroup items, 256 threads) ----------------
+// ---- items of the steps before the GEMMs (workgroup items) -------------------------------
+//
+// Each item does the work of 256 threads; in the 512-thread kernel the upper 256 only take
+// part in the barriers.
 
-template <int MODE>
+static __device__ __noinline__ void route_tile8_call(const uint16_t *x, const uint16_t *wr, int T, int d, int E, int nks,
+                                             int b, float *part);
+
+// W8: the 512-thread kernel's items (the tiled router runs only there)
+template <int MODE, bool W8 = false>
 __device__ __forceinline__ void front_item(const FusedArgs &a, long i, uint8_t *lds, bool &routed) {
     const int nr = (int)(a.b_sel - a.b_r);
     if (i < a.b_r) {  // FP8 activations: 64 blocks of 128 per item
         const long nblocks = (long)a.T * a.d / 128;
+        if (threadIdx.x < 256) {
 #pragma unroll
-        for (int pass = 0; pass < 4; ++pass)
-            quant_x_lane<true>((const uint16_t *)a.x, nblocks, a.xq, a.xs, (i * 4 + pass) * 256 + threadIdx.x);
+            for (int pass = 0; pass < 4; ++pass)
+                quant_x_lane<true>((const uint16_t *)a.x, nblocks, a.xq, a.xs, (i * 4 + pass) * 256 + threadIdx.x);
+        }
         wg_count(a.sync, CNT_QUANT, i);
     } else if (i < a.b_sel) {  // router
         const int b = (int)(i - a.b_r);
         float *lg = (float *)lds;
-        if (a.router == ROUTER_SPLITK) {
+        if (W8 && a.router == ROUTER_TILE) {
+            // one 256 x 256 tile of one K slice; its partial logits go out with plain stores,
+            // written back by the release fence before the count (selection reads them with
+            // device-coherent loads)
+            if constexpr (W8 && MODE != MODE_F32)
+                route_tile8_call((const uint16_t *)a.x, (const uint16_t *)a.wr, a.T, a.d, a.E, a.nks, b, a.rpart);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        } else if (a.router == ROUTER_SPLITK) {
             const long w = (long)b * 4 + (threadIdx.x >> 6);
-            if (w < (long)(a.E / 32) * a.nks * ((a.T + 31) / 32))
+            if (threadIdx.x < 256 && w < (long)(a.E / 32) * a.nks * ((a.T + 31) / 32))
                 route_splitk_wave<true>((const uint16_t *)a.x, (const uint16_t *)a.wr, a.T, a.d, a.E, a.nks, w,
                                         a.rpart);
         } else if (a.router == ROUTER_MFMA) {
@@ -198,16 +214,24 @@ __device__ __forceinline__ void front_item(const FusedArgs &a, long i, uint8_t *
                                                         a.idx, a.gate, nullptr, nullptr, a.err);
         }
         wg_count(a.sync, CNT_ROUTE, b);
-    } else if (i < a.b_cnt) {  // split-K router: one token's selection
+    } else if (i < a.b_cnt) {  // sliced router: selection, four tokens (a wave each) or one
         if (!routed) {
             wg_counter_wait(a.sync, CNT_ROUTE, nr, a.err);
             routed = true;
         }
-        route_sum_select<true>(a.rpart, a.nks, a.T, a.E, a.k, a.gating, a.bias, i - a.b_sel, (float *)lds, a.idx,
-                               a.gate, nullptr, nullptr, a.err);
+        if (a.sel4) {
+            const int wave = threadIdx.x >> 6;
+            const long t = (i - a.b_sel) * 4 + wave;
+            if (wave < 4 && t < a.T)
+                route_sum_select_wave<true>(a.rpart, a.nks, a.T, a.E, a.k, a.gating, a.bias, t,
+                                            (float *)lds + wave * a.E, a.idx, a.gate, nullptr, nullptr, a.err);
+        } else {
+            route_sum_select<true>(a.rpart, a.nks, a.T, a.E, a.k, a.gating, a.bias, i - a.b_sel, (float *)lds, a.idx,
+                                   a.gate, nullptr, nullptr, a.err);
+        }
         wg_count(a.sync, CNT_SELECT, i - a.b_sel);
     } else if (i < a.b_plan) {  // dispatch histogram of one block
-        if (a.router == ROUTER_SPLITK) wg_counter_wait(a.sync, CNT_SELECT, a.T, a.err);
+        if (router_in_slices(a.router)) wg_counter_wait(a.sync, CNT_SELECT, (int)(a.b_cnt - a.b_sel), a.err);
         else wg_counter_wait(a.sync, CNT_ROUTE, nr, a.err);
         count_block<true>(a.idx, a.T, a.k, a.E, (int)(i - a.b_cnt), (unsigned long long *)lds, a.blockcounts,
                           a.err);
@@ -216,7 +240,7 @@ __device__ __forceinline__ void front_item(const FusedArgs &a, long i, uint8_t *
         int32_t *sh = (int32_t *)lds;
         if (a.nblk == 1) {
             // one dispatch block: histogram, scan and scatter through LDS, then the plan
-            if (a.router == ROUTER_SPLITK) wg_counter_wait(a.sync, CNT_SELECT, a.T, a.err);
+            if (router_in_slices(a.router)) wg_counter_wait(a.sync, CNT_SELECT, (int)(a.b_cnt - a.b_sel), a.err);
             else wg_counter_wait(a.sync, CNT_ROUTE, nr, a.err);
             dispatch_single_block<true>(a.idx, a.T, a.k, a.E, a.S, a.counts, a.offsets, a.s2r, a.r2s, a.err, lds);
             wait_vmcnt<0>();
@@ -276,22 +300,165 @@ __device__ __forceinline__ void fused_exit(const FusedArgs &a, uint8_t *lds) {
     }
 }
 
-// ---- tiled variants (bf16, FP8 x FP4, fp32): every item is a workgroup item ------------
+// ---- 8-wave GEMM tiles, called out of line -----------------------------------------------
+//
+// The persistent kernel is one large function: inlined into it, the 8-wave tiles (about 200
+// VGPRs each at two waves per SIMD) would share its register allocation and spill.  Called
+// out of line they keep their own, and the call saves the caller's live registers once per
+// tile.  Arguments arrive in vector registers, so they are read back as uniform values, and
+// the tiles take the kernel's dynamic LDS directly.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <typename P>
+__device__ __forceinline__ P *unip(P *p) {
+    const uint64_t u = (uint64_t)p;
+    return (P *)(((uint64_t)(uint32_t)uni((int)(u >> 32)) << 32) | (uint32_t)uni((int)(uint32_t)u));
+}
+template <typename Args>
+__device__ __forceinline__ void uniform_ints(Args &a) {
+    a.T = uni(a.T); a.k = uni(a.k); a.K = uni(a.K); a.Ntot = uni(a.Ntot);
+    a.ldc = uni(a.ldc); a.G = uni(a.G); a.F = uni(a.F);
+}
 
-template <int MODE, int BM, int BN2>
+template <bool SWIGLU>
+__device__ __noinline__ void bf16_tile8_call(GemmArgs a, int tile) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+    a.A = unip(a.A); a.row_to_slot = unip(a.row_to_slot); a.B = unip(a.B); a.C = unip(a.C);
+    a.offsets = unip(a.offsets); a.tile_start = unip(a.tile_start);
+    uniform_ints(a);
+    bf16_tile8<SWIGLU, SWIGLU>(a, uni(tile), lds_dyn);
+}
+
+template <bool SWIGLU>
+__device__ __noinline__ void fp8_tile8_call(Fp8Args a, int tile) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+    a.A = unip(a.A); a.As = unip(a.As); a.row_to_slot = unip(a.row_to_slot); a.B = unip(a.B);
+    a.Bs = unip(a.Bs); a.C = unip(a.C); a.Cs = unip(a.Cs); a.offsets = unip(a.offsets);
+    a.tile_start = unip(a.tile_start);
+    uniform_ints(a);
+    fp8_tile8<SWIGLU ? 1 : 2, SWIGLU ? 8 : 4, SWIGLU, SWIGLU>(a, uni(tile), lds_dyn);
+}
+
+// Router tile b of the tiled router (the stand-alone path's route_tile_kernel without its
+// XCD-aware order: slice b / per, then the 256-token tile fastest and the 256-expert tile).
+static __device__ __noinline__ void route_tile8_call(const uint16_t *x, const uint16_t *wr, int T, int d, int E, int nks,
+                                             int b, float *part) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+    x = unip(x);
+    wr = unip(wr);
+    part = unip(part);
+    T = uni(T);
+    d = uni(d);
+    E = uni(E);
+    nks = uni(nks);
+    b = uni(b);
+    const int mtn = (T + 255) / 256, per = mtn * (E / 256);
+    const int ks = b / per, rem = b % per;
+    TileInfo ti;
+    ti.g = 0;
+    ti.mt = rem % mtn;
+    ti.nt = rem / mtn;
+    ti.row0 = ti.mt * 256;
+    ti.nrows = min(256, T - ti.row0);
+    GemmArgs g = {x, nullptr, wr, (uint16_t *)(part + (long)ks * T * E), nullptr, nullptr, T, 1, d, E, E, 1, 0};
+    const int kchunk = d / nks;
+    bf16_tile8_rows<false, false, true>(g, ti, d, ks * kchunk, kchunk / 32, lds_dyn);
+}
+
+// The steps before the GEMMs, out of line as well in the 512-thread kernel (inlined, they
+// would spill there); the kernel arguments are read back as uniform values.
+template <int MODE>
+__device__ __noinline__ int front_item_call(FusedArgs a, long i, int routed) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+    static_assert(sizeof(FusedArgs) % 4 == 0, "argument words");
+    FusedArgs u;
+    const int32_t *src = (const int32_t *)&a;
+    int32_t *dst = (int32_t *)&u;
+#pragma unroll
+    for (int w = 0; w < (int)(sizeof(FusedArgs) / 4); ++w) dst[w] = uni(src[w]);
+    const long iu = ((long)uni((int)(i >> 32)) << 32) | (uint32_t)uni((int)i);
+    bool r = uni(routed) != 0;
+    front_item<MODE, true>(u, iu, lds_dyn, r);
+    return r ? 1 : 0;
+}
+
+// ---- tiled variants (bf16, FP8 x FP4, fp32): every item is a workgroup item ------------
+//
+// W8: 512 threads, and the GEMM items run the 8-wave 256 x 256 tiles of the stand-alone
+// kernels (same k order per output element, so the same bits).
+
+template <int MODE, int BM, int BN2, bool W8 = false>
 __device__ __forceinline__ void fused_tiled(const FusedArgs &a, uint8_t *lds) {
+    static_assert(!W8 || (MODE != MODE_F32 && BM == 256 && BN2 == 256), "8-wave tiles are 256 x 256");
     const long P = gridDim.x;
     long i = blockIdx.x;
     bool routed = false;
     for (; i < a.b_end; i += P) {
         __syncthreads();  // the previous item may still read its LDS
-        front_item<MODE>(a, i, lds, routed);
+        if constexpr (W8) routed = front_item_call<MODE>(a, i, routed ? 1 : 0) != 0;
+        else front_item<MODE>(a, i, lds, routed);
     }
     // everything before linear1, then one acquire: the GEMMs read it with cached loads
     wg_flag_wait(a.sync, FLAG_FRONT, a.err);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const long N1 = MODE == MODE_F32 ? a.n1 : a.ts1[a.G], N2 = MODE == MODE_F32 ? a.n2 : a.ts2[a.G];
     const long e1 = a.b_end + round8(N1), e2 = e1 + round8(N2), e3 = e2 + a.ncb;
+    if constexpr (W8) {
+        // GEMM tiles vary in cost (a group's last row tile holds few rows), so they are
+        // taken from queues as workgroups free up instead of dealt round robin: queue
+        // b % 8 hands workgroup b the items q * 8 + b % 8 (its XCD's tiles under the
+        // XCD-aware tile order), linear1 before linear2.  A workgroup leaves linear1 (and
+        // counts itself past it) when it first takes a linear2 item or runs out; linear2
+        // waits for every workgroup past linear1 -- which each reaches, as linear1 items
+        // wait on nothing.  The taken index is broadcast through LDS between tiles.
+        const int nq = P % 8 == 0 ? 8 : 1, qid = (int)(blockIdx.x % nq);
+        int32_t *queue = counter_sub(a.sync, CNT_QUEUE, qid);
+        const long n1 = e1 - a.b_end, n12 = e2 - a.b_end;
+        bool past1 = false, open2 = false;
+        int *slot = (int *)lds;
+        for (;;) {
+            __syncthreads();  // the previous tile is done with the LDS
+            if (threadIdx.x == 0) *slot = atomic_add(queue, 1);
+            __syncthreads();
+            const long j = (long)*slot * nq + qid;
+            __syncthreads();  // every thread has the index before a tile reuses the LDS
+            if (j >= n12) break;
+            if (j < n1) {
+                const int tile = pick_tile((int)j, (int)N1);
+                if (tile < 0) continue;
+                if constexpr (MODE == MODE_BF16) {
+                    GemmArgs g = {(const uint16_t *)a.x, a.r2s, (const uint16_t *)a.w1, (uint16_t *)a.h, a.offsets,
+                                  a.ts1, a.T, a.k, a.d, 2 * a.F, a.F, a.G, a.F};
+                    bf16_tile8_call<true>(g, tile);
+                } else {
+                    Fp8Args g = {a.xq, a.xs, a.r2s, (const uint8_t *)a.w1, (const uint8_t *)a.w1s, a.h, a.hs,
+                                 a.offsets, a.ts1, a.T, a.k, a.d, 2 * a.F, a.F, a.G, a.F};
+                    fp8_tile8_call<true>(g, tile);
+                }
+            } else {
+                if (!past1) {
+                    wg_release_count(a.sync, CNT_LIN1);
+                    past1 = true;
+                }
+                if (!open2) {
+                    wg_counter_wait_acquire(a.sync, CNT_LIN1, (int)P, a.err);
+                    open2 = true;
+                }
+                const int tile = pick_tile((int)(j - n1), (int)N2);
+                if (tile < 0) continue;
+                if constexpr (MODE == MODE_BF16) {
+                    GemmArgs g = {(const uint16_t *)a.h, nullptr, (const uint16_t *)a.w2, (uint16_t *)a.yperm,
+                                  a.offsets, a.ts2, a.T, a.k, a.F, a.d, a.d, a.G, a.F};
+                    bf16_tile8_call<false>(g, tile);
+                } else {
+                    Fp8Args g = {(const uint8_t *)a.h, a.hs, nullptr, (const uint8_t *)a.w2, (const uint8_t *)a.w2s,
+                                 a.yperm, nullptr, a.offsets, a.ts2, a.T, a.k, a.F, a.d, a.d, a.G, a.F};
+                    fp8_tile8_call<false>(g, tile);
+                }
+            }
+        }
+        if (!past1) wg_release_count(a.sync, CNT_LIN1);
+        i = e2 + blockIdx.x;  // the combine items stay dealt round robin
+    }
     for (; i < e1; i += P) {  // linear1
         __syncthreads();
         const long j = i - a.b_end;
@@ -305,15 +472,17 @@ __device__ __forceinline__ void fused_tiled(const FusedArgs &a, uint8_t *lds) {
             if constexpr (MODE == MODE_BF16) {
                 GemmArgs g = {(const uint16_t *)a.x, a.r2s, (const uint16_t *)a.w1, (uint16_t *)a.h, a.offsets, a.ts1,
                               a.T, a.k, a.d, 2 * a.F, a.F, a.G, a.F};
-                bf16_tile<BM, 256, true, true>(g, tile, lds);
+                if constexpr (W8) bf16_tile8_call<true>(g, tile);
+                else bf16_tile<BM, 256, true, true>(g, tile, lds);
             } else {
                 Fp8Args g = {a.xq, a.xs, a.r2s, (const uint8_t *)a.w1, (const uint8_t *)a.w1s, a.h, a.hs, a.offsets,
                              a.ts1, a.T, a.k, a.d, 2 * a.F, a.F, a.G, a.F};
-                fp8_tile<BM, 256, 4, true, true>(g, tile, lds);
+                if constexpr (W8) fp8_tile8_call<true>(g, tile);
+                else fp8_tile<BM, 256, 4, true, true>(g, tile, lds);
             }
         }
     }
-    wg_release_count(a.sync, CNT_LIN1);
+    if constexpr (!W8) wg_release_count(a.sync, CNT_LIN1);  // (W8: counted in the queue loop)
     bool waited = false;
     for (; i < e2; i += P) {  // linear2
         if (!waited) {
@@ -332,11 +501,13 @@ __device__ __forceinline__ void fused_tiled(const FusedArgs &a, uint8_t *lds) {
             if constexpr (MODE == MODE_BF16) {
                 GemmArgs g = {(const uint16_t *)a.h, nullptr, (const uint16_t *)a.w2, (uint16_t *)a.yperm, a.offsets,
                               a.ts2, a.T, a.k, a.F, a.d, a.d, a.G, a.F};
-                bf16_tile<BM, BN2, false, false>(g, tile, lds);
+                if constexpr (W8) bf16_tile8_call<false>(g, tile);
+                else bf16_tile<BM, BN2, false, false>(g, tile, lds);
             } else {
                 Fp8Args g = {(const uint8_t *)a.h, a.hs, nullptr, (const uint8_t *)a.w2, (const uint8_t *)a.w2s,
                              a.yperm, nullptr, a.offsets, a.ts2, a.T, a.k, a.F, a.d, a.d, a.G, a.F};
-                fp8_tile<BM, BN2, 2, false, false>(g, tile, lds);
+                if constexpr (W8) fp8_tile8_call<false>(g, tile);
+                else fp8_tile<BM, BN2, 2, false, false>(g, tile, lds);
             }
         }
     }
@@ -347,8 +518,9 @@ __device__ __forceinline__ void fused_tiled(const FusedArgs &a, uint8_t *lds) {
             wg_counter_wait_acquire(a.sync, CNT_LIN2, (int)P, a.err);
             waited = true;
         }
-        combine_lane<MODE == MODE_F32, false>(a.yperm, a.s2r, a.gate, a.y, a.T, a.k, a.d, a.S,
-                                              (i - e2) * 256 + threadIdx.x);
+        if (threadIdx.x < 256)
+            combine_lane<MODE == MODE_F32, false>(a.yperm, a.s2r, a.gate, a.y, a.T, a.k, a.d, a.S,
+                                                  (i - e2) * 256 + threadIdx.x);
     }
     fused_exit(a, lds);
 }
@@ -446,6 +618,13 @@ __global__ __launch_bounds__(256) void fused_layer_kernel(FusedArgs a) {
     fused_tiled<MODE, BM, BN2>(a, lds);
 }
 
+// 512 threads, 8-wave 256 x 256 GEMM tiles (bf16 or FP8 x FP4)
+template <int MODE>
+__global__ __launch_bounds__(512) void fused_layer_kernel8(FusedArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    fused_tiled<MODE, 256, 256, true>(a, lds);
+}
+
 // The decode variant streams weights: it is held to 128 registers so that four waves
 // share each SIMD.
 template <int UNUSED = 0>
@@ -456,7 +635,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void f
 
 // Host side: a cooperative launch of as many workgroups as fit on the device at once
 // (at most cu_limit CUs' worth when cu_limit > 0).
-inline hipError_t launch_fused_fn(const void *fn, FusedArgs &a, size_t lds, int cu_limit, hipStream_t st) {
+inline hipError_t launch_fused_fn(const void *fn, FusedArgs &a, size_t lds, int cu_limit, hipStream_t st,
+                                  int threads = 256) {
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -464,7 +644,7 @@ inline hipError_t launch_fused_fn(const void *fn, FusedArgs &a, size_t lds, int 
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, lds);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds);
     if (e != hipSuccess) return e;
     if (per_cu < 1) return hipErrorInvalidConfiguration;
     if (cu_limit > 0 && cu_limit < cus) cus = cu_limit;
@@ -472,7 +652,7 @@ inline hipError_t launch_fused_fn(const void *fn, FusedArgs &a, size_t lds, int 
     if (P >= 8) P -= P % 8;  // item i then runs on XCD i % 8
     void *args[] = {&a};
     prof_begin(st);
-    e = hipLaunchCooperativeKernel(fn, dim3(P), dim3(256), args, (unsigned)lds, st);
+    e = hipLaunchCooperativeKernel(fn, dim3(P), dim3(threads), args, (unsigned)lds, st);
     prof_end("layer_fused", st);
     return e;
 }
@@ -480,6 +660,11 @@ inline hipError_t launch_fused_fn(const void *fn, FusedArgs &a, size_t lds, int 
 template <int MODE, int BM, int BN2>
 hipError_t launch_fused_kernel(FusedArgs &a, size_t lds, int cu_limit, hipStream_t st) {
     return launch_fused_fn((const void *)fused_layer_kernel<MODE, BM, BN2>, a, lds, cu_limit, st);
+}
+
+template <int MODE>
+hipError_t launch_fused_kernel8(FusedArgs &a, size_t lds, int cu_limit, hipStream_t st) {
+    return launch_fused_fn((const void *)fused_layer_kernel8<MODE>, a, lds, cu_limit, st, 512);
 }
 
 }  // namespace moe

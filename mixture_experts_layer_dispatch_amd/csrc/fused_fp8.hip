@@ -3,8 +3,11 @@
 
 namespace moe {
 
-hipError_t launch_fused_fp8(FusedArgs &a, bool decode, int bm, int bn2, size_t lds, int cu_limit, hipStream_t st) {
+// w8: the 8-wave tiles apply (their A operands addressed with 32-bit byte offsets)
+hipError_t launch_fused_fp8(FusedArgs &a, bool decode, int bm, int bn2, bool w8, size_t lds, int cu_limit,
+                            hipStream_t st) {
     if (decode) return launch_fused_fn((const void *)fused_decode_kernel<0>, a, lds, cu_limit, st);
+    if (bm == 256 && bn2 == 256 && w8) return launch_fused_kernel8<MODE_FP8>(a, lds, cu_limit, st);
     if (bm == 256 && bn2 == 256) return launch_fused_kernel<MODE_FP8, 256, 256>(a, lds, cu_limit, st);
     if (bm == 256) return launch_fused_kernel<MODE_FP8, 256, 128>(a, lds, cu_limit, st);
     if (bn2 == 256) return launch_fused_kernel<MODE_FP8, 128, 256>(a, lds, cu_limit, st);

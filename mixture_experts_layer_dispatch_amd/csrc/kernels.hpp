@@ -64,6 +64,9 @@ hipError_t launch_ffn(const Shape &s, const FfnPlan &p, const void *w1, const vo
 hipError_t launch_combine(const Shape &s, const void *y_perm, const int32_t *slot_to_row, const float *gate,
                           void *y, hipStream_t st);
 
+// Selection after the split-K router by one wave per token (else one workgroup per token)
+inline bool route_select_by_wave(int E, int nks) { return E <= 256 && nks <= 16; }
+
 // ---- persistent layer kernel -------------------------------------------------------
 //
 // One launch runs every step of the layer.  Work items are numbered in step order and
@@ -81,12 +84,13 @@ constexpr int kSlot = 32;  // ints per 128-byte slot
 enum SyncCounter {
     CNT_QUANT = 0,  // FP8 activation items done
     CNT_ROUTE,      // router items done
-    CNT_SELECT,     // split-K router: tokens selected
+    CNT_SELECT,     // split-K router: selection items done
     CNT_COUNT,      // dispatch histogram blocks done
     CNT_SCATTER,    // dispatch scatter blocks done
     CNT_LIN1,       // tiled path: workgroups past linear1
     CNT_LIN2,       // linear2 items (decode) or workgroups past linear2 (tiled) done
     CNT_EXIT,       // workgroups finished
+    CNT_QUEUE,      // 512-thread tiled path: GEMM items taken, one sub-counter per queue
     NUM_COUNTERS
 };
 enum SyncFlag {
@@ -102,7 +106,9 @@ constexpr size_t kSyncInts = (size_t)kSyncTopScatter + kSlot;
 // SwiGLU blocks (17) and 8 replicas of its "h ready" flag (18-25)
 constexpr int kRowTileSlots = 26;
 
-enum RouterKind { ROUTER_SPLITK = 0, ROUTER_MFMA = 1, ROUTER_VALU8 = 2, ROUTER_VALU32 = 3 };
+enum RouterKind { ROUTER_SPLITK = 0, ROUTER_MFMA = 1, ROUTER_VALU8 = 2, ROUTER_VALU32 = 3, ROUTER_TILE = 4 };
+// routers that leave K-slice partial logits for separate selection items
+__host__ __device__ inline bool router_in_slices(int kind) { return kind == ROUTER_SPLITK || kind == ROUTER_TILE; }
 
 struct FusedArgs {
     int T, d, E, k, F, S, G, gating;
@@ -123,6 +129,7 @@ struct FusedArgs {
     float *rpart, *upart;
     // plan
     int router, nks, nblk;
+    int sel4;  // split-K router: 4 tokens per selection item (a wave each), else 1
     int bm, ntn1, ntn2, ks;
     long rows;
     int nm;   // row tiles bound (kRowTileSlots slots each in done1)

@@ -75,11 +75,11 @@ __global__ __launch_bounds__(256) void route_select_wave_kernel(const float *__r
         route_sum_select_wave<false>(part, nks, T, E, k, gating, bias, t, lgw + wave * E, idx, gate, logits, keys, err);
 }
 
-// Selection after the split-K router: a wave per token when the slices are few (at most 4,
+// Selection after the split-K router: a wave per token when the slices are few (at most 16,
 // E at most 256: all of a lane's loads in flight at once), else a workgroup per token.
 static hipError_t launch_route_select(const Shape &s, int nks, const float *part, const float *bias, int32_t *idx,
                                       float *gate, float *logits, float *keys, int32_t *err, hipStream_t st) {
-    if (nks <= 4 && s.E <= 256)
+    if (route_select_by_wave(s.E, nks))
         MOE_LAUNCH("route_select", route_select_wave_kernel, dim3((unsigned)((s.T + 3) / 4)), dim3(256),
                    (size_t)4 * s.E * sizeof(float), st, part, nks, s.T, s.E, s.k, s.gating, bias, idx, gate, logits,
                    keys, err);

@@ -185,10 +185,11 @@ __device__ __forceinline__ void route_valu_block(const void *x, const void *wr, 
                                                  float *gate, float *logits, float *keys, int32_t *err) {
     const int wave = threadIdx.x / kWave;
     const long t = (long)b * 4 + wave;
-    float *lg = lds + wave * E;
-    if (t < T) route_valu_token<F32, CH>(x, wr, d, E, t, lg);
+    const bool act = wave < 4 && t < T;  // waves past 4 (a larger workgroup) only meet the barrier
+    float *lg = lds + (wave & 3) * E;
+    if (act) route_valu_token<F32, CH>(x, wr, d, E, t, lg);
     __syncthreads();
-    if (t < T) select_token<COH>(lg, E, k, gating, bias, t, idx, gate, logits, keys, err);
+    if (act) select_token<COH>(lg, E, k, gating, bias, t, idx, gate, logits, keys, err);
 }
 
 // ---- MFMA router (bf16, E a multiple of 32): 32 tokens per workgroup ----------
@@ -211,7 +212,7 @@ __device__ __forceinline__ void route_mfma_block(const uint16_t *__restrict__ x,
     long trow = t0 + (lane & 31);
     if (trow >= T) trow = T - 1;
     const uint16_t *xa = x + trow * d + 8 * (lane >> 5);
-    for (int p = 0; p < ntile; p += 8) {
+    for (int p = 0; p < (wave < 4 ? ntile : 0); p += 8) {  // waves past 4 only meet the barrier
         const int nt0 = p + wave, nt1 = p + wave + 4;
         const bool has0 = nt0 < ntile, has1 = nt1 < ntile;
         const uint16_t *wb0 = wr + (long)((has0 ? nt0 : 0) * 32 + (lane & 31)) * d + 8 * (lane >> 5);
@@ -248,7 +249,7 @@ __device__ __forceinline__ void route_mfma_block(const uint16_t *__restrict__ x,
         }
     }
     __syncthreads();
-    for (int tr = wave; tr < kRouteTok; tr += 4) {
+    for (int tr = wave; tr < (wave < 4 ? kRouteTok : 0); tr += 4) {
         long t = t0 + tr;
         if (t < T) select_token<COH>(lds + tr * E, E, k, gating, bias, t, idx, gate, logits, keys, err);
     }
@@ -329,8 +330,31 @@ __device__ __forceinline__ float sum_slices(const float *__restrict__ part, int 
     return s;
 }
 
+// One wave, token t (E <= 256, at most QS K slices): lane l adds the slices of experts l,
+// l + 64, l + 128, l + 192 in slice order into lg, every load (clamped) in flight together.
+template <bool COH, int QS>
+__device__ __forceinline__ void wave_sum_slices(const float *__restrict__ part, int nks, int T, int E, long t,
+                                                float *lg) {
+    const int lane = lane_id();
+    float v[4][QS];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + kWave * i < E ? lane + kWave * i : E - 1;
+#pragma unroll
+        for (int q = 0; q < QS; ++q) v[i][q] = ldc<COH>(part + ((long)(q < nks ? q : nks - 1) * T + t) * E + e);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int q = 0; q < QS; ++q)
+            if (q < nks) sum += v[i][q];
+        if (lane + kWave * i < E) lg[lane + kWave * i] = sum;
+    }
+}
+
 // One wave, token t: lane l adds the K slices of experts l, l + 64, ... into lg (this
-// wave's E floats of LDS), then selects; used when the slices are few, so that all four
+// wave's E floats of LDS), then selects (E <= 256, at most 16 slices); used when the slices are few, so that all four
 // waves of a workgroup select (four tokens at a time).  Same sums, same order, same bits
 // as route_sum_select.
 template <bool COH>
@@ -338,27 +362,8 @@ __device__ __forceinline__ void route_sum_select_wave(const float *__restrict__ 
                                                       int gating, const float *__restrict__ bias, long t, float *lg,
                                                       int32_t *idx, float *gate, float *logits, float *keys,
                                                       int32_t *err) {
-    const int lane = lane_id();
-    if (nks <= 4 && E <= 4 * kWave) {
-        // every load of the lane (4 experts x 4 slices, clamped) in flight together
-        float v[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = lane + kWave * i < E ? lane + kWave * i : E - 1;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) v[i][q] = ldc<COH>(part + ((long)(q < nks ? q : nks - 1) * T + t) * E + e);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float sum = 0.0f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (q < nks) sum += v[i][q];
-            if (lane + kWave * i < E) lg[lane + kWave * i] = sum;
-        }
-    } else {
-        for (int e = lane; e < E; e += kWave) lg[e] = sum_slices<COH, 16>(part, nks, T, E, t, e);
-    }
+    if (nks <= 4) wave_sum_slices<COH, 4>(part, nks, T, E, t, lg);
+    else wave_sum_slices<COH, 16>(part, nks, T, E, t, lg);
     __builtin_amdgcn_wave_barrier();  // the wave reads back its own LDS stores
     select_token<COH>(lg, E, k, gating, bias, t, idx, gate, logits, keys, err);
 }
