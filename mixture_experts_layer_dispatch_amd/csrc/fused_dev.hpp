@@ -320,22 +320,22 @@ __device__ __forceinline__ void uniform_ints(Args &a) {
 }
 
 template <bool SWIGLU>
-__device__ __noinline__ void bf16_tile8_call(GemmArgs a, int tile) {
+__device__ __noinline__ void bf16_tile8_call(GemmArgs a, int tile, int half) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
     a.A = unip(a.A); a.row_to_slot = unip(a.row_to_slot); a.B = unip(a.B); a.C = unip(a.C);
     a.offsets = unip(a.offsets); a.tile_start = unip(a.tile_start);
     uniform_ints(a);
-    bf16_tile8<SWIGLU, SWIGLU>(a, uni(tile), lds_dyn);
+    bf16_tile8<SWIGLU, SWIGLU>(a, uni(tile), lds_dyn, uni(half));
 }
 
 template <bool SWIGLU>
-__device__ __noinline__ void fp8_tile8_call(Fp8Args a, int tile) {
+__device__ __noinline__ void fp8_tile8_call(Fp8Args a, int tile, int half) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
     a.A = unip(a.A); a.As = unip(a.As); a.row_to_slot = unip(a.row_to_slot); a.B = unip(a.B);
     a.Bs = unip(a.Bs); a.C = unip(a.C); a.Cs = unip(a.Cs); a.offsets = unip(a.offsets);
     a.tile_start = unip(a.tile_start);
     uniform_ints(a);
-    fp8_tile8<SWIGLU ? 1 : 2, SWIGLU ? 8 : 4, SWIGLU, SWIGLU>(a, uni(tile), lds_dyn);
+    fp8_tile8<SWIGLU ? 1 : 2, SWIGLU ? 8 : 4, SWIGLU, SWIGLU>(a, uni(tile), lds_dyn, uni(half));
 }
 
 // Router tile b of the tiled router (the stand-alone path's route_tile_kernel without its
@@ -409,10 +409,14 @@ __device__ __forceinline__ void fused_tiled(const FusedArgs &a, uint8_t *lds) {
         // XCD-aware tile order), linear1 before linear2.  A workgroup leaves linear1 (and
         // counts itself past it) when it first takes a linear2 item or runs out; linear2
         // waits for every workgroup past linear1 -- which each reaches, as linear1 items
-        // wait on nothing.  The taken index is broadcast through LDS between tiles.
+        // wait on nothing.  The taken index is broadcast through LDS between tiles.  Indices
+        // map to tiles as block indices do in the stand-alone kernels, tail split included
+        // (a queue's short last round of 256-row tiles as 128-row halves; C = workgroups
+        // per queue).
         const int nq = P % 8 == 0 ? 8 : 1, qid = (int)(blockIdx.x % nq);
+        const int C = (int)(P / 8 > 0 ? P / 8 : 1);
         int32_t *queue = counter_sub(a.sync, CNT_QUEUE, qid);
-        const long n1 = e1 - a.b_end, n12 = e2 - a.b_end;
+        const long n1 = 8L * ((N1 + 7) / 8 + C / 2), n12 = n1 + 8L * ((N2 + 7) / 8 + C / 2);
         bool past1 = false, open2 = false;
         int *slot = (int *)lds;
         for (;;) {
@@ -422,17 +426,18 @@ __device__ __forceinline__ void fused_tiled(const FusedArgs &a, uint8_t *lds) {
             const long j = (long)*slot * nq + qid;
             __syncthreads();  // every thread has the index before a tile reuses the LDS
             if (j >= n12) break;
+            int half;
             if (j < n1) {
-                const int tile = pick_tile((int)j, (int)N1);
+                const int tile = pick_tile_split((int)j, (int)N1, C, half);
                 if (tile < 0) continue;
                 if constexpr (MODE == MODE_BF16) {
                     GemmArgs g = {(const uint16_t *)a.x, a.r2s, (const uint16_t *)a.w1, (uint16_t *)a.h, a.offsets,
                                   a.ts1, a.T, a.k, a.d, 2 * a.F, a.F, a.G, a.F};
-                    bf16_tile8_call<true>(g, tile);
+                    bf16_tile8_call<true>(g, tile, half);
                 } else {
                     Fp8Args g = {a.xq, a.xs, a.r2s, (const uint8_t *)a.w1, (const uint8_t *)a.w1s, a.h, a.hs,
                                  a.offsets, a.ts1, a.T, a.k, a.d, 2 * a.F, a.F, a.G, a.F};
-                    fp8_tile8_call<true>(g, tile);
+                    fp8_tile8_call<true>(g, tile, half);
                 }
             } else {
                 if (!past1) {
@@ -443,16 +448,16 @@ __device__ __forceinline__ void fused_tiled(const FusedArgs &a, uint8_t *lds) {
                     wg_counter_wait_acquire(a.sync, CNT_LIN1, (int)P, a.err);
                     open2 = true;
                 }
-                const int tile = pick_tile((int)(j - n1), (int)N2);
+                const int tile = pick_tile_split((int)(j - n1), (int)N2, C, half);
                 if (tile < 0) continue;
                 if constexpr (MODE == MODE_BF16) {
                     GemmArgs g = {(const uint16_t *)a.h, nullptr, (const uint16_t *)a.w2, (uint16_t *)a.yperm,
                                   a.offsets, a.ts2, a.T, a.k, a.F, a.d, a.d, a.G, a.F};
-                    bf16_tile8_call<false>(g, tile);
+                    bf16_tile8_call<false>(g, tile, half);
                 } else {
                     Fp8Args g = {(const uint8_t *)a.h, a.hs, nullptr, (const uint8_t *)a.w2, (const uint8_t *)a.w2s,
                                  a.yperm, nullptr, a.offsets, a.ts2, a.T, a.k, a.F, a.d, a.d, a.G, a.F};
-                    fp8_tile8_call<false>(g, tile);
+                    fp8_tile8_call<false>(g, tile, half);
                 }
             }
         }
@@ -472,12 +477,12 @@ __device__ __forceinline__ void fused_tiled(const FusedArgs &a, uint8_t *lds) {
             if constexpr (MODE == MODE_BF16) {
                 GemmArgs g = {(const uint16_t *)a.x, a.r2s, (const uint16_t *)a.w1, (uint16_t *)a.h, a.offsets, a.ts1,
                               a.T, a.k, a.d, 2 * a.F, a.F, a.G, a.F};
-                if constexpr (W8) bf16_tile8_call<true>(g, tile);
+                if constexpr (W8) bf16_tile8_call<true>(g, tile, -1);
                 else bf16_tile<BM, 256, true, true>(g, tile, lds);
             } else {
                 Fp8Args g = {a.xq, a.xs, a.r2s, (const uint8_t *)a.w1, (const uint8_t *)a.w1s, a.h, a.hs, a.offsets,
                              a.ts1, a.T, a.k, a.d, 2 * a.F, a.F, a.G, a.F};
-                if constexpr (W8) fp8_tile8_call<true>(g, tile);
+                if constexpr (W8) fp8_tile8_call<true>(g, tile, -1);
                 else fp8_tile<BM, 256, 4, true, true>(g, tile, lds);
             }
         }
@@ -501,12 +506,12 @@ __device__ __forceinline__ void fused_tiled(const FusedArgs &a, uint8_t *lds) {
             if constexpr (MODE == MODE_BF16) {
                 GemmArgs g = {(const uint16_t *)a.h, nullptr, (const uint16_t *)a.w2, (uint16_t *)a.yperm, a.offsets,
                               a.ts2, a.T, a.k, a.F, a.d, a.d, a.G, a.F};
-                if constexpr (W8) bf16_tile8_call<false>(g, tile);
+                if constexpr (W8) bf16_tile8_call<false>(g, tile, -1);
                 else bf16_tile<BM, BN2, false, false>(g, tile, lds);
             } else {
                 Fp8Args g = {(const uint8_t *)a.h, a.hs, nullptr, (const uint8_t *)a.w2, (const uint8_t *)a.w2s,
                              a.yperm, nullptr, a.offsets, a.ts2, a.T, a.k, a.F, a.d, a.d, a.G, a.F};
-                if constexpr (W8) fp8_tile8_call<false>(g, tile);
+                if constexpr (W8) fp8_tile8_call<false>(g, tile, -1);
                 else fp8_tile<BM, BN2, 2, false, false>(g, tile, lds);
             }
         }
