@@ -523,9 +523,16 @@ __device__ __forceinline__ void fused_tiled(const FusedArgs &a, uint8_t *lds) {
             wg_counter_wait_acquire(a.sync, CNT_LIN2, (int)P, a.err);
             waited = true;
         }
-        if (threadIdx.x < 256)
+        if constexpr (W8) {  // the upper 256 threads take the next round's item
+            const long item = threadIdx.x < 256 ? i : i + P;
+            if (item < e3)
+                combine_lane<false, false>(a.yperm, a.s2r, a.gate, a.y, a.T, a.k, a.d, a.S,
+                                           (item - e2) * 256 + (threadIdx.x & 255));
+            i += P;
+        } else if (threadIdx.x < 256) {
             combine_lane<MODE == MODE_F32, false>(a.yperm, a.s2r, a.gate, a.y, a.T, a.k, a.d, a.S,
                                                   (i - e2) * 256 + threadIdx.x);
+        }
     }
     fused_exit(a, lds);
 }
