@@ -43,6 +43,11 @@ SMALL = {
     # the router as a tiled GEMM (E a multiple of 256, T >= 2048) with a ragged last token tile
     "bf16_router_tiled": Workload("bf16_router_tiled", 2013, "bf16", 2100, 512, 256, 8, 128, 1, "sigmoid",
                                   zipf_alpha=0.25),
+    # 256-row tiles with N a multiple of 256 (at least 160 rows per group): the 8-wave GEMM
+    # tiles, and the persistent kernel's 512-thread variant -- bf16 with the one-pass
+    # router, FP8 x FP4 with the tiled router
+    "bf16_w8": Workload("bf16_w8", 2014, "bf16", 1024, 256, 8, 2, 256, 0, "softmax"),
+    "fp8_w8_tiled_router": Workload("fp8_w8_tiled_router", 2015, "fp8_mxfp4", 5120, 256, 256, 8, 256, 1, "softmax"),
 }
 
 
@@ -95,7 +100,8 @@ def test_small_layer_parity(name):
     log(f"case {name}: rel L2 {err:.2e} (tol {TOL[w.mode]:.0e}), near-tie tokens {near}")
 
 
-@pytest.mark.parametrize("name", ["bf16_sigmoid_shared", "f32_sigmoid_shared", "fp8_softmax_shared", "fp8_decode_5"])
+@pytest.mark.parametrize("name", ["bf16_sigmoid_shared", "f32_sigmoid_shared", "fp8_softmax_shared", "fp8_decode_5",
+                                  "bf16_w8", "fp8_w8_tiled_router"])
 def test_fused_grid_sizes_and_repeats(name):
     """The persistent kernel gives the unfused bits on a full grid, on 8 CUs and on 3 CUs
     (many items per workgroup), call after call (each launch leaves its counters clean for
