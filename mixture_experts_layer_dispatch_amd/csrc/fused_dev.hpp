@@ -366,7 +366,7 @@ static __device__ __noinline__ void route_tile8_call(const uint16_t *x, const ui
 
 // The steps before the GEMMs, out of line as well in the 512-thread kernel (inlined, they
 // would spill there); the kernel arguments are read back as uniform values.
-template <int MODE>
+template <int MODE, bool W8 = true>
 __device__ __noinline__ int front_item_call(FusedArgs a, long i, int routed) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
     static_assert(sizeof(FusedArgs) % 4 == 0, "argument words");
@@ -377,7 +377,7 @@ __device__ __noinline__ int front_item_call(FusedArgs a, long i, int routed) {
     for (int w = 0; w < (int)(sizeof(FusedArgs) / 4); ++w) dst[w] = uni(src[w]);
     const long iu = ((long)uni((int)(i >> 32)) << 32) | (uint32_t)uni((int)i);
     bool r = uni(routed) != 0;
-    front_item<MODE, true>(u, iu, lds_dyn, r);
+    front_item<MODE, W8>(u, iu, lds_dyn, r);
     return r ? 1 : 0;
 }
 
@@ -539,13 +539,26 @@ __device__ __forceinline__ void fused_tiled(const FusedArgs &a, uint8_t *lds) {
 
 // ---- decode variant (FP8 x FP4, few rows per group): wave items after the plan --------
 
+// One weight-streaming tile, out of line (its own register allocation: two blocks of
+// weights in flight per wave), with the plan read from the kernel's LDS.
+template <bool LIN1>
+__device__ __noinline__ void fp8_decode_tile_call(DecArgs d, int tile, int G) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+    const int32_t *lts = (const int32_t *)lds_dyn + (LIN1 ? 0 : uni(G) + 1), *loffs = (const int32_t *)lds_dyn + 2 * (uni(G) + 1);
+    d.A = unip(d.A); d.As = unip(d.As); d.row_to_slot = unip(d.row_to_slot); d.offsets = unip(d.offsets);
+    d.tile_start = unip(d.tile_start); d.B = unip(d.B); d.Bs = unip(d.Bs); d.part = unip(d.part); d.Y = unip(d.Y);
+    d.T = uni(d.T); d.k = uni(d.k); d.K = uni(d.K); d.N = uni(d.N); d.G = uni(d.G); d.ks = uni(d.ks);
+    d.rows = ((long)uni((int)(d.rows >> 32)) << 32) | (uint32_t)uni((int)d.rows);
+    fp8_decode_tile<LIN1, true, true>(d, uni(tile), lts, loffs);
+}
+
 __device__ __forceinline__ void fused_decode(const FusedArgs &a, uint8_t *lds) {
     const long P = gridDim.x;
     long i = blockIdx.x;
     bool routed = false;
     for (; i < a.b_end; i += P) {
         __syncthreads();
-        front_item<MODE_FP8>(a, i, lds, routed);
+        routed = front_item_call<MODE_FP8, false>(a, i, routed ? 1 : 0) != 0;
     }
     wg_flag_wait(a.sync, FLAG_FRONT, a.err);
     // the plan in LDS: tile prefixes of both GEMMs and the group offsets
@@ -572,7 +585,7 @@ __device__ __forceinline__ void fused_decode(const FusedArgs &a, uint8_t *lds) {
     for (long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6); w < e3; w += 4 * P) {
         if (w < e1) {  // linear1 K slice of a (32 rows x 32 columns) tile
             const int tile = (int)w;
-            fp8_decode_tile<true, true>(d1, tile, lts1, loffs);
+            fp8_decode_tile_call<true>(d1, tile, G);
             const TileInfo ti = decode_tile(tile, lts1, loffs, G, 32);
             int32_t *rt = row_tile(lts1[ti.g] / a.ntn1 + ti.mt);
             // two-level count of this row tile's linear1 items: sub-counter (item % 8), then
@@ -608,7 +621,7 @@ __device__ __forceinline__ void fused_decode(const FusedArgs &a, uint8_t *lds) {
             const int tile = (int)(w - es);
             const TileInfo ti = decode_tile(tile, lts2, loffs, G, 32);
             spin_until<4>(row_tile(lts2[ti.g] / a.ntn2 + ti.mt) + (18 + (int)(w % 8)) * kSlot, 1, a.err);
-            fp8_decode_tile<false, true>(d2, tile, lts2, loffs);
+            fp8_decode_tile_call<false>(d2, tile, G);
             wait_vmcnt<0>();
             compiler_fence();
             if (lane == 0) atomic_add(counter_sub(a.sync, CNT_LIN2, w), 1);
@@ -637,10 +650,11 @@ __global__ __launch_bounds__(512) void fused_layer_kernel8(FusedArgs a) {
     fused_tiled<MODE, 256, 256, true>(a, lds);
 }
 
-// The decode variant streams weights: it is held to 128 registers so that four waves
-// share each SIMD.
+// The decode variant streams weights: two waves per SIMD, its weight-streaming tiles (two
+// blocks in flight per wave) and the steps before them called out of line, each with its
+// own register allocation.
 template <int UNUSED = 0>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void fused_decode_kernel(FusedArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fused_decode_kernel(FusedArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     fused_decode(a, lds);
 }
