@@ -364,8 +364,9 @@ static __device__ __noinline__ void route_tile8_call(const uint16_t *x, const ui
     bf16_tile8_rows<false, false, true>(g, ti, d, ks * kchunk, kchunk / 32, lds_dyn);
 }
 
-// The steps before the GEMMs, out of line as well in the 512-thread kernel (inlined, they
-// would spill there); the kernel arguments are read back as uniform values.
+// The steps before the GEMMs, out of line in the 512-thread and decode kernels (inlined
+// there, they would share those kernels' register allocation and spill); the kernel
+// arguments are read back as uniform values.  W8: the 512-thread kernel's items.
 template <int MODE, bool W8 = true>
 __device__ __noinline__ int front_item_call(FusedArgs a, long i, int routed) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
@@ -464,60 +465,58 @@ __device__ __forceinline__ void fused_tiled(const FusedArgs &a, uint8_t *lds) {
         if (!past1) wg_release_count(a.sync, CNT_LIN1);
         i = e2 + blockIdx.x;  // the combine items stay dealt round robin
     }
-    for (; i < e1; i += P) {  // linear1
-        __syncthreads();
-        const long j = i - a.b_end;
-        if constexpr (MODE == MODE_F32) {
-            if (j < N1)
-                ffn1_f32_lane((const float *)a.x, a.r2s, (const float *)a.w1, a.offsets, a.G, a.T, a.k, a.d, a.F,
-                              a.rows, (float *)a.h, j * 256 + threadIdx.x);
-        } else {
-            const int tile = pick_tile((int)j, (int)N1);
-            if (tile < 0) continue;
-            if constexpr (MODE == MODE_BF16) {
-                GemmArgs g = {(const uint16_t *)a.x, a.r2s, (const uint16_t *)a.w1, (uint16_t *)a.h, a.offsets, a.ts1,
-                              a.T, a.k, a.d, 2 * a.F, a.F, a.G, a.F};
-                if constexpr (W8) bf16_tile8_call<true>(g, tile, -1);
-                else bf16_tile<BM, 256, true, true>(g, tile, lds);
+    if constexpr (!W8) {  // GEMM items dealt round robin
+        for (; i < e1; i += P) {  // linear1
+            __syncthreads();
+            const long j = i - a.b_end;
+            if constexpr (MODE == MODE_F32) {
+                if (j < N1)
+                    ffn1_f32_lane((const float *)a.x, a.r2s, (const float *)a.w1, a.offsets, a.G, a.T, a.k, a.d,
+                                  a.F, a.rows, (float *)a.h, j * 256 + threadIdx.x);
             } else {
-                Fp8Args g = {a.xq, a.xs, a.r2s, (const uint8_t *)a.w1, (const uint8_t *)a.w1s, a.h, a.hs, a.offsets,
-                             a.ts1, a.T, a.k, a.d, 2 * a.F, a.F, a.G, a.F};
-                if constexpr (W8) fp8_tile8_call<true>(g, tile, -1);
-                else fp8_tile<BM, 256, 4, true, true>(g, tile, lds);
+                const int tile = pick_tile((int)j, (int)N1);
+                if (tile < 0) continue;
+                if constexpr (MODE == MODE_BF16) {
+                    GemmArgs g = {(const uint16_t *)a.x, a.r2s, (const uint16_t *)a.w1, (uint16_t *)a.h, a.offsets,
+                                  a.ts1, a.T, a.k, a.d, 2 * a.F, a.F, a.G, a.F};
+                    bf16_tile<BM, 256, true, true>(g, tile, lds);
+                } else {
+                    Fp8Args g = {a.xq, a.xs, a.r2s, (const uint8_t *)a.w1, (const uint8_t *)a.w1s, a.h, a.hs,
+                                 a.offsets, a.ts1, a.T, a.k, a.d, 2 * a.F, a.F, a.G, a.F};
+                    fp8_tile<BM, 256, 4, true, true>(g, tile, lds);
+                }
             }
         }
-    }
-    if constexpr (!W8) wg_release_count(a.sync, CNT_LIN1);  // (W8: counted in the queue loop)
-    bool waited = false;
-    for (; i < e2; i += P) {  // linear2
-        if (!waited) {
-            wg_counter_wait_acquire(a.sync, CNT_LIN1, (int)P, a.err);
-            waited = true;
-        }
-        __syncthreads();
-        const long j = i - e1;
-        if constexpr (MODE == MODE_F32) {
-            if (j < N2)
-                ffn2_f32_lane((const float *)a.h, (const float *)a.w2, a.offsets, a.G, a.d, a.F, a.rows,
-                              (float *)a.yperm, j * 256 + threadIdx.x);
-        } else {
-            const int tile = pick_tile((int)j, (int)N2);
-            if (tile < 0) continue;
-            if constexpr (MODE == MODE_BF16) {
-                GemmArgs g = {(const uint16_t *)a.h, nullptr, (const uint16_t *)a.w2, (uint16_t *)a.yperm, a.offsets,
-                              a.ts2, a.T, a.k, a.F, a.d, a.d, a.G, a.F};
-                if constexpr (W8) bf16_tile8_call<false>(g, tile, -1);
-                else bf16_tile<BM, BN2, false, false>(g, tile, lds);
+        wg_release_count(a.sync, CNT_LIN1);
+        bool open2 = false;
+        for (; i < e2; i += P) {  // linear2
+            if (!open2) {
+                wg_counter_wait_acquire(a.sync, CNT_LIN1, (int)P, a.err);
+                open2 = true;
+            }
+            __syncthreads();
+            const long j = i - e1;
+            if constexpr (MODE == MODE_F32) {
+                if (j < N2)
+                    ffn2_f32_lane((const float *)a.h, (const float *)a.w2, a.offsets, a.G, a.d, a.F, a.rows,
+                                  (float *)a.yperm, j * 256 + threadIdx.x);
             } else {
-                Fp8Args g = {(const uint8_t *)a.h, a.hs, nullptr, (const uint8_t *)a.w2, (const uint8_t *)a.w2s,
-                             a.yperm, nullptr, a.offsets, a.ts2, a.T, a.k, a.F, a.d, a.d, a.G, a.F};
-                if constexpr (W8) fp8_tile8_call<false>(g, tile, -1);
-                else fp8_tile<BM, BN2, 2, false, false>(g, tile, lds);
+                const int tile = pick_tile((int)j, (int)N2);
+                if (tile < 0) continue;
+                if constexpr (MODE == MODE_BF16) {
+                    GemmArgs g = {(const uint16_t *)a.h, nullptr, (const uint16_t *)a.w2, (uint16_t *)a.yperm,
+                                  a.offsets, a.ts2, a.T, a.k, a.F, a.d, a.d, a.G, a.F};
+                    bf16_tile<BM, BN2, false, false>(g, tile, lds);
+                } else {
+                    Fp8Args g = {(const uint8_t *)a.h, a.hs, nullptr, (const uint8_t *)a.w2, (const uint8_t *)a.w2s,
+                                 a.yperm, nullptr, a.offsets, a.ts2, a.T, a.k, a.F, a.d, a.d, a.G, a.F};
+                    fp8_tile<BM, BN2, 2, false, false>(g, tile, lds);
+                }
             }
         }
     }
     wg_release_count(a.sync, CNT_LIN2);
-    waited = false;
+    bool waited = false;
     for (; i < e3; i += P) {  // combine
         if (!waited) {
             wg_counter_wait_acquire(a.sync, CNT_LIN2, (int)P, a.err);
