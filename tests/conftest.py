@@ -10,4 +10,4 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
-    config.addinivalue_line("markers", "slow: full-size workload (GPU box only)")
+    config.addinivalue_line("markers", "slow: full-size workload (needs the GPU and minutes)")
