@@ -206,7 +206,7 @@ __device__ __forceinline__ void bf16_tile(const GemmArgs &a, int tile, uint8_t *
 #pragma unroll
                 for (int j = 0; j < TNh; ++j) {
                     float gv = acc[i][j][r], uv = acc[i][j + TNh][r];
-                    float h = gv / (1.0f + __expf(-gv)) * uv;
+                    float h = swiglu(gv, uv);
                     int f = f0 + wn * (BN / 4) + j * 32 + (lane & 31);
                     a.C[grow * a.F + f] = f32_to_bf16(h);
                 }
@@ -408,7 +408,7 @@ __device__ __forceinline__ void bf16_tile8_core(const GemmArgs &a, const TileInf
             const long grow = ti.row0 + row;
             if (SWIGLU) {
                 const float gv = acc[i][0][r], uv = acc[i][1][r];
-                const float h = gv / (1.0f + __expf(-gv)) * uv;
+                const float h = swiglu(gv, uv);
                 a.C[grow * a.F + f0 + wn * 32 + (lane & 31)] = f32_to_bf16(h);
             } else if (F32OUT) {
 #pragma unroll

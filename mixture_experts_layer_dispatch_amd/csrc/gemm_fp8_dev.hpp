@@ -282,7 +282,7 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args &a, int tile, uint8_t *ld
 #pragma unroll
                 for (int j = 0; j < TNh; ++j) {
                     float gv = acc[i][j][r], uv = acc[i][j + TNh][r];
-                    hv[j] = gv / (1.0f + __expf(-gv)) * uv;
+                    hv[j] = swiglu(gv, uv);
                     amax = fmaxf(amax, fabsf(hv[j]));
                 }
                 // the 32 lanes of this half-wave hold the 128 columns of the row
@@ -673,7 +673,7 @@ __device__ __forceinline__ void fp8_tile8(const Fp8Args &a, int tile, uint8_t *l
 #pragma unroll
                 for (int j = 0; j < TNh; ++j) {
                     const float gv = acc[i][j][r], uv = acc[i][j + TNh][r];
-                    hv[j] = gv / (1.0f + __expf(-gv)) * uv;
+                    hv[j] = swiglu(gv, uv);
                     amax = fmaxf(amax, fabsf(hv[j]));
                 }
 #pragma unroll
@@ -1003,7 +1003,7 @@ __device__ __forceinline__ void decode_swiglu_wave(const float *__restrict__ par
     }
     float h[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) h[i] = gsum[i] / (1.0f + __expf(-gsum[i])) * usum[i];
+    for (int i = 0; i < 2; ++i) h[i] = swiglu(gsum[i], usum[i]);
     float amax = fmaxf(fabsf(h[0]), fabsf(h[1]));
     amax = wave_max(amax);
     const int e = e4m3_block_exponent(amax);
