@@ -90,6 +90,28 @@ __device__ __forceinline__ uint32_t cvt_e4m3x4(float a, float b, float c, float 
     return (uint32_t)w;
 }
 
+// ---- lane reductions with DPP -------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over each row of 16 lanes, left in every lane of the row: quad swaps, then the
+// half-row and row mirrors (max is exact, so any pairing gives the same value).
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_f32<0xB1>(v));     // quad_perm [1, 0, 3, 2]
+    v = fmaxf(v, dpp_f32<0x4E>(v));     // quad_perm [2, 3, 0, 1]
+    v = fmaxf(v, dpp_f32<0x141>(v));    // row_half_mirror
+    return fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+}
+
+// Maximum over each half-wave (lanes 0-31, 32-63): the rows, then one swap across them.
+__device__ __forceinline__ float half_wave_max(float v) {
+    v = row16_max(v);
+    return fmaxf(v, __shfl_xor(v, 16, kWave));
+}
+
 // ---- LDS DMA, counted waits and LDS swizzles (shared by the GEMM tiles) ----------
 
 // global_load_lds_dwordx4 / _dword (gfx950): lane L's bytes land in LDS at (M0 base +

@@ -293,8 +293,7 @@ __device__ __forceinline__ void quant_x_lane(const uint16_t *__restrict__ x, lon
         v[i] = bf16_to_f32(h[i]);
         amax = fmaxf(amax, fabsf(v[i]));
     }
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 16));
+    amax = row16_max(amax);
     if (!live) return;
     const int e = e4m3_block_exponent(amax);
     const float inv = ldexpf(1.0f, -e);

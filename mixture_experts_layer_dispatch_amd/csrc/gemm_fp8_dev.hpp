@@ -286,8 +286,7 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args &a, int tile, uint8_t *ld
                     amax = fmaxf(amax, fabsf(hv[j]));
                 }
                 // the 32 lanes of this half-wave hold the 128 columns of the row
-#pragma unroll
-                for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+                amax = half_wave_max(amax);
                 if (row < nrows) {
                     const int e = e4m3_block_exponent(amax);
                     const float inv = ldexpf(1.0f, -e);
@@ -676,8 +675,7 @@ __device__ __forceinline__ void fp8_tile8(const Fp8Args &a, int tile, uint8_t *l
                     hv[j] = swiglu(gv, uv);
                     amax = fmaxf(amax, fabsf(hv[j]));
                 }
-#pragma unroll
-                for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+                amax = half_wave_max(amax);
                 if (row < nrows) {
                     const int e = e4m3_block_exponent(amax);
                     const float inv = ldexpf(1.0f, -e);
