@@ -182,6 +182,24 @@ moe_status moe_dispatch(const moe_cfg *cfg, const int32_t *topk_idx, const void 
                         float *xq_scale, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_dispatch for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * kernels and results as moe_dispatch, without a workspace: the per-(dispatch block,
+ * expert) counts those kernels need live in a fixed 1 MiB device array of the library
+ * (one per GPU, held until the process ends), so dispatch_blocks(T) * E * 4 bytes must
+ * fit -- (T + 255) / 256 * E <= 262144, e.g. T <= 262144 at E = 256; larger shapes
+ * return MOE_ERR_WORKSPACE.  The call allocates nothing.
+ *  err: device pointer to one int32, the sticky error word for bad or duplicate indices
+ *       (first error wins; the caller clears it), or NULL to skip the checks' report.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU (two
+ * streams, two threads) race and must be serialised by the caller.  Each call writes
+ * every array word it reads first, so nothing needs clearing between calls.
+ */
+moe_status moe_dispatch_noalloc(const moe_cfg *cfg, const int32_t *topk_idx, const void *x, int32_t *counts,
+                                int32_t *offsets, int32_t *slot_to_row, int32_t *row_to_slot, uint8_t *xq,
+                                float *xq_scale, int32_t *err, hipStream_t stream);
+
+/*
  * Expert FFNs over the dispatched rows: linear1 (gate+up) with SwiGLU fused in
  * its epilogue, then linear2 (Mega MoE blog, donniechu.com, spec table).
  * Row r of group g reads token row_to_slot[r] / k (routed) or r - T*k (shared).

@@ -66,11 +66,12 @@ def lib():
         L.moe_ffn.argtypes = [CP, WP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_combine.argtypes = [CP, VP, VP, VP, VP, VP]
         L.moe_layer_fused.argtypes = [CP, WP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_dispatch_noalloc.argtypes = [CP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP]
         L.moe_profile_enable.argtypes = [I32]
         L.moe_profile_report.argtypes = [ctypes.c_char_p, SZ]
         L.moe_profile_report.restype = I32
         for f in ("moe_profile_enable", "moe_device_check", "moe_clear_device_error", "moe_read_device_error", "moe_route",
-                  "moe_dispatch", "moe_ffn", "moe_combine", "moe_layer_fused"):
+                  "moe_dispatch", "moe_ffn", "moe_combine", "moe_layer_fused", "moe_dispatch_noalloc"):
             getattr(L, f).restype = I32
         _lib = L
     return _lib
@@ -78,7 +79,7 @@ def lib():
 
 EXPORTS = ("moe_status_str", "moe_device_check", "moe_workspace_bytes", "moe_clear_device_error",
            "moe_read_device_error", "moe_route", "moe_dispatch", "moe_ffn", "moe_combine", "moe_layer_fused",
-           "moe_profile_enable", "moe_profile_report")
+           "moe_profile_enable", "moe_profile_report", "moe_dispatch_noalloc")
 
 
 @dataclass(frozen=True)
@@ -218,6 +219,32 @@ def dispatch(cfg: Config, topk_idx, x=None, *, ws, out=None, stream=None):
     _check(lib().moe_dispatch(ctypes.byref(cfg.c()), _p(topk_idx), _p(x), _p(o["counts"]), _p(o["offsets"]),
                               _p(o["slot_to_row"]), _p(o["row_to_slot"]), _p(o["xq"]), _p(o["xq_scale"]),
                               _p(ws), ws.numel(), _stream(stream)), "moe_dispatch")
+    return o
+
+
+def dispatch_noalloc(cfg: Config, topk_idx, x=None, *, err=None, out=None, stream=None):
+    """S5-S7 without a workspace (moe_dispatch_noalloc): the library's fixed device scratch
+    holds the block counts.  err: optional int32 [1] device tensor, the sticky error word.
+    Returns the same dict as dispatch()."""
+    dev = topk_idx.device
+    _expect(topk_idx, (cfg.T, cfg.k), torch.int32, "topk_idx")
+    o = dict(out or {})
+    o.setdefault("counts", torch.empty(cfg.G, dtype=torch.int32, device=dev))
+    o.setdefault("offsets", torch.empty(cfg.G + 1, dtype=torch.int32, device=dev))
+    o.setdefault("slot_to_row", torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev))
+    o.setdefault("row_to_slot", torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev))
+    if cfg.mode == "fp8_mxfp4":
+        _expect(x, (cfg.T, cfg.d), torch.bfloat16, "x")
+        o.setdefault("xq", torch.empty(cfg.T, cfg.d, dtype=torch.uint8, device=dev))
+        o.setdefault("xq_scale", torch.empty(cfg.T, cfg.d // 128, dtype=torch.float32, device=dev))
+    else:
+        o.setdefault("xq", None)
+        o.setdefault("xq_scale", None)
+    if err is not None:
+        _expect(err, (1,), torch.int32, "err")
+    _check(lib().moe_dispatch_noalloc(ctypes.byref(cfg.c()), _p(topk_idx), _p(x), _p(o["counts"]),
+                                      _p(o["offsets"]), _p(o["slot_to_row"]), _p(o["row_to_slot"]), _p(o["xq"]),
+                                      _p(o["xq_scale"]), _p(err), _stream(stream)), "moe_dispatch_noalloc")
     return o
 
 
