@@ -229,7 +229,11 @@ moe_status moe_combine(const moe_cfg *cfg, const void *y_perm, const int32_t *sl
  * counters in the workspace with bounded waits.  A cooperative launch of every
  * workgroup the device (or cfg->cu_limit CUs) can hold at once; MOE_ERR_LAUNCH if the
  * runtime cannot make it co-resident.  A wait that exceeds 2 s sets
- * MOE_DEVERR_TIMEOUT and the call's outputs are then unspecified.  Bitwise equal to
+ * MOE_DEVERR_TIMEOUT (if the error word is still clear) and raises a second word
+ * of the workspace's error region, so every later wait of the launch gives up at
+ * once, whatever code the error word holds; a wait also gives up at once while the
+ * error word reads MOE_DEVERR_TIMEOUT.  The call's outputs are then unspecified, and
+ * the launch still clears its synchronisation words (and that second word) on exit.  Bitwise equal to
  * moe_route -> moe_dispatch -> moe_ffn -> moe_combine on the same inputs.
  *  x [T, d], w_router [E, d], bias [E] or NULL, w: as above; y [T, d] out.
  *  topk_idx_out [T, k], topk_gate_out [T, k], counts_out [G]: optional copies (NULL to skip).

@@ -4,6 +4,9 @@
 #include "fused_dev.hpp"
 #include "kernels.hpp"
 
+#include <mutex>
+#include <vector>
+
 namespace moe {
 
 hipError_t launch_fused_bf16(FusedArgs &a, int bm, int bn2, size_t lds, int cu_limit, hipStream_t st);
@@ -74,6 +77,35 @@ size_t fused_lds_bytes(const Shape &s, const FfnPlan &p) {
     const size_t cached = p.decode ? (size_t)3 * (s.G() + 1) * 4 : 0;  // the plan, kept in LDS
     for (size_t v : {r, m, plan, cached}) b = v > b ? v : b;
     return b;
+}
+
+hipError_t fused_occupancy(const void *fn, int dev, int threads, size_t lds, int &cus, int &per_cu) {
+    struct Entry {
+        const void *fn;
+        int dev, threads;
+        size_t lds;
+        int cus, per_cu;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    std::lock_guard<std::mutex> lk(mu);
+    for (const Entry &c : cache)
+        if (c.fn == fn && c.dev == dev && c.threads == threads && c.lds == lds) {
+            cus = c.cus;
+            per_cu = c.per_cu;
+            return hipSuccess;
+        }
+    if (lds > 65536) {
+        // the cap of the kernel's dynamic LDS: the whole 160 KB of a CU, so that every LDS
+        // size a later launch asks for is within it
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+    }
+    hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds);
+    if (e != hipSuccess) return e;
+    cache.push_back({fn, dev, threads, lds, cus, per_cu});
+    return hipSuccess;
 }
 
 hipError_t launch_layer_fused(const Shape &s, const FfnPlan &p, FusedArgs &a, int cu_limit, hipStream_t st) {

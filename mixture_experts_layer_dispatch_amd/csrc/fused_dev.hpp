@@ -55,6 +55,18 @@ __device__ __forceinline__ int atomic_add(int32_t *p, int v) {
 }
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
+// Timeouts.  The sticky error word err[0] keeps the first error of any kind; err[1] is
+// raised by every wait that expires, so the later waits of the launch give up at once
+// even when err[0] already held another code.  A wait also gives up when err[0] reads
+// DEVERR_TIMEOUT.  The launch's last workgroup clears err[1] on its way out.
+__device__ __forceinline__ bool timed_out(const int32_t *err) {
+    return atomic_ld(err + 1) != 0 || atomic_ld(err) == DEVERR_TIMEOUT;
+}
+__device__ __forceinline__ void report_timeout(int32_t *err) {
+    set_error(err, DEVERR_TIMEOUT);
+    __hip_atomic_store(err + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Lane 0 spins until *p >= target, or until a timeout is (or was) reported.  The sleep
 // between polls doubles up to MAXSLEEP x 8 x 64 cycles: many waves polling one word at
 // full rate would starve the memory channel that serves it, and with it the very
@@ -66,9 +78,9 @@ __device__ __forceinline__ void spin_until(const int32_t *p, int target, int32_t
         int backoff = 1;
         for (unsigned n = 1; atomic_ld(p) < target; ++n) {
             if ((n & 15) == 0) {
-                if (atomic_ld(err) == DEVERR_TIMEOUT) break;
+                if (timed_out(err)) break;
                 if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
-                    set_error(err, DEVERR_TIMEOUT);
+                    report_timeout(err);
                     break;
                 }
             }
@@ -105,9 +117,9 @@ __device__ __forceinline__ void counter_wait(int32_t *sync, int c, int target, i
         int backoff = 1;
         for (unsigned n = 1; counter_sum(sync, c) < target; ++n) {
             if ((n & 15) == 0) {
-                if (__shfl(atomic_ld(err), 0, kWave) == DEVERR_TIMEOUT) break;
+                if (__shfl((int)timed_out(err), 0, kWave)) break;
                 if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
-                    if (lane_id() == 0) set_error(err, DEVERR_TIMEOUT);
+                    if (lane_id() == 0) report_timeout(err);
                     break;
                 }
             }
@@ -296,6 +308,7 @@ __device__ __forceinline__ void fused_exit(const FusedArgs &a, uint8_t *lds) {
         if (threadIdx.x == 0) {
             __hip_atomic_store(a.sync + kSyncTopExit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(a.sync + kSyncTopScatter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.err + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -658,18 +671,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     fused_decode(a, lds);
 }
 
+// Workgroups per CU of a kernel at (threads, lds) on device dev, and the device's CU
+// count: queried once per (kernel, device, threads, LDS bytes) and kept, together with
+// the kernel's LDS attribute, so a launch makes no runtime query.
+hipError_t fused_occupancy(const void *fn, int dev, int threads, size_t lds, int &cus, int &per_cu);
+
 // Host side: a cooperative launch of as many workgroups as fit on the device at once
 // (at most cu_limit CUs' worth when cu_limit > 0).
 inline hipError_t launch_fused_fn(const void *fn, FusedArgs &a, size_t lds, int cu_limit, hipStream_t st,
                                   int threads = 256) {
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds);
+    if (e == hipSuccess) e = fused_occupancy(fn, dev, threads, lds, cus, per_cu);
     if (e != hipSuccess) return e;
     if (per_cu < 1) return hipErrorInvalidConfiguration;
     if (cu_limit > 0 && cu_limit < cus) cus = cu_limit;
