@@ -132,6 +132,23 @@ moe_status moe_device_check(void);
 size_t moe_workspace_bytes(const moe_cfg *cfg);
 
 /*
+ * Where an intermediate result lives in a workspace, for verification tools (the
+ * layout is otherwise private and may change between versions of the library).
+ *  MOE_WS_ERROR:   the error words (256 bytes; the sticky error word first).
+ *  MOE_WS_H:       h, the SwiGLU output per dispatched row [T*k + n_shared*T, F]: fp32
+ *                  (F32 mode), bf16 (BF16 mode) or e4m3 codes (FP8 x MXFP4 mode).
+ *  MOE_WS_H_SCALE: FP8 x MXFP4 mode: h's power-of-two fp32 scales [rows, F/128]
+ *                  (0 bytes in the other modes).
+ * moe_ffn and moe_layer_fused leave h there; row r is dispatched row r.
+ * *offset and *bytes (host memory) receive the region's byte offset from the start of
+ * the workspace and its size.  MOE_ERR_SHAPE for an unknown region.
+ */
+#define MOE_WS_ERROR 0
+#define MOE_WS_H 1
+#define MOE_WS_H_SCALE 2
+moe_status moe_workspace_region(const moe_cfg *cfg, int32_t region, size_t *offset, size_t *bytes);
+
+/*
  * Clears the sticky error word and the persistent kernel's synchronisation words
  * (stream-ordered).  A workspace must be zero-filled, or cleared by this call, before
  * its first moe_layer_fused; every moe_layer_fused launch leaves those words zero
@@ -198,6 +215,24 @@ moe_status moe_dispatch(const moe_cfg *cfg, const int32_t *topk_idx, const void 
 moe_status moe_dispatch_noalloc(const moe_cfg *cfg, const int32_t *topk_idx, const void *x, int32_t *counts,
                                 int32_t *offsets, int32_t *slot_to_row, int32_t *row_to_slot, uint8_t *xq,
                                 float *xq_scale, int32_t *err, hipStream_t stream);
+
+/*
+ * The FP8 activation quantiser on its own: rows of K values (K a multiple of 128) to
+ * e4m3 codes with one power-of-two fp32 scale per 1x128 block along K -- the rule the
+ * FP8 x MXFP4 mode applies to x (moe_dispatch) and to h (the linear1 epilogue), with the
+ * same conversion instructions.  Scale 2^e, e the smallest integer with
+ * max|v| <= 448 * 2^e over the block (clamped to [-127, 127]; an all-zero block has
+ * e = 0); code_i = e4m3 round-to-nearest-even of v_i * 2^-e (Mega MoE blog,
+ * donniechu.com, spec table: FP8 activations).  Feeds moe_gemm_fp8_mxfp4.
+ *  in [rows, K]         fp32 (in_dtype MOE_QUANT_IN_F32) or bf16 (MOE_QUANT_IN_BF16)
+ *  codes [rows, K]      uint8 out
+ *  scales [rows, K/128] fp32 out
+ * Inputs must be finite.  rows == 0 is a no-op.
+ */
+#define MOE_QUANT_IN_F32 0
+#define MOE_QUANT_IN_BF16 1
+moe_status moe_quant_e4m3(const void *in, int32_t in_dtype, int64_t rows, int32_t K, uint8_t *codes, float *scales,
+                          hipStream_t stream);
 
 /*
  * Expert FFNs over the dispatched rows: linear1 (gate+up) with SwiGLU fused in

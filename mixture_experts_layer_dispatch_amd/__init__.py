@@ -66,6 +66,10 @@ def lib():
         L.moe_ffn.argtypes = [CP, WP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_combine.argtypes = [CP, VP, VP, VP, VP, VP]
         L.moe_layer_fused.argtypes = [CP, WP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_workspace_region.argtypes = [CP, I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
+        L.moe_workspace_region.restype = I32
+        L.moe_quant_e4m3.argtypes = [VP, I32, ctypes.c_int64, I32, VP, VP, VP]
+        L.moe_quant_e4m3.restype = I32
         L.moe_dispatch_noalloc.argtypes = [CP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP]
         L.moe_profile_enable.argtypes = [I32]
         L.moe_profile_report.argtypes = [ctypes.c_char_p, SZ]
@@ -79,7 +83,8 @@ def lib():
 
 EXPORTS = ("moe_status_str", "moe_device_check", "moe_workspace_bytes", "moe_clear_device_error",
            "moe_read_device_error", "moe_route", "moe_dispatch", "moe_ffn", "moe_combine", "moe_layer_fused",
-           "moe_profile_enable", "moe_profile_report", "moe_dispatch_noalloc")
+           "moe_profile_enable", "moe_profile_report", "moe_dispatch_noalloc",
+           "moe_workspace_region", "moe_quant_e4m3")
 
 
 @dataclass(frozen=True)
@@ -169,6 +174,18 @@ def alloc_workspace(cfg: Config, device="cuda") -> torch.Tensor:
     return ws
 
 
+WS_REGIONS = {"error": 0, "h": 1, "h_scale": 2}
+
+
+def workspace_region(cfg: Config, ws: torch.Tensor, region: str) -> torch.Tensor:
+    """A byte view of an internal workspace region (moe_workspace_region): "error", "h" or
+    "h_scale" (verification only; the layout is private to the library)."""
+    off, n = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(lib().moe_workspace_region(ctypes.byref(cfg.c()), WS_REGIONS[region], ctypes.byref(off),
+                                      ctypes.byref(n)), "moe_workspace_region")
+    return ws[off.value: off.value + n.value]
+
+
 def clear_device_error(cfg: Config, ws: torch.Tensor, stream=None):
     _check(lib().moe_clear_device_error(ctypes.byref(cfg.c()), _p(ws), ws.numel(), _stream(stream)),
            "moe_clear_device_error")
@@ -246,6 +263,21 @@ def dispatch_noalloc(cfg: Config, topk_idx, x=None, *, err=None, out=None, strea
                                       _p(o["offsets"]), _p(o["slot_to_row"]), _p(o["row_to_slot"]), _p(o["xq"]),
                                       _p(o["xq_scale"]), _p(err), _stream(stream)), "moe_dispatch_noalloc")
     return o
+
+
+def quant_e4m3(v, *, codes=None, scales=None, stream=None):
+    """Rows [rows, K] of fp32 or bf16 -> (e4m3 codes uint8 [rows, K], fp32 power-of-two
+    scales [rows, K/128]) (moe_quant_e4m3)."""
+    if v.dim() != 2 or v.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("expected a 2-D fp32 or bf16 tensor")
+    rows, K = v.shape
+    codes = codes if codes is not None else torch.empty(rows, K, dtype=torch.uint8, device=v.device)
+    scales = scales if scales is not None else torch.empty(rows, K // 128, dtype=torch.float32, device=v.device)
+    _expect(codes, (rows, K), torch.uint8, "codes")
+    _expect(scales, (rows, K // 128), torch.float32, "scales")
+    _check(lib().moe_quant_e4m3(_p(v), 0 if v.dtype == torch.float32 else 1, rows, K, _p(codes), _p(scales),
+                                _stream(stream)), "moe_quant_e4m3")
+    return codes, scales
 
 
 def _weights(cfg: Config, w1, w2, w1_scale=None, w2_scale=None) -> MoeWeights:

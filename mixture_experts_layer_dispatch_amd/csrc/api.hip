@@ -152,6 +152,20 @@ size_t moe_workspace_bytes(const moe_cfg *cfg) {
     return layout_of(cfg).total;
 }
 
+moe_status moe_workspace_region(const moe_cfg *cfg, int32_t region, size_t *offset, size_t *bytes) {
+    MOE_TRY(validate(cfg));
+    if (!offset || !bytes) return MOE_ERR_NULL;
+    const Layout L = layout_of(cfg);
+    const size_t rows = (size_t)cfg->T * cfg->k + (size_t)cfg->n_shared * cfg->T;
+    const bool fp8 = cfg->mode == MOE_MODE_FP8_MXFP4, f32 = cfg->mode == MOE_MODE_F32;
+    switch (region) {
+        case MOE_WS_ERROR: *offset = L.err; *bytes = 256; return MOE_OK;
+        case MOE_WS_H: *offset = L.h; *bytes = rows * cfg->F * (f32 ? 4 : fp8 ? 1 : 2); return MOE_OK;
+        case MOE_WS_H_SCALE: *offset = L.hs; *bytes = fp8 ? rows * (cfg->F / 128) * 4 : 0; return MOE_OK;
+        default: return MOE_ERR_SHAPE;
+    }
+}
+
 moe_status moe_clear_device_error(const moe_cfg *cfg, void *ws, size_t ws_bytes, hipStream_t stream) {
     MOE_TRY(validate(cfg));
     MOE_TRY(check_ws(cfg, ws, ws_bytes));
@@ -172,6 +186,19 @@ moe_status moe_read_device_error(const moe_cfg *cfg, const void *ws, int32_t *co
     if (hipStreamSynchronize(stream) != hipSuccess) return MOE_ERR_LAUNCH;
     *code_out = v;
     return v == 0 ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+moe_status moe_quant_e4m3(const void *in, int32_t in_dtype, int64_t rows, int32_t K, uint8_t *codes, float *scales,
+                          hipStream_t stream) {
+    if (in_dtype != MOE_QUANT_IN_F32 && in_dtype != MOE_QUANT_IN_BF16) return MOE_ERR_MODE;
+    if (rows < 0 || K < 128 || K % 128 || (double)rows * K >= 9.0e18) return MOE_ERR_SHAPE;
+    if (rows == 0) return MOE_OK;
+    if (!in || !codes || !scales) return MOE_ERR_NULL;
+    for (const void *p : {in, (const void *)codes, (const void *)scales})
+        if (!aligned16(p)) return MOE_ERR_ALIGN;
+    MOE_TRY(arch_check());
+    return launched(launch_quant_e4m3(in, in_dtype == MOE_QUANT_IN_F32, (long)(rows * (K / 128)), codes, scales,
+                                      stream));
 }
 
 moe_status moe_route(const moe_cfg *cfg, const void *x, const void *w_router, const float *bias, int32_t *topk_idx,

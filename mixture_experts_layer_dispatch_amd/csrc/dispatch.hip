@@ -90,4 +90,26 @@ hipError_t launch_dispatch(const Shape &s, const int32_t *idx, int32_t *blockcou
     return hipGetLastError();
 }
 
+// Stand-alone FP8 quantiser: rows of fp32 or bf16 values, 1024 lanes per workgroup (64
+// blocks of 128), a grid-stride loop beyond 2^20 workgroups.
+template <bool F32>
+__global__ __launch_bounds__(256) void quant_e4m3_kernel(const void *__restrict__ in, long nblocks,
+                                                        uint8_t *__restrict__ q, float *__restrict__ qs) {
+    const long lanes = nblocks * 16;
+    for (long gid = (long)blockIdx.x * blockDim.x + threadIdx.x; gid - threadIdx.x < lanes;
+         gid += (long)gridDim.x * blockDim.x) {
+        if constexpr (F32) quant_f32_lane((const float *)in, nblocks, q, qs, gid);
+        else quant_x_lane<false>((const uint16_t *)in, nblocks, q, qs, gid);
+    }
+}
+
+hipError_t launch_quant_e4m3(const void *in, bool f32, long nblocks, uint8_t *q, float *qs, hipStream_t st) {
+    if (nblocks == 0) return hipSuccess;
+    const long wg = (nblocks * 16 + 255) / 256;
+    const dim3 grid((unsigned)(wg < (1L << 20) ? wg : (1L << 20)));
+    if (f32) MOE_LAUNCH("quant_e4m3", quant_e4m3_kernel<true>, grid, dim3(256), 0, st, in, nblocks, q, qs);
+    else MOE_LAUNCH("quant_e4m3", quant_e4m3_kernel<false>, grid, dim3(256), 0, st, in, nblocks, q, qs);
+    return hipGetLastError();
+}
+
 }  // namespace moe

@@ -304,4 +304,26 @@ __device__ __forceinline__ void quant_x_lane(const uint16_t *__restrict__ x, lon
     if (sub == 0) stc<COH>(xs + blk, ldexpf(1.0f, e));
 }
 
+// The same quantiser over fp32 values: 16 lanes per 128-value block, 8 values (two 16-byte
+// loads) each.
+__device__ __forceinline__ void quant_f32_lane(const float *__restrict__ v, long nblocks, uint8_t *__restrict__ q,
+                                               float *__restrict__ qs, long gid) {
+    const long blk = gid >> 4;
+    const int sub = (int)(gid & 15);
+    const bool live = blk < nblocks;
+    float4 a = live ? *(const float4 *)(v + blk * 128 + sub * 8) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 b = live ? *(const float4 *)(v + blk * 128 + sub * 8 + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float amax = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                       fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+    amax = row16_max(amax);
+    if (!live) return;
+    const int e = e4m3_block_exponent(amax);
+    const float inv = ldexpf(1.0f, -e);
+    uint2 out;
+    out.x = cvt_e4m3x4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+    out.y = cvt_e4m3x4(b.x * inv, b.y * inv, b.z * inv, b.w * inv);
+    *(uint2 *)(q + blk * 128 + sub * 8) = out;
+    if (sub == 0) qs[blk] = ldexpf(1.0f, e);
+}
+
 }  // namespace moe

@@ -73,6 +73,8 @@ def lib():
         L.oracle_layer.restype = I32
         L.oracle_expert_rows.argtypes = [CP, VP, VP, VP, VP, I32, VP, I64, VP, VP]
         L.oracle_expert_rows.restype = None
+        L.oracle_down_rows.argtypes = [CP, VP, VP, I32, VP, I64, VP]
+        L.oracle_down_rows.restype = None
         L.oracle_keys_from.argtypes = [CP, VP, VP, VP]
         L.oracle_keys_from.restype = None
         L.oracle_input_row.argtypes = [CP, VP, I64, VP]
@@ -204,6 +206,18 @@ def expert_rows(inp: dict, g: int, xin: np.ndarray, want_h: bool = False):
     lib().oracle_expert_rows(ctypes.byref(c), _p(inp["w1"]), _p(inp["w1_scale"]), _p(inp["w2"]),
                              _p(inp["w2_scale"]), int(g), _p(xin), n, _p(out), _p(h))
     return (out, h) if want_h else out
+
+
+def down_rows(inp: dict, g: int, hhat: np.ndarray) -> np.ndarray:
+    """linear2 of expert g on given fp64 rows hhat [n, F] (in FP8 mode: dequantised e4m3 h)
+    -> [n, d]."""
+    w = inp["workload"]
+    c = _cfg(w)
+    hhat = np.ascontiguousarray(hhat, dtype=np.float64)
+    n = hhat.shape[0]
+    out = np.empty((n, w.d), dtype=np.float64)
+    lib().oracle_down_rows(ctypes.byref(c), _p(inp["w2"]), _p(inp["w2_scale"]), int(g), _p(hhat), n, _p(out))
+    return out
 
 
 def layer(inp: dict, tokens=None, idx=None, gates=None, nthreads: int = 0):

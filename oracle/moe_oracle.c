@@ -478,3 +478,20 @@ void oracle_expert_rows(const oracle_cfg *c, const void *w1, const void *w1s, co
 void oracle_keys_from(const oracle_cfg *c, const float *logits, const float *bias, float *keys) {
     for (int64_t t = 0; t < c->T; ++t) oracle_keys_token(c, logits + t * c->E, bias, keys + t * c->E);
 }
+
+/*
+ * linear2 alone: out[r][c] = sum_f hhat[r][f] W2[g][c][f] for given rows hhat [nrows, F]
+ * (fp64; in FP8 mode the dequantised e4m3 h rows, code * scale). It lets a caller project
+ * the very h codes another implementation produced, as the MXFP4 weights are dequantised
+ * exactly and the sum is taken in fp64 in f order.
+ */
+void oracle_down_rows(const oracle_cfg *c, const void *w2, const void *w2s, int g, const double *hhat,
+                      int64_t nrows, double *out) {
+    int64_t d = c->d, F = c->F;
+    for (int64_t r = 0; r < nrows; ++r)
+        for (int64_t o = 0; o < d; ++o) {
+            double s = 0.0;
+            for (int64_t f = 0; f < F; ++f) s += hhat[r * F + f] * weight(c, w2, w2s, g, d, F, o, f);
+            out[r * d + o] = s;
+        }
+}

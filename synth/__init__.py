@@ -11,7 +11,8 @@ Workloads (sizes from the pages' model shapes and per-rank batch sizes):
 * ``dsv3_bf16``      T=8192, d=7168, E=256, k=8, F=2048, 1 shared, sigmoid + Zipf bias, bf16
 * ``dsv3_fp8fp4``    d=7168, E=256, k=8, F=2048, 1 shared, softmax, FP8 e4m3 x MXFP4,
                      T in {512, 8192, 32768}
-* ``decode_fp8fp4``  as above, T in {1, 64}
+* ``decode_fp8fp4``  the same layer and tensors (same seed), T in {1, 64}
+* ``dsv3_fp8fp4_zipf`` the same layer and tensors with sigmoid scores and the Zipf bias
 """
 from __future__ import annotations
 
@@ -170,8 +171,12 @@ WORKLOADS = {
                           zipf_alpha=0.25),
     "dsv3_fp8fp4": Workload("dsv3_fp8fp4", 1004, MODE_FP8, 8192, 7168, 256, 8, 2048, 1, "softmax",
                             t_values=(512, 8192, 32768)),
-    "decode_fp8fp4": Workload("decode_fp8fp4", 1005, MODE_FP8, 1, 7168, 256, 8, 2048, 1, "softmax",
+    # the same layer (same seed, so the same tensors) at decode batch sizes
+    "decode_fp8fp4": Workload("decode_fp8fp4", 1004, MODE_FP8, 1, 7168, 256, 8, 2048, 1, "softmax",
                               t_values=(1, 64)),
+    # the same layer with the DeepSeek-V3-shaped router: sigmoid scores and Zipf-skewed bias
+    "dsv3_fp8fp4_zipf": Workload("dsv3_fp8fp4_zipf", 1004, MODE_FP8, 8192, 7168, 256, 8, 2048, 1, "sigmoid",
+                                 zipf_alpha=0.25, t_values=(8192,)),
 }
 
 

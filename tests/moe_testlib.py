@@ -137,4 +137,186 @@ def check_outputs(w: Workload, inp: dict, y, idx, gate, tokens, tol=None, nthrea
     err = rel_l2(y_gpu, y_ref)
     assert np.all(np.isfinite(y_gpu)), "non-finite GPU output"
     assert err <= tol, f"output rel L2 {err:.3e} > {tol:.1e}"
+    if w.mode != "fp8_mxfp4":
+        # every token on its own as well (a token's output depends only on its row and the
+        # weights); in FP8 mode a token's h codes may sit one step apart at a rounding midpoint,
+        # which moves a single token by up to about 1e-2 at small F, so there the per-token check
+        # takes the GPU's own h codes (check_tokens_fp8)
+        assert_per_row(y_gpu, y_ref, tol, tokens, "token")
     return err
+
+
+def assert_per_row(got, ref, tol, ids, what):
+    per = np.linalg.norm(got - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+    nz = np.linalg.norm(ref, axis=1) > 0
+    if not nz.any():
+        return 0.0
+    worst = int(np.argmax(np.where(nz, per, 0.0)))
+    assert per[worst] <= tol, f"{what} {ids[worst]}: rel L2 {per[worst]:.3e} > {tol:.1e}"
+    return float(per[worst])
+
+
+# ---- per-row checks: the expert output (y_perm) and FP8 h of chosen dispatched rows -------
+
+def row_tokens(w: Workload, r2s: np.ndarray, rows: np.ndarray) -> np.ndarray:
+    """Token feeding each dispatched row: routed rows carry slot t*k + j, shared rows are T*k + t."""
+    tk = w.T * w.k
+    rows = np.asarray(rows, dtype=np.int64)
+    return np.where(rows < tk, r2s[np.minimum(rows, tk - 1)] // w.k, rows - tk)
+
+
+def row_groups(offsets: np.ndarray, rows: np.ndarray) -> np.ndarray:
+    return np.searchsorted(offsets, np.asarray(rows, dtype=np.int64), side="right") - 1
+
+
+def cover_rows(offsets: np.ndarray, block: int = 128, seed: int = 0) -> np.ndarray:
+    """One seeded row in every block of `block` rows of every group (blocks start at the
+    group's first row, as the GEMM row tiles and their 128-row halves do)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for g in range(offsets.size - 1):
+        a, b = int(offsets[g]), int(offsets[g + 1])
+        for s in range(a, b, block):
+            out.append(int(rng.integers(s, min(s + block, b))))
+    return np.array(out, dtype=np.int64)
+
+
+def oracle_rows(inp: dict, groups: np.ndarray, tokens: np.ndarray, want_h: bool = False, threads: int = 16):
+    """Oracle expert outputs (and h before FP8 rounding) of the rows (group, token), computed
+    by `threads` concurrent calls into the C oracle."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    w = inp["workload"]
+    n = len(groups)
+    out = np.empty((n, w.d), dtype=np.float64)
+    h = np.empty((n, w.F), dtype=np.float64) if want_h else None
+
+    def job(i):
+        xin = oracle.input_rows(inp, [int(tokens[i])])
+        r = oracle.expert_rows(inp, int(groups[i]), xin, want_h=want_h)
+        if want_h:
+            out[i], h[i] = r[0][0], r[1][0]
+        else:
+            out[i] = r[0]
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(job, range(n)))
+    return out, h
+
+
+def check_rows(w: Workload, inp: dict, dsp: dict, y_perm, rows: np.ndarray, ws=None, cfg=None, tol=None):
+    """The GPU's expert output rows (y_perm) against the oracle, row by row (rel L2 each, and
+    over all of them); in FP8 mode also the GPU's h codes and scales of those rows against
+    the oracle's rule applied to the oracle's h (fp32): scales equal wherever the block
+    maximum is clear of a power-of-two boundary, and codes equal except single steps at a
+    rounding midpoint.  Returns (aggregate rel L2, worst row rel L2, code mismatches)."""
+    import e4m3_ref
+
+    tol = TOL[w.mode] if tol is None else tol
+    offs = dsp["offsets"].cpu().numpy()
+    r2s = dsp["row_to_slot"].cpu().numpy()
+    groups = row_groups(offs, rows)
+    toks = row_tokens(w, r2s, rows)
+    fp8 = w.mode == "fp8_mxfp4"
+    ref, h = oracle_rows(inp, groups, toks, want_h=fp8)
+    got = to_f64(y_perm[torch.from_numpy(rows).to(y_perm.device)])
+    assert np.all(np.isfinite(got)), "non-finite expert output"
+    if fp8:
+        # linear2 of the GPU's own h codes (the oracle dequantising the identical codes)
+        ref = down_of_gpu_h(w, inp, ws, cfg, rows, groups)
+    worst = assert_per_row(got, ref, tol, rows, "row")
+    agg = rel_l2(got, ref)
+    assert agg <= tol
+    mism = 0
+    if fp8:
+        nrows = w.T * (w.k + w.S)
+        codes_all = moe.workspace_region(cfg, ws, "h").view(nrows, w.F)
+        scales_all = moe.workspace_region(cfg, ws, "h_scale").view(torch.float32).view(nrows, w.F // 128)
+        idx = torch.from_numpy(rows).to(codes_all.device)
+        g_codes = codes_all[idx].cpu().numpy()
+        g_scales = scales_all[idx].cpu().numpy()
+        hf = h.astype(np.float32)
+        o_codes, o_scales = oracle.quant_e4m3_b128(hf)
+        amax = np.abs(hf).reshape(len(rows), -1, 128).max(axis=2).astype(np.float64)
+        # a block whose maximum lies within 1e-4 of a power-of-two scale boundary may take
+        # either exponent when h is computed in another summation order
+        lo = np.array([[oracle.e4m3_block_exponent(float(a * (1 - 1e-4))) for a in r] for r in amax])
+        hi = np.array([[oracle.e4m3_block_exponent(float(a * (1 + 1e-4))) for a in r] for r in amax])
+        clear = lo == hi
+        assert np.array_equal(g_scales[clear], o_scales[clear]), "h block scales differ"
+        same_scale = (g_scales == o_scales)
+        cmp = np.repeat(same_scale, 128, axis=1)
+        diff = (g_codes != o_codes) & cmp
+        mism = int(diff.sum())
+        if mism:
+            gi, gj = np.nonzero(diff)
+            gc, oc = g_codes[gi, gj], o_codes[gi, gj]
+            v = hf[gi, gj].astype(np.float64) / o_scales[gi, gj // 128]  # the oracle's h, scaled
+            # The GPU's h is an fp32 sum in another order (and, on the MFMA, another internal
+            # rounding): its error scales with the block's terms rather than with the element, so
+            # it is bounded relative to the block maximum (448 in scaled units), at 1e-4 of it.
+            # The GPU's code must be a round-to-nearest-even of some value within that distance
+            # of the oracle's h: between the codes of v - delta and v + delta.
+            delta = 448.0 * 1e-4
+            lo = e4m3_ref.decode_codes(e4m3_ref.encode_bits((v - delta).astype(np.float32).view(np.uint32)))
+            hi = e4m3_ref.decode_codes(e4m3_ref.encode_bits((v + delta).astype(np.float32).view(np.uint32)))
+            gv = e4m3_ref.decode_codes(gc)
+            ok = (gv >= lo) & (gv <= hi)
+            bad = np.nonzero(~ok)[0][:5]
+            assert ok.all(), ("h code is no rounding of a value near the oracle's h: " +
+                              "; ".join(f"row {rows[gi[b]]} col {gj[b]}: scaled oracle h {v[b]:.6g}, gpu code "
+                                        f"{gv[b]:.6g}, oracle code {e4m3_ref.decode_codes(oc[b:b + 1])[0]:.6g}"
+                                        for b in bad))
+            assert mism <= 1e-2 * cmp.sum(), f"{mism} of {int(cmp.sum())} h codes differ"
+    return agg, worst, mism
+
+
+def gpu_hhat(w: Workload, ws, cfg, rows: np.ndarray) -> np.ndarray:
+    """The GPU's FP8 h of dispatched rows, dequantised with the oracle's e4m3 decoder: code x scale."""
+    import e4m3_ref
+
+    nrows = w.T * (w.k + w.S)
+    codes = moe.workspace_region(cfg, ws, "h").view(nrows, w.F)
+    scales = moe.workspace_region(cfg, ws, "h_scale").view(torch.float32).view(nrows, w.F // 128)
+    idx = torch.from_numpy(np.asarray(rows, dtype=np.int64)).to(codes.device)
+    c = codes[idx].cpu().numpy()
+    sc = scales[idx].cpu().numpy().astype(np.float64)
+    return e4m3_ref.decode_codes(c) * np.repeat(sc, 128, axis=1)
+
+
+def down_of_gpu_h(w: Workload, inp: dict, ws, cfg, rows: np.ndarray, groups: np.ndarray, threads: int = 16):
+    from concurrent.futures import ThreadPoolExecutor
+
+    hh = gpu_hhat(w, ws, cfg, rows)
+    out = np.empty((len(rows), w.d), dtype=np.float64)
+
+    def job(i):
+        out[i] = oracle.down_rows(inp, int(groups[i]), hh[i:i + 1])[0]
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(job, range(len(rows))))
+    return out
+
+
+def check_tokens_fp8(w: Workload, inp: dict, y, dsp: dict, gate, ws, cfg, tokens, tol=None):
+    """FP8 mode, token by token: the GPU's y against the gate-weighted sum, in the layer's
+    fixed order, of the oracle's linear2 of the GPU's own h codes of the token's rows."""
+    tol = TOL[w.mode] if tol is None else tol
+    tokens = np.asarray(tokens, dtype=np.int64)
+    s2r = dsp["slot_to_row"].cpu().numpy()
+    offs = dsp["offsets"].cpu().numpy()
+    g_np = gate.cpu().numpy().astype(np.float64)
+    rows = [s2r[t * w.k + j] for t in tokens for j in range(w.k)]
+    if w.S:
+        rows += [w.T * w.k + t for t in tokens]
+    rows = np.array(rows, dtype=np.int64)
+    o = down_of_gpu_h(w, inp, ws, cfg, rows, row_groups(offs, rows))
+    n = len(tokens)
+    ref = np.zeros((n, w.d))
+    for i in range(n):
+        for j in range(w.k):
+            ref[i] += g_np[tokens[i], j] * o[i * w.k + j]
+        if w.S:
+            ref[i] += o[n * w.k + i]
+    got = to_f64(y)[tokens]
+    return assert_per_row(got, ref, tol, tokens, "token")

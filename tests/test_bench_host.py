@@ -38,25 +38,41 @@ def test_kernel_work_adds_up_to_the_layer(name):
     assert bench.kernel_work(w, "linear1", none)[1] < b1
 
 
-def _fake_tree(tmp_path, body: bytes):
+def _fake_tree(tmp_path, files):
     csrc = tmp_path / "mixture_experts_layer_dispatch_amd" / "csrc"
     csrc.mkdir(parents=True)
-    (csrc / "k.hip").write_bytes(body)
+    for name, body in files.items():
+        (csrc / name).write_bytes(body)
     (tmp_path / "profiles").mkdir()
     return csrc
 
 
 def test_traffic_only_for_the_measured_sources(tmp_path, monkeypatch):
-    csrc = _fake_tree(tmp_path, b"kernel v1")
+    csrc = _fake_tree(tmp_path, {"ffn.hip": b"launchers v1", "gemm_bf16_dev.hpp": b"tile v1",
+                                 "common.hpp": b"helpers", "dispatch_dev.hpp": b"dispatch", "route.hip": b"r1"})
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     w = WORKLOADS["mixtral_bf16"]
-    h = bench.sources_hash()
+    h = bench.sources_hash("linear1", "bf16")
     (tmp_path / "profiles" / "traffic.txt").write_text(
         "# header\n"
         f"workload={w.name} T={w.T} kernel=linear1 fetch_kib=100.0 write_kib=10.0 fetch_scale=2.0 "
         f"write_scale=1.0 dispatches=8 sources={h}\n")
     assert bench.traffic_of(w, "linear1") == (100.0 * 2.0 + 10.0) * 1024.0
     assert bench.traffic_of(w, "linear2") is None  # not measured
-    (csrc / "k.hip").write_bytes(b"kernel v2")  # a kernel changed since the counters
-    assert bench.sources_hash() != h
+    (csrc / "route.hip").write_bytes(b"r2")  # a file the GEMM is not built from
+    assert bench.traffic_of(w, "linear1") == (100.0 * 2.0 + 10.0) * 1024.0
+    (csrc / "gemm_bf16_dev.hpp").write_bytes(b"tile v2")  # the GEMM changed since the counters
+    assert bench.sources_hash("linear1", "bf16") != h
     assert bench.traffic_of(w, "linear1") is None
+
+
+def test_load_statistics():
+    w = WORKLOADS["dsv3_fp8fp4"].with_T(64)
+    even = np.full(w.G, 2, dtype=np.int64)
+    st = bench.load_stats(w, even)
+    assert st["max_over_mean"] == 1.0 and st["gini"] == 0.0 and st["experts_touched"] == w.E
+    one = np.zeros(w.G, dtype=np.int64)
+    one[5] = 512
+    st = bench.load_stats(w, one)
+    # all load on one of E experts: max / mean = E, Gini = 1 - 1/E
+    assert st["max_over_mean"] == w.E and abs(st["gini"] - (1 - 1 / w.E)) < 1e-12

@@ -15,8 +15,8 @@ import mixture_experts_layer_dispatch_amd as moe
 import oracle
 import synth
 from synth import WORKLOADS, Workload
-from moe_testlib import (TOL, cfg_of, check_dispatch, check_outputs, check_routing, check_xq, log, rel_l2,
-                         sample_tokens, to_dev, to_f64, upload)
+from moe_testlib import (TOL, cfg_of, check_dispatch, check_outputs, check_routing, check_rows, check_tokens_fp8,
+                         check_xq, cover_rows, log, rel_l2, sample_tokens, to_dev, to_f64, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -88,6 +88,10 @@ def test_small_layer_parity(name):
     if w.mode == "fp8_mxfp4":
         check_xq(w, inp, r["dsp"]["xq"], r["dsp"]["xq_scale"])
     err = check_outputs(w, inp, r["y"], r["idx"], r["gate"], np.arange(w.T))
+    # every expert output row, and in FP8 mode every row's h codes and scales
+    check_rows(w, inp, r["dsp"], r["y_perm"], np.arange(w.T * (w.k + w.S)), ws=ws, cfg=cfg)
+    if w.mode == "fp8_mxfp4":
+        check_tokens_fp8(w, inp, r["y"], r["dsp"], r["gate"], ws, cfg, np.arange(w.T))
     # the fused entry point gives the same bits
     y2, idx2, gate2, counts2 = run_fused(w, d, cfg, ws)
     assert torch.equal(idx2, r["idx"]) and torch.equal(gate2, r["gate"])
@@ -241,6 +245,14 @@ def test_full_size_parity(name, T):
         check_xq(w, inp, r["dsp"]["xq"], r["dsp"]["xq_scale"], tokens=toks)
     log(f"oracle on {len(toks)} sampled tokens")
     err = check_outputs(w, inp, r["y"], r["idx"], r["gate"], toks)
+    # one row in every 128-row block of every group: every (group, row tile) of the GEMMs
+    # and both halves of any tile the tail split runs as two
+    rows = cover_rows(r["dsp"]["offsets"].cpu().numpy(), 128 if T > 64 else 32, seed=T)
+    log(f"oracle on {rows.size} rows covering every 128-row block of every group")
+    agg, worst, mism = check_rows(w, inp, r["dsp"], r["y_perm"], rows, ws=ws, cfg=cfg)
+    log(f"rows: rel L2 {agg:.2e}, worst row {worst:.2e}, h code mismatches {mism}")
+    if w.mode == "fp8_mxfp4":
+        check_tokens_fp8(w, inp, r["y"], r["dsp"], r["gate"], ws, cfg, toks)
     y2, idx2, _, _ = run_fused(w, d, cfg, ws)
     assert torch.equal(idx2, r["idx"])
     assert torch.equal(y2.view(torch.int16), r["y"].view(torch.int16)), "fused != unfused"

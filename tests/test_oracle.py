@@ -456,3 +456,57 @@ def test_golden_routing_examples():
         r = oracle.route(_route_inputs(w, logits, bias))
         assert list(r["idx"][0]) == case["idx"], case["name"]
         np.testing.assert_allclose(r["gates"][0], case["gates"], rtol=2e-7, err_msg=case["name"])
+
+
+def test_vectorised_e4m3_reference_matches_the_oracle_encoder():
+    """tests/e4m3_ref.py (used for the exhaustive GPU conversion check) equals the oracle's
+    per-value encoder on every code value, every midpoint, their fp32 neighbours, values
+    past the saturation point and a seeded sample of fp32 patterns."""
+    import e4m3_ref
+
+    vals = np.array([oracle.e4m3_decode(c) for c in range(0x7F)], dtype=np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2.0
+    pts = np.concatenate([vals, mids, [448.0, 449.0, 464.0, 480.0, 1e4, 3e38, 1e-30, 1e-45]]).astype(np.float32)
+    bits = pts.view(np.uint32)
+    nb = np.concatenate([bits, bits + 1, bits - 1, np.array([0, 1], dtype=np.uint32)])
+    nb = nb[(nb & 0x7F800000) != 0x7F800000]
+    rng = np.random.default_rng(5)
+    sample = rng.integers(0, 0x43E00001, size=20000, dtype=np.uint32)
+    allbits = np.concatenate([nb, sample, sample | 0x80000000, nb | 0x80000000])
+    got = e4m3_ref.encode_bits(allbits)
+    want = np.array([oracle.e4m3_encode(float(v)) for v in allbits.view(np.float32)], dtype=np.uint8)
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("mode", ["fp8_mxfp4", "bf16"])
+def test_down_rows_is_linear2(mode):
+    """oracle.down_rows: torch fp64 matmul on independently dequantised W2 (FP8 x MXFP4: the
+    OCP e2m1 table times 2^(e8m0 - 127)); integer rows and integer weights give exact sums."""
+    w = Workload("down", 41, mode, 4, 256, 3, 1, 256, 1, "softmax")
+    inp = synth.make_inputs(w)
+    rng = np.random.default_rng(3)
+    hhat = rng.standard_normal((5, w.F))
+    if mode == "fp8_mxfp4":
+        lut = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0., -.5, -1, -1.5, -2, -3, -4, -6])
+        codes, scales = inp["w2"][2], inp["w2_scale"][2]
+        nib = np.stack([codes & 15, codes >> 4], -1).reshape(codes.shape[0], -1)
+        W2 = lut[nib] * np.exp2(np.repeat(scales.astype(np.int64) - 127, 32, axis=-1))
+    else:
+        W2 = _as_f64(inp["w2"][2], "bf16")
+    got = oracle.down_rows(inp, 2, hhat)
+    np.testing.assert_allclose(got, (torch.from_numpy(hhat) @ torch.from_numpy(W2).T).numpy(), rtol=1e-11,
+                               atol=1e-12)
+    g = synth.make_inputs(w, grid=True)
+    hi = rng.integers(-3, 4, size=(3, w.F)).astype(np.float64)
+    W2g = _as_f64(g["w2"][1], "bf16") if mode == "bf16" else None
+    if mode == "bf16":
+        np.testing.assert_array_equal(oracle.down_rows(g, 1, hi), hi @ W2g.T)
+    # the expert on an input row equals linear2 of its quantised h (FP8) or of h
+    xin = oracle.input_rows(inp, [1])
+    out, h = oracle.expert_rows(inp, 0, xin, want_h=True)
+    if mode == "fp8_mxfp4":
+        c, s = oracle.quant_e4m3_b128(h.astype(np.float32))
+        hq = np.array([oracle.e4m3_decode(int(v)) for v in c.reshape(-1)]).reshape(c.shape) * np.repeat(s, 128, 1)
+    else:
+        hq = h
+    np.testing.assert_array_equal(oracle.down_rows(inp, 0, hq), out)
