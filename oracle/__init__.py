@@ -75,6 +75,12 @@ def lib():
         L.oracle_expert_rows.restype = None
         L.oracle_down_rows.argtypes = [CP, VP, VP, I32, VP, I64, VP]
         L.oracle_down_rows.restype = None
+        L.oracle_layer_dropping.argtypes = [CP, VP, VP, VP, VP, VP, VP, VP, VP, VP, I64, VP, I32]
+        L.oracle_layer_dropping.restype = I32
+        L.oracle_dispatch_capacity.argtypes = [CP, VP, I32, VP, VP, VP, VP, VP]
+        L.oracle_dispatch_capacity.restype = I32
+        L.oracle_bias_update.argtypes = [I32, VP, VP, ctypes.c_float]
+        L.oracle_bias_update.restype = None
         L.oracle_keys_from.argtypes = [CP, VP, VP, VP]
         L.oracle_keys_from.restype = None
         L.oracle_input_row.argtypes = [CP, VP, I64, VP]
@@ -183,6 +189,32 @@ def dispatch(w, idx: np.ndarray):
     return {"counts": counts, "offsets": offsets, "slot_to_row": s2r, "row_to_slot": r2s}
 
 
+def dispatch_capacity(w, idx: np.ndarray, capacity: int):
+    """The capacity variant of S5-S6: at most `capacity` slots per routed expert, the first
+    ones in slot order kept -> dict(counts [G] (kept), dropped [E], offsets [G+1],
+    slot_to_row [T*k] (-1 when dropped), row_to_slot [T*k])."""
+    T = idx.shape[0]
+    c = _cfg(w, T)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    G = w.E + w.S
+    counts = np.empty(G, dtype=np.int32)
+    dropped = np.empty(w.E, dtype=np.int32)
+    offsets = np.empty(G + 1, dtype=np.int32)
+    s2r = np.empty(T * w.k, dtype=np.int32)
+    r2s = np.empty(T * w.k, dtype=np.int32)
+    _check(lib().oracle_dispatch_capacity(ctypes.byref(c), _p(idx), int(capacity), _p(counts), _p(dropped),
+                                          _p(offsets), _p(s2r), _p(r2s)))
+    return {"counts": counts, "dropped": dropped, "offsets": offsets, "slot_to_row": s2r, "row_to_slot": r2s}
+
+
+def bias_update(counts: np.ndarray, bias: np.ndarray, gamma: float) -> np.ndarray:
+    """One aux-loss-free bias update from routed per-expert counts [E] -> new bias [E] (fp32)."""
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    out = np.ascontiguousarray(bias, dtype=np.float32).copy()
+    lib().oracle_bias_update(counts.size, _p(counts), _p(out), float(gamma))
+    return out
+
+
 # ---- experts and the layer -------------------------------------------------------
 
 def input_rows(inp: dict, tokens) -> np.ndarray:
@@ -218,6 +250,24 @@ def down_rows(inp: dict, g: int, hhat: np.ndarray) -> np.ndarray:
     out = np.empty((n, w.d), dtype=np.float64)
     lib().oracle_down_rows(ctypes.byref(c), _p(inp["w2"]), _p(inp["w2_scale"]), int(g), _p(hhat), n, _p(out))
     return out
+
+
+def layer_dropping(inp: dict, idx, gates, keep, tokens=None, nthreads: int = 0):
+    """y [ntok, d] fp64 under the capacity variant: the given routing, minus the dropped slots
+    (keep [T, k] false); their gates are not renormalised."""
+    w = inp["workload"]
+    T = inp["x"].shape[0]
+    c = _cfg(w, T)
+    tokens = np.arange(T, dtype=np.int64) if tokens is None else np.ascontiguousarray(tokens, dtype=np.int64)
+    n = tokens.shape[0]
+    y = np.empty((n, w.d), dtype=np.float64)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    gates = np.ascontiguousarray(gates, dtype=np.float32)
+    keep = np.ascontiguousarray(keep, dtype=np.uint8)
+    _check(lib().oracle_layer_dropping(ctypes.byref(c), _p(inp["x"]), _p(inp["w1"]), _p(inp["w1_scale"]),
+                                       _p(inp["w2"]), _p(inp["w2_scale"]), _p(idx), _p(gates), _p(keep),
+                                       _p(tokens), n, _p(y), nthreads))
+    return y
 
 
 def layer(inp: dict, tokens=None, idx=None, gates=None, nthreads: int = 0):

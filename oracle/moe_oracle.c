@@ -403,6 +403,7 @@ typedef struct {
     int32_t *idx_out;
     float *gates_out;
     int status;
+    const uint8_t *keep; /* [T*k] or NULL: a slot with keep 0 was dropped (capacity variant) */
 } layer_ctx;
 
 static void layer_range(void *p, int64_t a, int64_t b) {
@@ -435,6 +436,7 @@ static void layer_range(void *p, int64_t a, int64_t b) {
         for (int64_t i = 0; i < d; ++i) y[i] = 0.0;
         /* fixed order: routed experts j = 0..k-1 in selection order, then the shared expert */
         for (int j = 0; j < k; ++j) {
+            if (L->keep && !L->keep[t * k + j]) continue; /* a dropped slot skips the layer */
             oracle_expert_row(c, &L->w, idx[j], xin, o, NULL);
             for (int64_t i = 0; i < d; ++i) y[i] += (double)g[j] * o[i];
         }
@@ -461,9 +463,108 @@ int oracle_layer(const oracle_cfg *c, const void *x, const void *wr, const float
                  float *gates_out, int nthreads) {
     if (c->k < 1 || c->k > c->E || c->k > 64) return ORC_SHAPE;
     if (c->mode == ORC_FP8_MXFP4 && (c->d % 128 || c->F % 128)) return ORC_SHAPE;
-    layer_ctx L = {c, x, wr, bias, {w1, w1s, w2, w2s}, idx_in, gates_in, tokens, y, idx_out, gates_out, ORC_OK};
+    layer_ctx L = {c, x, wr, bias, {w1, w1s, w2, w2s}, idx_in, gates_in, tokens, y, idx_out, gates_out, ORC_OK, NULL};
     run_split(layer_range, &L, ntok, nthreads);
     return L.status;
+}
+
+/*
+ * The layer under the capacity variant: as oracle_layer with the given routing
+ * (idx_in, gates_in [T,k]), except that a slot whose keep[t*k + j] is 0 was dropped
+ * and contributes nothing -- its token skips that expert (MoE lesson, "The
+ * load-balancing problem", item 2: tokens over an expert's capacity skip the layer).
+ * The remaining gates are not renormalised; the shared expert always applies.
+ */
+int oracle_layer_dropping(const oracle_cfg *c, const void *x, const void *w1, const void *w1s, const void *w2,
+                          const void *w2s, const int32_t *idx_in, const float *gates_in, const uint8_t *keep,
+                          const int64_t *tokens, int64_t ntok, double *y, int nthreads) {
+    if (c->k < 1 || c->k > c->E || c->k > 64 || !idx_in || !gates_in || !keep) return ORC_SHAPE;
+    if (c->mode == ORC_FP8_MXFP4 && (c->d % 128 || c->F % 128)) return ORC_SHAPE;
+    layer_ctx L = {c, x, NULL, NULL, {w1, w1s, w2, w2s}, idx_in, gates_in, tokens, y, NULL, NULL, ORC_OK, keep};
+    run_split(layer_range, &L, ntok, nthreads);
+    return L.status;
+}
+
+/* ---- the capacity variant of the dispatch ----------------------------------------- */
+
+/*
+ * Expert capacity with token dropping (MoE lesson, "The load-balancing problem",
+ * item 2): each routed expert takes at most `capacity` of the slots that chose it;
+ * the others are dropped.  Which ones: the slots of one expert in slot order (that is,
+ * ascending token order, the order of the dropless dispatch); the first `capacity` are
+ * kept.  The shared expert has no capacity.
+ *
+ * Outputs, with kept_e = min(n_e, capacity), dropped_e = n_e - kept_e and
+ * D = sum of dropped_e:
+ *  counts[e] = kept_e (counts[E] = T when S = 1); dropped[e] = dropped_e;
+ *  offsets[0] = D, offsets[e + 1] = offsets[e] + kept_e, so offsets[E] = T*k and the
+ *  shared group keeps rows T*k + t;
+ *  rows 0 .. D-1 list the dropped slots, expert by expert, in slot order;
+ *  slot_to_row[s] = the kept row of slot s, or -1 when s was dropped;
+ *  row_to_slot[r] = the slot of row r (kept and dropped rows alike).
+ */
+int oracle_dispatch_capacity(const oracle_cfg *c, const int32_t *idx, int32_t capacity, int32_t *counts,
+                             int32_t *dropped, int32_t *offsets, int32_t *slot_to_row, int32_t *row_to_slot) {
+    int64_t T = c->T;
+    int k = c->k, E = c->E, G = c->E + c->S;
+    if (capacity < 0) return ORC_SHAPE;
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int32_t e = idx[t * k + j];
+            if (e < 0 || e >= E) return ORC_BAD_INDEX;
+            for (int jj = 0; jj < j; ++jj) if (idx[t * k + jj] == e) return ORC_DUP_INDEX;
+        }
+    int32_t *n = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    int32_t *drop_base = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    int32_t *seen = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    for (int64_t s = 0; s < T * k; ++s) n[idx[s]]++;
+    int32_t D = 0;
+    for (int e = 0; e < E; ++e) {
+        counts[e] = n[e] < capacity ? n[e] : capacity;
+        dropped[e] = n[e] - counts[e];
+        drop_base[e] = D;
+        D += dropped[e];
+    }
+    if (c->S) counts[E] = (int32_t)T;
+    offsets[0] = D;
+    for (int g = 0; g < G; ++g) offsets[g + 1] = offsets[g] + counts[g];
+    for (int64_t s = 0; s < T * k; ++s) {
+        int32_t e = idx[s];
+        int32_t rank = seen[e]++;  /* position of slot s among expert e's slots, in slot order */
+        int32_t row;
+        if (rank < capacity) {
+            row = offsets[e] + rank;
+            slot_to_row[s] = row;
+        } else {
+            row = drop_base[e] + (rank - capacity);
+            slot_to_row[s] = -1;
+        }
+        row_to_slot[row] = (int32_t)s;
+    }
+    free(n);
+    free(drop_base);
+    free(seen);
+    return ORC_OK;
+}
+
+/* ---- aux-loss-free load balancing ------------------------------------------------ */
+
+/*
+ * One update of the per-expert selection bias (MoE lesson, "The load-balancing
+ * problem", the DeepSeek-V3 scheme, and "Build it -- Step 2: route 100 tokens"):
+ * after a step, an expert used more than its target gets -gamma, one used less gets
+ * +gamma.  The target is the mean load over the E routed experts, sum(counts) / E; an
+ * expert exactly on target keeps its bias (compared exactly, as counts[e] * E against
+ * the total).  The addition is an fp32 add, as the bias is fp32.
+ */
+void oracle_bias_update(int32_t E, const int32_t *counts, float *bias, float gamma) {
+    int64_t total = 0;
+    for (int e = 0; e < E; ++e) total += counts[e];
+    for (int e = 0; e < E; ++e) {
+        int64_t scaled = (int64_t)counts[e] * E;
+        if (scaled > total) bias[e] = bias[e] - gamma;
+        else if (scaled < total) bias[e] = bias[e] + gamma;
+    }
 }
 
 /* One expert applied to given input rows (already in the mode's input precision). */

@@ -510,3 +510,101 @@ def test_down_rows_is_linear2(mode):
     else:
         hq = h
     np.testing.assert_array_equal(oracle.down_rows(inp, 0, hq), out)
+
+
+# ---------------------------------------------------------------- capacity variant and bias update
+
+def _brute_capacity(idx, E, S, capacity):
+    """Per expert, its slots in slot order; the first `capacity` kept."""
+    T, k = idx.shape
+    slots = {e: [s for s in range(T * k) if idx.reshape(-1)[s] == e] for e in range(E)}
+    kept = {e: v[:capacity] for e, v in slots.items()}
+    drop = {e: v[capacity:] for e, v in slots.items()}
+    return kept, drop
+
+
+@pytest.mark.parametrize("T,E,k,S,cap", [(40, 8, 2, 1, 7), (33, 6, 3, 0, 10), (50, 16, 4, 1, 0), (21, 5, 5, 1, 4),
+                                         (64, 8, 2, 0, 1000)])
+def test_capacity_dispatch_brute_force(T, E, k, S, cap):
+    w = _tiny(E, k, T=T, S=S)
+    rng = np.random.default_rng(T * 7 + E)
+    p = rng.dirichlet(np.full(E, 0.4))
+    idx = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    r = oracle.dispatch_capacity(w, idx, cap)
+    kept, drop = _brute_capacity(idx, E, S, cap)
+    nk = np.array([len(kept[e]) for e in range(E)])
+    nd = np.array([len(drop[e]) for e in range(E)])
+    np.testing.assert_array_equal(r["counts"][:E], nk)
+    np.testing.assert_array_equal(r["dropped"], nd)
+    assert np.all(nk <= cap) and nk.sum() + nd.sum() == T * k
+    D = nd.sum()
+    assert r["offsets"][0] == D and r["offsets"][E] == T * k
+    np.testing.assert_array_equal(np.diff(r["offsets"][: E + 1]), nk)
+    if S:
+        assert r["counts"][E] == T and r["offsets"][E + 1] == T * k + T
+    # kept rows: expert by expert, in slot order; dropped rows 0..D-1 likewise
+    exp_r2s = [s for e in range(E) for s in drop[e]] + [s for e in range(E) for s in kept[e]]
+    np.testing.assert_array_equal(r["row_to_slot"], np.array(exp_r2s, dtype=np.int32))
+    s2r = np.full(T * k, -1, dtype=np.int32)
+    for row, s in enumerate(exp_r2s):
+        if row >= D:
+            s2r[s] = row
+    np.testing.assert_array_equal(r["slot_to_row"], s2r)
+    assert sorted(r["row_to_slot"].tolist()) == list(range(T * k))
+    if cap >= max(np.bincount(idx.reshape(-1), minlength=E)):
+        d = oracle.dispatch(w, idx)  # nothing dropped: the dropless dispatch
+        for key in ("counts", "offsets", "slot_to_row", "row_to_slot"):
+            np.testing.assert_array_equal(r[key], d[key])
+
+
+def test_dropping_layer_closed_forms():
+    """Keeping every slot is the layer; dropping a slot equals giving it gate 0; dropping all
+    leaves the shared expert, a dense SwiGLU FFN."""
+    w = Workload("drop", 61, "bf16", 12, 64, 6, 3, 64, 1, "softmax")
+    inp = synth.make_inputs(w)
+    y, idx, gates = oracle.layer(inp)
+    keep = np.ones_like(idx, dtype=np.uint8)
+    np.testing.assert_array_equal(oracle.layer_dropping(inp, idx, gates, keep), y)
+    rng = np.random.default_rng(1)
+    keep = (rng.random(idx.shape) < 0.6).astype(np.uint8)
+    g0 = np.where(keep == 1, gates, 0.0).astype(np.float32)
+    y0, _, _ = oracle.layer(inp, idx=idx, gates=g0)
+    np.testing.assert_array_equal(oracle.layer_dropping(inp, idx, gates, keep), y0)
+    none = oracle.layer_dropping(inp, idx, gates, np.zeros_like(keep))
+    x = _as_f64(inp["x"], "bf16")
+    ref = _dense_swiglu_torch(x, _as_f64(inp["w1"][w.E], "bf16"), _as_f64(inp["w2"][w.E], "bf16"))
+    np.testing.assert_allclose(none, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_bias_update_closed_forms():
+    E = 8
+    b = np.linspace(-0.3, 0.4, E).astype(np.float32)
+    np.testing.assert_array_equal(oracle.bias_update(np.full(E, 5), b, 0.01), b)  # on target
+    c = np.zeros(E, dtype=np.int32)
+    c[3] = 40
+    got = oracle.bias_update(c, b, 0.125)
+    want = b + np.float32(0.125)
+    want[3] = b[3] - np.float32(0.125)
+    np.testing.assert_array_equal(got, want)
+    c = np.array([3, 5, 4, 4, 4, 4, 4, 4], dtype=np.int32)  # mean 4: experts 2..7 exactly on target
+    got = oracle.bias_update(c, np.zeros(E, np.float32), 0.5)
+    np.testing.assert_array_equal(got, np.array([0.5, -0.5, 0, 0, 0, 0, 0, 0], dtype=np.float32))
+
+
+def test_bias_update_loop_balances_a_skewed_router():
+    """The MoE lesson's loop (Step 2: 100 tokens routed, then +-gamma per expert, repeated):
+    on a router skewed towards a few experts the per-expert load moves towards uniform."""
+    w = Workload("loop", 62, "f32", 100, 32, 8, 2, 128, 0, "softmax")
+    inp = synth.make_inputs(w)
+    # skew: scale up the router rows of experts 0 and 1
+    inp["w_router"][:2] *= 4.0
+    bias = np.zeros(w.E, dtype=np.float32)
+    loads = []
+    for _ in range(50):
+        inp["bias"] = bias
+        r = oracle.route(inp)
+        counts = oracle.dispatch(w, r["idx"])["counts"]
+        loads.append(counts.max() / counts.mean())
+        bias = oracle.bias_update(counts, bias, 0.05)
+    assert loads[0] > 1.5, loads[0]
+    assert max(loads[-10:]) <= 1.2 and max(loads[-10:]) < loads[0] - 0.3, loads
