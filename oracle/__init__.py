@@ -81,6 +81,10 @@ def lib():
         L.oracle_dispatch_capacity.restype = I32
         L.oracle_bias_update.argtypes = [I32, VP, VP, ctypes.c_float]
         L.oracle_bias_update.restype = None
+        L.oracle_dequant_e4m3_rows.argtypes = [VP, VP, I64, I64, VP]
+        L.oracle_dequant_e4m3_rows.restype = None
+        L.oracle_gemm_fp8_mxfp4.argtypes = [I64, I64, I64, VP, VP, VP, VP, VP]
+        L.oracle_gemm_fp8_mxfp4.restype = None
         L.oracle_keys_from.argtypes = [CP, VP, VP, VP]
         L.oracle_keys_from.restype = None
         L.oracle_input_row.argtypes = [CP, VP, I64, VP]
@@ -250,6 +254,30 @@ def down_rows(inp: dict, g: int, hhat: np.ndarray) -> np.ndarray:
     out = np.empty((n, w.d), dtype=np.float64)
     lib().oracle_down_rows(ctypes.byref(c), _p(inp["w2"]), _p(inp["w2_scale"]), int(g), _p(hhat), n, _p(out))
     return out
+
+
+def dequant_e4m3_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """e4m3 codes [n, K] and fp32 scales [n, K/128] -> fp64 values [n, K]."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    n, K = codes.shape
+    out = np.empty((n, K), dtype=np.float64)
+    lib().oracle_dequant_e4m3_rows(_p(codes), _p(scales), n, K, _p(out))
+    return out
+
+
+def gemm_fp8_mxfp4(a, a_scale, b, b_scale, rows=None) -> np.ndarray:
+    """Dense FP8 x MXFP4 GEMM: A codes [M, K] + scales [M, K/128], B MXFP4 [N, K/2] + e8m0
+    [N, K/32] -> C [M, N] fp64 (for the listed rows of A only, when given)."""
+    a = np.ascontiguousarray(a if rows is None else a[rows], dtype=np.uint8)
+    a_scale = np.ascontiguousarray(a_scale if rows is None else a_scale[rows], dtype=np.float32)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    b_scale = np.ascontiguousarray(b_scale, dtype=np.uint8)
+    M, K = a.shape
+    N = b.shape[0]
+    c = np.empty((M, N), dtype=np.float64)
+    lib().oracle_gemm_fp8_mxfp4(M, N, K, _p(a), _p(a_scale), _p(b), _p(b_scale), _p(c))
+    return c
 
 
 def layer_dropping(inp: dict, idx, gates, keep, tokens=None, nthreads: int = 0):

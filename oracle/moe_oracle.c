@@ -596,3 +596,34 @@ void oracle_down_rows(const oracle_cfg *c, const void *w2, const void *w2s, int 
             out[r * d + o] = s;
         }
 }
+
+/* ---- FP8 operands given as codes ----------------------------------------------------- */
+
+/* Rows of e4m3 codes [n, K] with fp32 scales per 128 [n, K/128] -> fp64 values code * scale. */
+void oracle_dequant_e4m3_rows(const uint8_t *codes, const float *scales, int64_t n, int64_t K, double *out) {
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t i = 0; i < K; ++i)
+            out[r * K + i] = oracle_e4m3_decode(codes[r * K + i]) * (double)scales[r * (K / 128) + i / 128];
+}
+
+/*
+ * The dense FP8 x MXFP4 GEMM that ships next to the fused MoE kernel (Mega MoE blog,
+ * "What's new"): C[m][n] = sum_k A[m][k] B[n][k], A given as e4m3 codes [M, K] with fp32
+ * scales per 1x128 [M, K/128], B as MXFP4 (e2m1 codes [N, K/2], even k in the low nibble,
+ * e8m0 scales [N, K/32]); every operand dequantised exactly, the sum in fp64 in k order.
+ */
+void oracle_gemm_fp8_mxfp4(int64_t M, int64_t N, int64_t K, const uint8_t *a, const float *as, const uint8_t *b,
+                           const uint8_t *bs, double *c) {
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double av = oracle_e4m3_decode(a[m * K + k]) * (double)as[m * (K / 128) + k / 128];
+                uint8_t byte = b[(n * K + k) >> 1];
+                uint8_t code = (k & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+                double bv = oracle_e2m1_decode(code) * oracle_e8m0_decode(bs[n * (K / 32) + k / 32]);
+                s += av * bv;
+            }
+            c[m * N + n] = s;
+        }
+}

@@ -57,8 +57,11 @@ def lib():
         L.synth_u32.argtypes = [U64, U32, U64, U64, VP]
         L.synth_mxfp4.argtypes = [U64, U32, U64, U64, U64, F32, VP, VP, I32]
         L.synth_mxfp4_intgrid.argtypes = [U64, U32, U64, U64, U64, I32, I32, VP, VP, I32]
+        L.synth_fp8_rows.argtypes = [U64, U32, U64, U64, U64, F32, VP, VP, I32]
+        L.synth_fp8_rows_intgrid.argtypes = [U64, U32, U64, U64, U64, I32, I32, VP, VP, I32]
         for f in ("synth_philox4x32_10", "synth_normal_f32", "synth_normal_bf16", "synth_intgrid_f32",
-                  "synth_intgrid_bf16", "synth_u32", "synth_mxfp4", "synth_mxfp4_intgrid"):
+                  "synth_intgrid_bf16", "synth_u32", "synth_mxfp4", "synth_mxfp4_intgrid", "synth_fp8_rows",
+                  "synth_fp8_rows_intgrid"):
             getattr(L, f).restype = None
         _lib = L
     return _lib
@@ -129,6 +132,21 @@ def mxfp4(seed, tid, G, R, K, sigma, grid=None):
     else:
         lib().synth_mxfp4_intgrid(seed, tid, 0, G * R, K, grid[0], grid[1], _ptr(codes), _ptr(scales),
                                   threads())
+    return codes, scales
+
+
+def fp8_rows(seed, tid, rows, K, sigma, grid=None, row0=0):
+    """[rows, K] drawn N(0, sigma^2) (or integers in grid=(lo, hi), scale 1), encoded as FP8 e4m3
+    with one power-of-two fp32 scale per 128 along K (the OCP MX v1.0 scale rule, E4M3
+    elements).  Returns (codes uint8 [rows, K], scales float32 [rows, K/128])."""
+    assert K % 128 == 0
+    codes = np.empty((rows, K), dtype=np.uint8)
+    scales = np.empty((rows, K // 128), dtype=np.float32)
+    if grid is None:
+        lib().synth_fp8_rows(seed, tid, row0, rows, K, sigma, _ptr(codes), _ptr(scales), threads())
+    else:
+        lib().synth_fp8_rows_intgrid(seed, tid, row0, rows, K, grid[0], grid[1], _ptr(codes), _ptr(scales),
+                                     threads())
     return codes, scales
 
 

@@ -284,3 +284,94 @@ void synth_mxfp4_intgrid(uint64_t seed, uint32_t tensor_id, uint64_t row0, uint6
     mx_ctx c = {seed, tensor_id, row0, K, 0.f, lo, hi, 1, codes, scales};
     parallel_range(mx_rows, &c, rows, 1, nthreads);
 }
+
+/* ---- FP8 e4m3 rows with one power-of-two scale per 128 (OCP MX v1.0, E4M3 elements) ---- */
+
+/* OCP E4M3FN code of v, round-to-nearest-even, saturating at 448 (code 0x7E). */
+static inline uint8_t e4m3_rne_sat(float v) {
+    uint8_t s = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (!(a < 448.0)) return (uint8_t)(s | 0x7E);
+    int code;
+    if (a < ldexp(1.0, -6)) {                 /* subnormals: multiples of 2^-9 */
+        double q = a * 512.0, f = floor(q);
+        int m = (int)f;
+        if (q - f > 0.5 || (q - f == 0.5 && (m & 1))) ++m;
+        code = m;                             /* m == 8 is the smallest normal, code 0x08 */
+    } else {
+        int ex;
+        double m = frexp(a, &ex);             /* a = m 2^ex, m in [0.5, 1) */
+        int E = ex - 1;                       /* a = (2m) 2^E, 2m in [1, 2) */
+        double q = (2.0 * m - 1.0) * 8.0, f = floor(q);
+        int mant = (int)f;
+        if (q - f > 0.5 || (q - f == 0.5 && (mant & 1))) ++mant;
+        if (mant == 8) { mant = 0; ++E; }
+        code = ((E + 7) << 3) | mant;
+        if (code > 0x7E) code = 0x7E;
+    }
+    return (uint8_t)(s | code);
+}
+
+typedef struct {
+    uint64_t seed;
+    uint32_t tensor_id;
+    uint64_t row0, K;
+    float sigma;
+    int grid_lo, grid_hi, use_grid;
+    uint8_t *codes;
+    float *scales;
+} f8_ctx;
+
+static void f8_rows(void *p, uint64_t r0, uint64_t r1) {
+    f8_ctx *c = (f8_ctx *)p;
+    uint64_t K = c->K;
+    float v[128];
+    for (uint64_t r = r0; r < r1; ++r) {
+        uint64_t grow = c->row0 + r;
+        for (uint64_t kb = 0; kb < K / 128; ++kb) {
+            uint64_t base = grow * K + kb * 128;
+            if (c->use_grid) {
+                grid_ctx g = {c->seed, base, c->tensor_id, c->grid_lo, c->grid_hi, v, NULL};
+                grid_range(&g, 0, 128);
+            } else {
+                normal_ctx n = {c->seed, base, c->tensor_id, c->sigma, v, NULL};
+                normal_range(&n, 0, 128);
+            }
+            int e = 0;
+            if (!c->use_grid) {
+                float amax = 0.f;
+                for (int i = 0; i < 128; ++i) amax = fmaxf(amax, fabsf(v[i]));
+                if (amax > 0.f) {
+                    int p2;
+                    frexpf(amax, &p2);
+                    e = (p2 - 1) - 8;          /* floor(log2(amax)) - emax(e4m3) */
+                    if (e < -127) e = -127;
+                    if (e > 127) e = 127;
+                }
+            }
+            c->scales[r * (K / 128) + kb] = ldexpf(1.0f, e);
+            float inv = ldexpf(1.0f, -e);
+            for (int i = 0; i < 128; ++i) c->codes[r * K + kb * 128 + i] = e4m3_rne_sat(v[i] * inv);
+        }
+    }
+}
+
+/*
+ * Draws rows [row0, row0+rows) of a [*, K] tensor from N(0, sigma^2) and encodes them as
+ * FP8 e4m3 with one power-of-two fp32 scale per 128 consecutive values: the OCP MX v1.0
+ * scale rule with E4M3 elements (shared exponent floor(log2 amax) - 8, elements rounded to
+ * nearest even and saturated at 448).  codes [rows, K], scales [rows, K/128].  K must be a
+ * multiple of 128.
+ */
+void synth_fp8_rows(uint64_t seed, uint32_t tensor_id, uint64_t row0, uint64_t rows, uint64_t K, float sigma,
+                    uint8_t *codes, float *scales, int nthreads) {
+    f8_ctx c = {seed, tensor_id, row0, K, sigma, 0, 0, 0, codes, scales};
+    parallel_range(f8_rows, &c, rows, 1, nthreads);
+}
+
+/* Integer-grid FP8 rows: values drawn from [lo, hi] (|v| <= 16, exact in e4m3), scale 1. */
+void synth_fp8_rows_intgrid(uint64_t seed, uint32_t tensor_id, uint64_t row0, uint64_t rows, uint64_t K, int lo,
+                            int hi, uint8_t *codes, float *scales, int nthreads) {
+    f8_ctx c = {seed, tensor_id, row0, K, 0.f, lo, hi, 1, codes, scales};
+    parallel_range(f8_rows, &c, rows, 1, nthreads);
+}

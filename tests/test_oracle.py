@@ -608,3 +608,41 @@ def test_bias_update_loop_balances_a_skewed_router():
         bias = oracle.bias_update(counts, bias, 0.05)
     assert loads[0] > 1.5, loads[0]
     assert max(loads[-10:]) <= 1.2 and max(loads[-10:]) < loads[0] - 0.3, loads
+
+
+def test_fp8_row_generator_encodes_within_half_step():
+    """synth.fp8_rows: the scale is 2^(floor(log2 amax) - 8) per 128 values, and each code is
+    torch's e4m3 cast of value / scale (round to nearest even; saturated at 448)."""
+    codes, scales = synth.fp8_rows(5, 9, 6, 256, 0.3)
+    z = synth.normal(5, 9, (6, 256), 0.3)  # the very draws (same seed, tensor, counters)
+    for r in range(6):
+        for b in range(2):
+            v = z[r, b * 128:(b + 1) * 128]
+            e = math.floor(math.log2(float(np.abs(v).max()))) - 8
+            assert scales[r, b] == np.float32(2.0 ** e)
+            want = torch.from_numpy((v / scales[r, b]).astype(np.float32)).clamp(-448, 448).to(torch.float8_e4m3fn)
+            np.testing.assert_array_equal(codes[r, b * 128:(b + 1) * 128], want.view(torch.uint8).numpy())
+    gc, gs = synth.fp8_rows(5, 9, 4, 128, 0.0, grid=(-3, 3))
+    vals = np.array([oracle.e4m3_decode(int(c)) for c in gc.reshape(-1)]).reshape(gc.shape)
+    np.testing.assert_array_equal(vals, synth.intgrid(5, 9, (4, 128), -3, 3))
+    assert np.all(gs == 1.0)
+
+
+def test_dense_fp8_mxfp4_gemm():
+    """oracle.gemm_fp8_mxfp4: torch fp64 matmul on independently dequantised operands (torch's
+    float8 decode of the A codes; the OCP e2m1 table times 2^(e8m0 - 127) for B); integer
+    operands give exact integer sums; and linear2 of the layer is this GEMM on h."""
+    a, a_s = synth.fp8_rows(3, 1, 7, 256, 1.0)
+    b, b_s = synth.mxfp4(3, 2, 1, 64, 256, 0.1)
+    b, b_s = b[0], b_s[0]
+    lut = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0., -.5, -1, -1.5, -2, -3, -4, -6])
+    nib = np.stack([b & 15, b >> 4], -1).reshape(b.shape[0], -1)
+    B = lut[nib] * np.exp2(np.repeat(b_s.astype(np.int64) - 127, 32, axis=-1))
+    A = torch.from_numpy(a).view(torch.float8_e4m3fn).to(torch.float64).numpy() * np.repeat(a_s, 128, 1)
+    np.testing.assert_array_equal(oracle.dequant_e4m3_rows(a, a_s), A)
+    np.testing.assert_allclose(oracle.gemm_fp8_mxfp4(a, a_s, b, b_s), A @ B.T, rtol=1e-12, atol=1e-12)
+    gi, gs = synth.fp8_rows(3, 3, 5, 128, 0.0, grid=(-3, 3))
+    wb, ws_ = synth.mxfp4(3, 4, 1, 16, 128, 0.0, grid=(-2, 2))
+    want = synth.intgrid(3, 3, (5, 128), -3, 3).astype(np.int64) @ \
+        synth.intgrid(3, 4, (16, 128), -2, 2).astype(np.int64).T
+    np.testing.assert_array_equal(oracle.gemm_fp8_mxfp4(gi, gs, wb[0], ws_[0]), want.astype(np.float64))
