@@ -116,6 +116,7 @@ typedef struct {
 #define MOE_DEVERR_DUP 2       /* a token chose the same expert twice */
 #define MOE_DEVERR_NONFINITE 3 /* a selection key is NaN or infinite */
 #define MOE_DEVERR_TIMEOUT 4   /* a bounded wait in the persistent kernel expired */
+#define MOE_DEVERR_OVERFLOW 5  /* moe_ep_ffn: received rows exceed the receive buffer, or a count < 0 */
 
 /* Human-readable name of a status code (static string). */
 const char *moe_status_str(moe_status s);
@@ -199,6 +200,50 @@ moe_status moe_dispatch(const moe_cfg *cfg, const int32_t *topk_idx, const void 
                         float *xq_scale, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The capacity variant of the dispatch: expert capacity with token dropping (MoE
+ * lesson, factory.pai-world.com, "The load-balancing problem", item 2: each expert takes
+ * at most C x N / E tokens and the rest skip the layer).  `capacity` is that bound in
+ * slots per routed expert -- for a capacity factor C, floor(C * T * k / E), the N of the
+ * lesson's bound being the T*k routed slots (with k = 1, the tokens).  Of the slots that
+ * chose expert e, the first `capacity` in slot order (ascending token order, as in the
+ * dropless dispatch) are kept; the shared expert has no capacity.  Row layout, with
+ * D = the number of dropped slots:
+ *  rows 0 .. D-1         the dropped slots, expert by expert, in slot order (never computed);
+ *  rows offsets[e] ..    expert e's kept slots, offsets[0] = D, offsets[E] = T*k;
+ *  rows T*k + t          the shared expert (as in moe_dispatch).
+ * So moe_ffn runs unchanged on these offsets (only kept rows belong to a group), and
+ * moe_combine leaves dropped slots out: their slot_to_row is -1 (their gates are not
+ * renormalised).
+ *  capacity            >= 0 (0 drops every routed slot)
+ *  counts [G]          int32 out: kept rows per group (counts[E] = T when n_shared)
+ *  dropped [E]         int32 out: dropped slots per routed expert (the overflow)
+ *  offsets [G + 1]     int32 out: first row of each group, as above
+ *  slot_to_row [T*k]   int32 out: the row of a kept slot, -1 for a dropped one
+ *  row_to_slot [T*k]   int32 out: the slot of every row (dropped rows included)
+ *  x, xq, xq_scale     as in moe_dispatch (the FP8 activation stage)
+ * Bad or duplicate indices set the device error word as in moe_dispatch.
+ */
+moe_status moe_dispatch_capacity(const moe_cfg *cfg, const int32_t *topk_idx, const void *x, int32_t capacity,
+                                 int32_t *counts, int32_t *dropped, int32_t *offsets, int32_t *slot_to_row,
+                                 int32_t *row_to_slot, uint8_t *xq, float *xq_scale, void *ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/*
+ * Aux-loss-free load balancing, one update of the per-expert selection bias that
+ * moe_route adds to the keys (MoE lesson, "The load-balancing problem", the DeepSeek-V3
+ * scheme, and "Build it -- Step 2: route 100 tokens"): after a step, bias[e] -= gamma
+ * for a routed expert used more than the mean load, bias[e] += gamma for one used less,
+ * unchanged for one exactly on it (compared in integers: counts[e] * E against the sum
+ * of the E counts).  fp32 additions, on device, stream-ordered.
+ *  counts [>= E]  int32 in: routed slots per expert -- the counts moe_dispatch writes (or,
+ *                 under the capacity variant, counts + dropped: the load the router asked
+ *                 for); only the first E entries are read
+ *  bias [E]       fp32 in/out
+ *  gamma          >= 0
+ */
+moe_status moe_bias_update(const moe_cfg *cfg, const int32_t *counts, float *bias, float gamma, hipStream_t stream);
+
+/*
  * moe_dispatch for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation.  Same arguments,
  * kernels and results as moe_dispatch, without a workspace: the per-(dispatch block,
@@ -235,6 +280,55 @@ moe_status moe_quant_e4m3(const void *in, int32_t in_dtype, int64_t rows, int32_
                           hipStream_t stream);
 
 /*
+ * The dense FP8 x MXFP4 GEMM that ships alongside the fused MoE kernel (Mega MoE blog,
+ * donniechu.com, "What's new"), on the same scaled-MFMA tiles as the expert linears:
+ *   C[M, N] = A[M, K] . B[N, K]^T,  fp32 accumulation, C rounded to bf16 (nearest even).
+ *  a [M, K]        uint8 e4m3 codes (OCP E4M3FN), a_scale [M, K/128] fp32 power-of-two scales
+ *                  per 1x128 block (e.g. from moe_quant_e4m3)
+ *  b [N, K/2]      uint8 MXFP4: e2m1 codes, even K index in the low nibble; b_scale [N, K/32]
+ *                  e8m0 bytes (the PyTorch Linear layout, out x in)
+ *  c [M, N]        bf16 out
+ *  ws              MOE_GEMM_WORKSPACE_BYTES of device scratch (the tile plan)
+ * Limits: 0 <= M < 2^31, N and K multiples of 128 up to 65536.  M == 0 is a no-op.
+ */
+#define MOE_GEMM_WORKSPACE_BYTES 256
+moe_status moe_gemm_fp8_mxfp4(int64_t M, int32_t N, int32_t K, const uint8_t *a, const float *a_scale,
+                              const uint8_t *b, const uint8_t *b_scale, void *c, void *ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/*
+ * One expert-parallel rank's share of the layer (Mega MoE wiki, aiki.softdaddy-o.com,
+ * "Why it matters": EP8 with per-rank batches; Mega MoE blog, "What's new": the dispatch
+ * sends each token's FP8 row to the ranks that own its experts, and the expert outputs go
+ * back for the combine).  The rank owns cfg->E local experts (plus the replicated shared
+ * expert when cfg->n_shared = 1) and runs them over the rows it received, then the shared
+ * expert over its own cfg->T tokens; the outputs are left in receive order, ready to go
+ * back.  Receive buffer layout: the rows of local expert e from source rank s form block
+ * (e, s), blocks in expert-major order (expert 0: sources 0, 1, ..; then expert 1 ..),
+ * each block's rows in the source's token order; recv_counts [E, n_src] (device int32)
+ * holds the block sizes.  Same tile plan and kernels as moe_ffn's FP8 x MXFP4 path, the
+ * rows read in place (no gather).
+ *  cfg             mode MOE_MODE_FP8_MXFP4; E = local experts; T = the rank's own tokens
+ *                  (shared expert rows; k is not used)
+ *  w               the local experts' weights, canonical layout, G = E + n_shared groups
+ *                  (the shared expert last)
+ *  recv_capacity   rows the receive buffers hold (host value); the received rows
+ *                  (sum of recv_counts) must fit, else MOE_DEVERR_OVERFLOW and the rows past
+ *                  the capacity are not computed
+ *  recv_xq [recv_capacity, d] uint8 e4m3 codes, recv_xs [recv_capacity, d/128] fp32 scales
+ *  y_recv [recv_capacity, d] bf16 out: each received row's expert output, same row order
+ *  xq [T, d], xs [T, d/128]: the rank's own tokens in FP8 (moe_quant_e4m3 or moe_dispatch)
+ *  y_shared [T, d] bf16 out: the shared expert's output per own token
+ *  ws              moe_ep_workspace_bytes(cfg, recv_capacity) bytes (error word first:
+ *                  moe_read_device_error(cfg, ws, ...) reads it)
+ */
+size_t moe_ep_workspace_bytes(const moe_cfg *cfg, int64_t recv_capacity);
+moe_status moe_ep_ffn(const moe_cfg *cfg, const moe_weights *w, int32_t n_src, const int32_t *recv_counts,
+                      int64_t recv_capacity, const uint8_t *recv_xq, const float *recv_xs, void *y_recv,
+                      const uint8_t *xq, const float *xs, void *y_shared, void *ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/*
  * Expert FFNs over the dispatched rows: linear1 (gate+up) with SwiGLU fused in
  * its epilogue, then linear2 (Mega MoE blog, donniechu.com, spec table).
  * Row r of group g reads token row_to_slot[r] / k (routed) or r - T*k (shared).
@@ -251,7 +345,8 @@ moe_status moe_ffn(const moe_cfg *cfg, const moe_weights *w, const void *x, cons
 /*
  * Gate-weighted combine (MoE playbook "How it works", combine step; MoE lesson
  * "Shared expert"):  y[t] = (((g_0 o_0 + g_1 o_1) + ...) + g_{k-1} o_{k-1}) + o_shared
- * in fp32 in exactly that order, then rounded to nearest even to y's dtype.
+ * in fp32 in exactly that order, then rounded to nearest even to y's dtype.  A slot
+ * whose slot_to_row is negative (dropped by moe_dispatch_capacity) is left out.
  *  y_perm [T*k + n_shared*T, d], slot_to_row [T*k], topk_gate [T, k] in;  y [T, d] out.
  */
 moe_status moe_combine(const moe_cfg *cfg, const void *y_perm, const int32_t *slot_to_row,

@@ -70,6 +70,16 @@ def lib():
         L.moe_workspace_region.restype = I32
         L.moe_quant_e4m3.argtypes = [VP, I32, ctypes.c_int64, I32, VP, VP, VP]
         L.moe_quant_e4m3.restype = I32
+        L.moe_dispatch_capacity.argtypes = [CP, VP, VP, I32, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_dispatch_capacity.restype = I32
+        L.moe_bias_update.argtypes = [CP, VP, VP, ctypes.c_float, VP]
+        L.moe_bias_update.restype = I32
+        L.moe_gemm_fp8_mxfp4.argtypes = [ctypes.c_int64, I32, I32, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_gemm_fp8_mxfp4.restype = I32
+        L.moe_ep_workspace_bytes.argtypes = [CP, ctypes.c_int64]
+        L.moe_ep_workspace_bytes.restype = SZ
+        L.moe_ep_ffn.argtypes = [CP, WP, I32, VP, ctypes.c_int64, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_ep_ffn.restype = I32
         L.moe_dispatch_noalloc.argtypes = [CP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP]
         L.moe_profile_enable.argtypes = [I32]
         L.moe_profile_report.argtypes = [ctypes.c_char_p, SZ]
@@ -84,7 +94,10 @@ def lib():
 EXPORTS = ("moe_status_str", "moe_device_check", "moe_workspace_bytes", "moe_clear_device_error",
            "moe_read_device_error", "moe_route", "moe_dispatch", "moe_ffn", "moe_combine", "moe_layer_fused",
            "moe_profile_enable", "moe_profile_report", "moe_dispatch_noalloc",
-           "moe_workspace_region", "moe_quant_e4m3")
+           "moe_workspace_region", "moe_quant_e4m3", "moe_dispatch_capacity", "moe_bias_update",
+           "moe_gemm_fp8_mxfp4", "moe_ep_workspace_bytes", "moe_ep_ffn")
+DEVERR[5] = "received rows exceed the receive buffer"
+GEMM_WORKSPACE_BYTES = 256
 
 
 @dataclass(frozen=True)
@@ -237,6 +250,92 @@ def dispatch(cfg: Config, topk_idx, x=None, *, ws, out=None, stream=None):
                               _p(o["slot_to_row"]), _p(o["row_to_slot"]), _p(o["xq"]), _p(o["xq_scale"]),
                               _p(ws), ws.numel(), _stream(stream)), "moe_dispatch")
     return o
+
+
+def capacity_of(factor: float, cfg: Config) -> int:
+    """Slots per routed expert for a capacity factor C: floor(C * T * k / E)."""
+    import math
+    return int(math.floor(factor * cfg.T * cfg.k / cfg.E))
+
+
+def dispatch_capacity(cfg: Config, topk_idx, capacity: int, x=None, *, ws, out=None, stream=None):
+    """The capacity variant of S5-S7 (moe_dispatch_capacity).  Returns dict(counts (kept rows),
+    dropped, offsets, slot_to_row (-1 when dropped), row_to_slot, xq, xq_scale)."""
+    dev = topk_idx.device
+    _expect(topk_idx, (cfg.T, cfg.k), torch.int32, "topk_idx")
+    o = dict(out or {})
+    o.setdefault("counts", torch.empty(cfg.G, dtype=torch.int32, device=dev))
+    o.setdefault("dropped", torch.empty(cfg.E, dtype=torch.int32, device=dev))
+    o.setdefault("offsets", torch.empty(cfg.G + 1, dtype=torch.int32, device=dev))
+    o.setdefault("slot_to_row", torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev))
+    o.setdefault("row_to_slot", torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev))
+    if cfg.mode == "fp8_mxfp4":
+        _expect(x, (cfg.T, cfg.d), torch.bfloat16, "x")
+        o.setdefault("xq", torch.empty(cfg.T, cfg.d, dtype=torch.uint8, device=dev))
+        o.setdefault("xq_scale", torch.empty(cfg.T, cfg.d // 128, dtype=torch.float32, device=dev))
+    else:
+        o.setdefault("xq", None)
+        o.setdefault("xq_scale", None)
+    _check(lib().moe_dispatch_capacity(ctypes.byref(cfg.c()), _p(topk_idx), _p(x), int(capacity), _p(o["counts"]),
+                                       _p(o["dropped"]), _p(o["offsets"]), _p(o["slot_to_row"]),
+                                       _p(o["row_to_slot"]), _p(o["xq"]), _p(o["xq_scale"]), _p(ws), ws.numel(),
+                                       _stream(stream)), "moe_dispatch_capacity")
+    return o
+
+
+def bias_update(cfg: Config, counts, bias, gamma: float, stream=None):
+    """One aux-loss-free bias update in place (moe_bias_update): bias [E] fp32 from counts."""
+    if counts.dtype != torch.int32 or counts.numel() < cfg.E:
+        raise ValueError("counts: int32 with at least E entries")
+    _expect(bias, (cfg.E,), torch.float32, "bias")
+    _check(lib().moe_bias_update(ctypes.byref(cfg.c()), _p(counts), _p(bias), float(gamma), _stream(stream)),
+           "moe_bias_update")
+    return bias
+
+
+def gemm_fp8_mxfp4(a, a_scale, b, b_scale, *, ws=None, c=None, stream=None):
+    """Dense FP8 x MXFP4 GEMM (moe_gemm_fp8_mxfp4): a [M, K] e4m3 codes + [M, K/128] fp32 scales,
+    b [N, K/2] MXFP4 + [N, K/32] e8m0 -> c [M, N] bf16."""
+    M, K = a.shape
+    N = b.shape[0]
+    _expect(a, (M, K), torch.uint8, "a")
+    _expect(a_scale, (M, K // 128), torch.float32, "a_scale")
+    _expect(b, (N, K // 2), torch.uint8, "b")
+    _expect(b_scale, (N, K // 32), torch.uint8, "b_scale")
+    c = c if c is not None else torch.empty(M, N, dtype=torch.bfloat16, device=a.device)
+    ws = ws if ws is not None else torch.empty(GEMM_WORKSPACE_BYTES, dtype=torch.uint8, device=a.device)
+    _check(lib().moe_gemm_fp8_mxfp4(M, N, K, _p(a), _p(a_scale), _p(b), _p(b_scale), _p(c), _p(ws), ws.numel(),
+                                    _stream(stream)), "moe_gemm_fp8_mxfp4")
+    return c
+
+
+def ep_workspace(cfg: Config, recv_capacity: int, device="cuda") -> torch.Tensor:
+    n = lib().moe_ep_workspace_bytes(ctypes.byref(cfg.c()), int(recv_capacity))
+    if n == 0:
+        raise MoeError(2, "invalid expert-parallel configuration")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def ep_ffn(cfg: Config, w1, w2, w1_scale, w2_scale, *, recv_counts, recv_xq, recv_xs, xq=None, xs=None, ws,
+           y_recv=None, y_shared=None, stream=None):
+    """One expert-parallel rank's experts over its receive buffer (moe_ep_ffn).  cfg.E local
+    experts, cfg.T own tokens; recv_counts [E, n_src] int32.  Returns (y_recv, y_shared)."""
+    cap = recv_xq.shape[0]
+    n_src = recv_counts.shape[1]
+    _expect(recv_counts, (cfg.E, n_src), torch.int32, "recv_counts")
+    _expect(recv_xq, (cap, cfg.d), torch.uint8, "recv_xq")
+    _expect(recv_xs, (cap, cfg.d // 128), torch.float32, "recv_xs")
+    dev = recv_xq.device
+    y_recv = y_recv if y_recv is not None else torch.empty(cap, cfg.d, dtype=torch.bfloat16, device=dev)
+    if cfg.n_shared:
+        _expect(xq, (cfg.T, cfg.d), torch.uint8, "xq")
+        _expect(xs, (cfg.T, cfg.d // 128), torch.float32, "xs")
+        y_shared = y_shared if y_shared is not None else torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device=dev)
+    W = _weights(cfg, w1, w2, w1_scale, w2_scale)
+    _check(lib().moe_ep_ffn(ctypes.byref(cfg.c()), ctypes.byref(W), n_src, _p(recv_counts), cap, _p(recv_xq),
+                            _p(recv_xs), _p(y_recv), _p(xq), _p(xs), _p(y_shared), _p(ws), ws.numel(),
+                            _stream(stream)), "moe_ep_ffn")
+    return y_recv, y_shared
 
 
 def dispatch_noalloc(cfg: Config, topk_idx, x=None, *, err=None, out=None, stream=None):

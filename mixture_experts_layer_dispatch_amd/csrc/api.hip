@@ -33,7 +33,7 @@ Shape shape_of(const moe_cfg *c) {
 
 // Workspace regions (byte offsets, each aligned to 256).
 struct Layout {
-    size_t err, blockcounts, tiles, h, hs, rpart, upart;             // every path
+    size_t err, blockcounts, dbase, tiles, h, hs, rpart, upart;      // every path
     size_t idx, gate, counts, offsets, s2r, r2s, xq, xs, yperm, sync, done1;  // fused path
     size_t total;
 };
@@ -51,6 +51,7 @@ Layout layout_of(const moe_cfg *c) {
     const bool fp8 = c->mode == MOE_MODE_FP8_MXFP4, f32 = c->mode == MOE_MODE_F32;
     L.err = take(256);  // sticky error word
     L.blockcounts = take((size_t)dispatch_blocks(c->T) * E * 4);
+    L.dbase = take(E * 4);  // capacity variant: first dropped row per expert
     L.tiles = take(2 * (G + 1) * 4);
     L.h = take(rows * F * (f32 ? 4 : fp8 ? 1 : 2));
     L.hs = fp8 ? take(rows * (F / 128) * 4) : 0;
@@ -201,6 +202,78 @@ moe_status moe_quant_e4m3(const void *in, int32_t in_dtype, int64_t rows, int32_
                                       stream));
 }
 
+moe_status moe_gemm_fp8_mxfp4(int64_t M, int32_t N, int32_t K, const uint8_t *a, const float *a_scale,
+                              const uint8_t *b, const uint8_t *b_scale, void *c, void *ws, size_t ws_bytes,
+                              hipStream_t stream) {
+    if (M < 0 || M > (1L << 31) - 1 || N < 128 || N % 128 || N > 65536 || K < 128 || K % 128 || K > 65536)
+        return MOE_ERR_SHAPE;
+    if (M == 0) return MOE_OK;
+    if (!a || !a_scale || !b || !b_scale || !c || !ws) return MOE_ERR_NULL;
+    for (const void *p : {(const void *)a, (const void *)a_scale, (const void *)b, (const void *)b_scale, (const void *)c,
+                          (const void *)ws})
+        if (!aligned16(p)) return MOE_ERR_ALIGN;
+    if (ws_bytes < MOE_GEMM_WORKSPACE_BYTES) return MOE_ERR_WORKSPACE;
+    MOE_TRY(arch_check());
+    return launched(launch_gemm_fp8_dense(M, N, K, a, a_scale, b, b_scale, c, (int32_t *)ws, stream));
+}
+
+namespace {
+struct EpLayout {
+    size_t err, plan, h, hs, total;
+};
+EpLayout ep_layout(const moe_cfg *c, int64_t cap) {
+    EpLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += (bytes + 255) & ~(size_t)255;
+        return o;
+    };
+    const size_t rows = (size_t)cap + (size_t)c->n_shared * c->T;
+    L.err = take(256);
+    L.plan = take((3 * ((size_t)c->E + 1) + 6) * 4);
+    L.h = take(rows * c->F);
+    L.hs = take(rows * (c->F / 128) * 4);
+    L.total = off;
+    return L;
+}
+moe_status ep_validate(const moe_cfg *cfg, int64_t cap) {
+    MOE_TRY(validate(cfg));
+    if (cfg->mode != MOE_MODE_FP8_MXFP4) return MOE_ERR_MODE;
+    if (cap < 0 || cap + (int64_t)cfg->n_shared * cfg->T >= (1LL << 31)) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+}  // namespace
+
+size_t moe_ep_workspace_bytes(const moe_cfg *cfg, int64_t recv_capacity) {
+    if (ep_validate(cfg, recv_capacity) != MOE_OK) return 0;
+    return ep_layout(cfg, recv_capacity).total;
+}
+
+moe_status moe_ep_ffn(const moe_cfg *cfg, const moe_weights *w, int32_t n_src, const int32_t *recv_counts,
+                      int64_t recv_capacity, const uint8_t *recv_xq, const float *recv_xs, void *y_recv,
+                      const uint8_t *xq, const float *xs, void *y_shared, void *ws, size_t ws_bytes,
+                      hipStream_t stream) {
+    MOE_TRY(ep_validate(cfg, recv_capacity));
+    if (n_src < 1 || n_src > 4096) return MOE_ERR_SHAPE;
+    const bool routed = recv_capacity > 0, shared = cfg->n_shared && cfg->T > 0;
+    if (!routed && !shared) return MOE_OK;
+    if (!w || !w->w1 || !w->w1_scale || !w->w2 || !w->w2_scale || !ws) return MOE_ERR_NULL;
+    if (routed && (!recv_counts || !recv_xq || !recv_xs || !y_recv)) return MOE_ERR_NULL;
+    if (shared && (!xq || !xs || !y_shared)) return MOE_ERR_NULL;
+    for (const void *p : {w->w1, w->w1_scale, w->w2, w->w2_scale, (const void *)recv_counts, (const void *)recv_xq,
+                          (const void *)recv_xs, (const void *)y_recv, (const void *)xq, (const void *)xs,
+                          (const void *)y_shared, (const void *)ws})
+        if (p && !aligned16(p)) return MOE_ERR_ALIGN;
+    const EpLayout L = ep_layout(cfg, recv_capacity);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    MOE_TRY(arch_check());
+    return launched(launch_ep_ffn(shape_of(cfg), n_src, recv_counts, recv_capacity, recv_xq, recv_xs,
+                                  (const uint8_t *)w->w1, (const uint8_t *)w->w1_scale, (const uint8_t *)w->w2,
+                                  (const uint8_t *)w->w2_scale, y_recv, xq, xs, y_shared, at<int32_t>(ws, L.plan),
+                                  at<uint8_t>(ws, L.h), at<float>(ws, L.hs), at<int32_t>(ws, L.err), stream));
+}
+
 moe_status moe_route(const moe_cfg *cfg, const void *x, const void *w_router, const float *bias, int32_t *topk_idx,
                      float *topk_gate, float *logits, float *keys, void *ws, size_t ws_bytes, hipStream_t stream) {
     MOE_TRY(validate(cfg));
@@ -236,6 +309,38 @@ moe_status moe_dispatch(const moe_cfg *cfg, const int32_t *topk_idx, const void 
     return launched(launch_dispatch(s, topk_idx, at<int32_t>(ws, L.blockcounts), counts, offsets, slot_to_row,
                                     row_to_slot, at<int32_t>(ws, L.err), fp8 ? (const uint16_t *)x : nullptr,
                                     fp8 ? xq : nullptr, fp8 ? xq_scale : nullptr, stream));
+}
+
+moe_status moe_dispatch_capacity(const moe_cfg *cfg, const int32_t *topk_idx, const void *x, int32_t capacity,
+                                 int32_t *counts, int32_t *dropped, int32_t *offsets, int32_t *slot_to_row,
+                                 int32_t *row_to_slot, uint8_t *xq, float *xq_scale, void *ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+    MOE_TRY(validate(cfg));
+    if (capacity < 0) return MOE_ERR_SHAPE;
+    if (cfg->T == 0) return MOE_OK;
+    const bool fp8 = cfg->mode == MOE_MODE_FP8_MXFP4;
+    if (!topk_idx || !counts || !dropped || !offsets || !slot_to_row || !row_to_slot) return MOE_ERR_NULL;
+    if (fp8 && (!x || !xq || !xq_scale)) return MOE_ERR_NULL;
+    for (const void *p : {(const void *)topk_idx, x, (const void *)counts, (const void *)dropped,
+                          (const void *)offsets, (const void *)slot_to_row, (const void *)row_to_slot,
+                          (const void *)xq, (const void *)xq_scale})
+        if (p && !aligned16(p)) return MOE_ERR_ALIGN;
+    MOE_TRY(check_ws(cfg, ws, ws_bytes));
+    MOE_TRY(arch_check());
+    const Layout L = layout_of(cfg);
+    return launched(launch_dispatch_capacity(shape_of(cfg), topk_idx, capacity, at<int32_t>(ws, L.blockcounts),
+                                             counts, dropped, offsets, at<int32_t>(ws, L.dbase), slot_to_row,
+                                             row_to_slot, at<int32_t>(ws, L.err), fp8 ? (const uint16_t *)x : nullptr,
+                                             fp8 ? xq : nullptr, fp8 ? xq_scale : nullptr, stream));
+}
+
+moe_status moe_bias_update(const moe_cfg *cfg, const int32_t *counts, float *bias, float gamma, hipStream_t stream) {
+    MOE_TRY(validate(cfg));
+    if (!counts || !bias) return MOE_ERR_NULL;
+    if (!aligned16(counts) || !aligned16(bias)) return MOE_ERR_ALIGN;
+    if (!(gamma >= 0.0f) || gamma > 3.0e38f) return MOE_ERR_SHAPE;
+    MOE_TRY(arch_check());
+    return launched(launch_bias_update(counts, cfg->E, bias, gamma, stream));
 }
 
 moe_status moe_ffn(const moe_cfg *cfg, const moe_weights *w, const void *x, const uint8_t *xq, const float *xq_scale,

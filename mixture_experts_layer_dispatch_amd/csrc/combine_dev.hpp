@@ -5,7 +5,8 @@
 // the gate-weighted sum of the chosen experts' outputs; the lesson's "Shared
 // expert" section adds the always-on shared expert.  The sum is taken in fp32 in a
 // fixed order -- routed experts in selection order, then the shared expert -- so
-// results are bitwise reproducible, then rounded once to the output dtype.
+// results are bitwise reproducible, then rounded once to the output dtype.  A slot
+// whose slot_to_row is negative (dropped by the capacity variant) is left out.
 #pragma once
 
 #include "common.hpp"
@@ -60,9 +61,10 @@ __device__ __forceinline__ void combine_lane(const void *__restrict__ yp, const 
             const long rr = r[u] < 0 ? 0 : (r[u] >= tk ? tk - 1 : r[u]);
             q[u] = ldc16<COH>(yp, (size_t)(rr * d + c) * esz);
         }
+        // a slot without a row (slot_to_row < 0: dropped by the capacity variant) adds nothing
 #pragma unroll
         for (int u = 0; u < CH; ++u)
-            if (j0 + u < k) add_row(q[u], g[u], true);
+            if (j0 + u < k && r[u] >= 0) add_row(q[u], g[u], true);
     }
     if (S) add_row(qs, 1.0f, false);
     if constexpr (F32) {

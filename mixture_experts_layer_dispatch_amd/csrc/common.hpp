@@ -16,7 +16,14 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 enum Mode { MODE_F32 = 0, MODE_BF16 = 1, MODE_FP8 = 2 };
 enum Gating { GATE_SOFTMAX = 0, GATE_SIGMOID = 1 };
-enum DevErr { DEVERR_NONE = 0, DEVERR_INDEX = 1, DEVERR_DUP = 2, DEVERR_NONFINITE = 3, DEVERR_TIMEOUT = 4 };
+enum DevErr {
+    DEVERR_NONE = 0,
+    DEVERR_INDEX = 1,
+    DEVERR_DUP = 2,
+    DEVERR_NONFINITE = 3,
+    DEVERR_TIMEOUT = 4,
+    DEVERR_OVERFLOW = 5  // received rows exceed the receive buffer (or a negative count)
+};
 
 constexpr int kWave = 64;
 

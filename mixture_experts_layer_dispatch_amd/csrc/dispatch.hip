@@ -90,6 +90,73 @@ hipError_t launch_dispatch(const Shape &s, const int32_t *idx, int32_t *blockcou
     return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void dispatch_scan_cap_kernel(int32_t *__restrict__ blockcounts, int nblk, int T,
+                                                               int E, int S, int cap, int32_t *__restrict__ counts,
+                                                               int32_t *__restrict__ dropped,
+                                                               int32_t *__restrict__ offsets,
+                                                               int32_t *__restrict__ dbase) {
+    __shared__ int32_t sh[2048 + 256];
+    dispatch_scan_cap_block(blockcounts, nblk, T, E, S, cap, counts, dropped, offsets, dbase, sh);
+}
+
+__global__ __launch_bounds__(256) void dispatch_scatter_cap_kernel(const int32_t *__restrict__ idx, int T, int k,
+                                                                  int E, int cap, const int32_t *__restrict__ ranks,
+                                                                  const int32_t *__restrict__ offsets,
+                                                                  const int32_t *__restrict__ dbase,
+                                                                  int32_t *__restrict__ slot_to_row,
+                                                                  int32_t *__restrict__ row_to_slot) {
+    extern __shared__ unsigned long long masks[];  // [4][E]
+    scatter_cap_block(idx, T, k, E, blockIdx.x, cap, ranks, offsets, dbase, slot_to_row, row_to_slot, masks);
+}
+
+// The capacity variant: histogram (with the FP8 activations alongside), scan, scatter.
+hipError_t launch_dispatch_capacity(const Shape &s, const int32_t *idx, int cap, int32_t *blockcounts,
+                                    int32_t *counts, int32_t *dropped, int32_t *offsets, int32_t *dbase,
+                                    int32_t *slot_to_row, int32_t *row_to_slot, int32_t *err, const uint16_t *x,
+                                    uint8_t *xq, float *xs, hipStream_t st) {
+    if (s.T == 0) return hipSuccess;
+    const int nblk = dispatch_blocks(s.T);
+    const size_t lds = (size_t)4 * s.E * sizeof(unsigned long long);
+    const long nq = xq ? (long)s.T * s.d / 128 : 0;
+    const long qwg = nq ? (nq * 16 + 1023) / 1024 : 0;
+    MOE_LAUNCH("dispatch_count", dispatch_count_quant_kernel, dim3((unsigned)(nblk + qwg)), dim3(256), lds, st, idx,
+               s.T, s.k, s.E, nblk, blockcounts, err, x, nq, xq, xs);
+    MOE_LAUNCH("dispatch_scan", dispatch_scan_cap_kernel, dim3(1), dim3(256), 0, st, blockcounts, nblk, s.T, s.E, s.S,
+               cap, counts, dropped, offsets, dbase);
+    MOE_LAUNCH("dispatch_scatter", dispatch_scatter_cap_kernel, dim3(nblk), dim3(256), lds, st, idx, s.T, s.k, s.E,
+               cap, (const int32_t *)blockcounts, (const int32_t *)offsets, (const int32_t *)dbase, slot_to_row,
+               row_to_slot);
+    return hipGetLastError();
+}
+
+// Aux-loss-free balancing (MoE lesson, "The load-balancing problem", the DeepSeek-V3
+// scheme): bias[e] -= gamma for an expert above the mean load of the E routed experts,
+// += gamma below it, unchanged on it (counts[e] * E against the total, in integers).
+// One workgroup.
+__global__ __launch_bounds__(256) void bias_update_kernel(const int32_t *__restrict__ counts, int E,
+                                                         float *__restrict__ bias, float gamma) {
+    __shared__ long long part[256];
+    long long s = 0;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) s += counts[e];
+    part[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+        if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+        __syncthreads();
+    }
+    const long long total = part[0];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        const long long scaled = (long long)counts[e] * E;
+        if (scaled > total) bias[e] = bias[e] - gamma;
+        else if (scaled < total) bias[e] = bias[e] + gamma;
+    }
+}
+
+hipError_t launch_bias_update(const int32_t *counts, int E, float *bias, float gamma, hipStream_t st) {
+    MOE_LAUNCH("bias_update", bias_update_kernel, dim3(1), dim3(256), 0, st, counts, E, bias, gamma);
+    return hipGetLastError();
+}
+
 // Stand-alone FP8 quantiser: rows of fp32 or bf16 values, 1024 lanes per workgroup (64
 // blocks of 128), a grid-stride loop beyond 2^20 workgroups.
 template <bool F32>

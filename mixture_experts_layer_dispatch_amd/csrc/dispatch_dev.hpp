@@ -274,6 +274,84 @@ __device__ __forceinline__ void dispatch_single_block(const int32_t *__restrict_
     }
 }
 
+// ---- the capacity variant (expert capacity with token dropping) -------------------------
+//
+// MoE lesson (factory.pai-world.com, "The load-balancing problem", item 2): each routed
+// expert takes at most `cap` of the slots that chose it, the first ones in slot order (the
+// dropless dispatch's ascending token order); the rest skip the layer.  Layout: rows
+// 0 .. D-1 hold the D dropped slots, expert by expert in slot order (dbase[e] = the first
+// of expert e's); expert e's kept rows start at offsets[e] = D + (kept rows of the experts
+// before it), so offsets[E] = T*k and the shared expert keeps rows T*k + t.  A kept slot's
+// slot_to_row is its row, a dropped one's -1; row_to_slot covers every row.
+
+// One workgroup: per-expert totals n_e, kept min(n_e, cap) and dropped counts, both scans,
+// and each block's first rank among its expert's slots (written over the block counts).
+// sh: 2048 + 256 ints of LDS.
+__device__ __forceinline__ void dispatch_scan_cap_block(int32_t *__restrict__ blockcounts, int nblk, int T, int E,
+                                                        int S, int cap, int32_t *__restrict__ counts,
+                                                        int32_t *__restrict__ dropped,
+                                                        int32_t *__restrict__ offsets, int32_t *__restrict__ dbase,
+                                                        int32_t *sh) {
+    int32_t *kept = sh, *drop = sh + 1024, *tmp = sh + 2048;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        int n = 0;
+        for (int b = 0; b < nblk; ++b) {
+            const int c = blockcounts[(long)b * E + e];
+            blockcounts[(long)b * E + e] = n;  // the block's first rank within expert e
+            n += c;
+        }
+        const int kp = n < cap ? n : cap;
+        kept[e] = kp;
+        drop[e] = n - kp;
+        counts[e] = kp;
+        dropped[e] = n - kp;
+    }
+    __syncthreads();
+    const int nk = block_exclusive_scan(kept, E, tmp);  // kept[e] = kept rows before expert e
+    const int D = block_exclusive_scan(drop, E, tmp);   // drop[e] = dropped rows before expert e
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        offsets[e] = D + kept[e];
+        dbase[e] = drop[e];
+    }
+    if (threadIdx.x == 0) {
+        offsets[E] = D + nk;
+        if (S) {
+            counts[E] = T;
+            offsets[E + 1] = D + nk + T;
+        }
+    }
+}
+
+// Rows of dispatch block blk under the capacity: a slot's rank among its expert's slots is
+// the block's first rank plus the lanes below it (lane masks, as scatter_block).
+__device__ __forceinline__ void scatter_cap_block(const int32_t *__restrict__ idx, int T, int k, int E, int blk, int cap,
+                                                  const int32_t *__restrict__ ranks,
+                                                  const int32_t *__restrict__ offsets,
+                                                  const int32_t *__restrict__ dbase,
+                                                  int32_t *__restrict__ slot_to_row,
+                                                  int32_t *__restrict__ row_to_slot, unsigned long long *masks) {
+    build_masks<false>(idx, T, k, E, blk, masks, nullptr);  // errors were reported by the count pass
+    const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+    const long t = (long)blk * kDispTok + tid;
+    if (tid >= kDispTok || t >= T) return;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int ids[kMaxChoices];
+    bool bad, dup;
+    const uint32_t ok = load_choices<false>(idx, t, k, E, ids, bad, dup);
+#pragma unroll
+    for (int j = 0; j < kMaxChoices; ++j) {
+        if (!(ok >> j & 1u)) continue;
+        const int e = ids[j];
+        int rank = __popcll(masks[wave * E + e] & below);
+        for (int w = 0; w < wave; ++w) rank += __popcll(masks[w * E + e]);
+        rank += ranks[(long)blk * E + e];
+        const bool keep = rank < cap;
+        const int row = keep ? offsets[e] + rank : dbase[e] + (rank - cap);
+        slot_to_row[t * k + j] = keep ? row : -1;
+        row_to_slot[row] = (int32_t)(t * k + j);
+    }
+}
+
 // ---- FP8 activation stage: x (bf16) -> e4m3 codes + power-of-two scale per 1x128 ----
 //
 // 16 lanes own one 128-value block (8 values each, one 16-byte load); gid is the global

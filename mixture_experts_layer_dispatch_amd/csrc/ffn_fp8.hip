@@ -29,22 +29,23 @@ static hipError_t launch_fp8(const char *name, dim3 grid, const Fp8Args &a, hipS
 }
 
 // xcd_cus: CUs per XCD (one workgroup per CU), for the tail split
-template <bool SWIGLU>
+template <bool SWIGLU, bool GATHER>
 __global__ __launch_bounds__(512) void gemm_fp8_kernel8(Fp8Args a, int xcd_cus) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     int half;
     const int tile = pick_tile_split(blockIdx.x, a.tile_start[a.G], xcd_cus, half);
-    if (tile >= 0) fp8_tile8<SWIGLU ? 1 : 2, SWIGLU ? 8 : 4, SWIGLU, SWIGLU>(a, tile, lds, half);
+    if (tile >= 0) fp8_tile8<SWIGLU ? 1 : 2, SWIGLU ? 8 : 4, SWIGLU, GATHER>(a, tile, lds, half);
 }
 
-// 256 x 256 tiles: the 8-wave kernel (linear1 gathers its rows, linear2 does not).  ub: an
-// upper bound of the tile count; the grid adds the blocks of the tail split.
-template <bool SWIGLU>
+// 256 x 256 tiles: the 8-wave kernel (the layer's linear1 gathers its rows, linear2 does
+// not; rows that arrive grouped -- an expert-parallel receive buffer -- need no gather).
+// ub: an upper bound of the tile count; the grid adds the blocks of the tail split.
+template <bool SWIGLU, bool GATHER = SWIGLU>
 static hipError_t launch_fp8_8(const char *name, long ub, const Fp8Args &a, hipStream_t st) {
     constexpr size_t lds = fp8_tile8_lds();
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)gemm_fp8_kernel8<SWIGLU>,
+        hipError_t e = hipFuncSetAttribute((const void *)gemm_fp8_kernel8<SWIGLU, GATHER>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr = true;
@@ -52,7 +53,7 @@ static hipError_t launch_fp8_8(const char *name, long ub, const Fp8Args &a, hipS
     const int C = xcd_cus();
     if (C <= 0) return hipErrorInvalidDevice;
     const dim3 grid((unsigned)(8 * ((ub + 7) / 8 + C / 2)));
-    MOE_LAUNCH(name, gemm_fp8_kernel8<SWIGLU>, grid, dim3(512), lds, st, a, C);
+    MOE_LAUNCH(name, (gemm_fp8_kernel8<SWIGLU, GATHER>), grid, dim3(512), lds, st, a, C);
     return hipGetLastError();
 }
 
@@ -218,6 +219,128 @@ hipError_t launch_fp8_ffn(const Shape &s, const FfnPlan &p, const uint8_t *w1, c
     else if (p.bn2 == 256) e = launch_fp8<128, 256, 2, false, false>("linear2", grid_for(p.bm2, ntn2), a2, st);
     else if (p.bm2 == 256) e = launch_fp8<256, 128, 2, false, false>("linear2", grid_for(p.bm2, ntn2), a2, st);
     else e = launch_fp8<128, 128, 2, false, false>("linear2", grid_for(p.bm2, ntn2), a2, st);
+    return e;
+}
+
+// ---- grouped FP8 x FP4 FFN over rows that arrive grouped, and the dense GEMM ----------
+
+// offsets and tile plans of an expert-parallel rank's receive buffer: rows of local expert
+// e from source rank s are the block (e, s) of recv_counts [E, nsrc], expert-major.  The
+// cumulative offsets are clamped at the buffer's capacity (an overflow is a device error),
+// so no tile reaches past the buffer.  One workgroup.
+__global__ __launch_bounds__(256) void ep_plan_kernel(const int32_t *__restrict__ recv_counts, int E, int nsrc,
+                                                     long cap, int bm1, int ntn1, int bm2, int ntn2,
+                                                     int32_t *__restrict__ offsets, int32_t *__restrict__ ts1,
+                                                     int32_t *__restrict__ ts2, int32_t *err) {
+    __shared__ int32_t sh[2 * 1032 + 256];
+    if (threadIdx.x == 0) {
+        long run = 0;
+        bool over = false;
+        for (int e = 0; e < E; ++e) {
+            offsets[e] = (int32_t)run;
+            long n = 0;
+            for (int q = 0; q < nsrc; ++q) {
+                const int c = recv_counts[(long)e * nsrc + q];
+                n += c > 0 ? c : 0;
+                over |= c < 0;
+            }
+            run += n;
+            if (run > cap) {
+                run = cap;
+                over = true;
+            }
+        }
+        offsets[E] = (int32_t)run;
+        if (over) set_error(err, DEVERR_OVERFLOW);
+    }
+    __syncthreads();
+    tile_plan_block<false>(offsets, E, bm1, ntn1, bm2, ntn2, ts1, ts2, sh);
+}
+
+// the plan of one group of n rows (the dense GEMM, the shared expert of a shard)
+__global__ void one_group_plan_kernel(int32_t *__restrict__ plan, int n, int ntiles1, int ntiles2) {
+    if (threadIdx.x == 0) {
+        plan[0] = 0;
+        plan[1] = n;
+        plan[2] = 0;
+        plan[3] = ntiles1;
+        plan[4] = 0;
+        plan[5] = ntiles2;
+    }
+}
+
+// linear2-shaped GEMM over ungathered rows: y [*, N] bf16 = A [*, K] . B^T by tiles of the
+// plan (offsets, ts) over G groups, rows at most `rows`, N tiles of bn
+static hipError_t launch_fp8_plain(const char *name, const Fp8Args &a, long rows, int bm, int bn, hipStream_t st) {
+    const int G = a.G, ntn = a.Ntot / bn;
+    const long ub = ((rows + bm - 1) / bm + (G < rows ? G : rows)) * (long)ntn;
+    const bool small = rows * (long)a.K < (1L << 32);
+    if (bm == 256 && bn == 256 && small) return launch_fp8_8<false>(name, ub, a, st);
+    const dim3 grid((unsigned)((ub + 7) / 8 * 8));
+    if (bm == 256 && bn == 256) return launch_fp8<256, 256, 2, false, false>(name, grid, a, st);
+    if (bn == 256) return launch_fp8<128, 256, 2, false, false>(name, grid, a, st);
+    if (bm == 256) return launch_fp8<256, 128, 2, false, false>(name, grid, a, st);
+    return launch_fp8<128, 128, 2, false, false>(name, grid, a, st);
+}
+
+// linear1 + SwiGLU over ungathered rows (h codes and scales out)
+static hipError_t launch_fp8_swiglu_plain(const char *name, const Fp8Args &a, long rows, int bm, hipStream_t st) {
+    const int G = a.G, ntn = a.F / 128;
+    const long ub = ((rows + bm - 1) / bm + (G < rows ? G : rows)) * (long)ntn;
+    const bool small = rows * (long)a.K < (1L << 32);
+    if (bm == 256 && small) return launch_fp8_8<true, false>(name, ub, a, st);
+    const dim3 grid((unsigned)((ub + 7) / 8 * 8));
+    if (bm == 256) return launch_fp8<256, 256, 4, true, false>(name, grid, a, st);
+    return launch_fp8<128, 256, 4, true, false>(name, grid, a, st);
+}
+
+hipError_t launch_gemm_fp8_dense(long M, int N, int K, const uint8_t *a, const float *as, const uint8_t *b,
+                                 const uint8_t *bs, void *c, int32_t *plan, hipStream_t st) {
+    if (M == 0) return hipSuccess;
+    const int bm = M >= 160 ? 256 : 128, bn = N % 256 == 0 ? 256 : 128;
+    const long tiles = (M + bm - 1) / bm * (long)(N / bn);
+    MOE_LAUNCH("gemm_plan", one_group_plan_kernel, dim3(1), dim3(64), 0, st, plan, (int)M, (int)tiles, (int)tiles);
+    const Fp8Args g = {a, as, nullptr, b, bs, c, nullptr, plan, plan + 2, 0, 1, K, N, N, 1, 0};
+    return launch_fp8_plain("gemm_fp8_mxfp4", g, M, bm, bn, st);
+}
+
+// One expert-parallel rank: the E local experts over the receive buffer (rows grouped by
+// local expert, then by source rank), then the shared expert over the rank's own T tokens.
+// ws: plan ints (offsets [E + 1], ts1, ts2 [E + 1] each, then 6 for the shared group), h and
+// its scales for cap + S * T rows.
+hipError_t launch_ep_ffn(const Shape &s, int nsrc, const int32_t *recv_counts, long cap, const uint8_t *rq,
+                         const float *rs, const uint8_t *w1, const uint8_t *w1s, const uint8_t *w2,
+                         const uint8_t *w2s, void *y_recv, const uint8_t *xq, const float *xs, void *y_shared,
+                         int32_t *plan, uint8_t *h, float *hs, int32_t *err, hipStream_t st) {
+    const int E = s.E, d = s.d, F = s.F;
+    const int bm = cap >= 160L * E ? 256 : 128, bn2 = d % 256 == 0 ? 256 : 128;
+    const int ntn1 = F / 128, ntn2 = d / bn2;
+    int32_t *offs = plan, *ts1 = plan + (E + 1), *ts2 = plan + 2 * (E + 1), *p1 = plan + 3 * (E + 1);
+    hipError_t e = hipSuccess;
+    if (cap > 0) {
+        MOE_LAUNCH("ep_plan", ep_plan_kernel, dim3(1), dim3(256), 0, st, recv_counts, E, nsrc, cap, bm, ntn1, bm,
+                   ntn2, offs, ts1, ts2, err);
+        const Fp8Args a1 = {rq, rs, nullptr, w1, w1s, h, hs, offs, ts1, 0, 1, d, 2 * F, F, E, F};
+        const Fp8Args a2 = {h, hs, nullptr, w2, w2s, y_recv, nullptr, offs, ts2, 0, 1, F, d, d, E, F};
+        e = launch_fp8_swiglu_plain("linear1", a1, cap, bm, st);
+        if (e == hipSuccess) e = launch_fp8_plain("linear2", a2, cap, bm, bn2, st);
+        if (e != hipSuccess) return e;
+    }
+    if (s.S && s.T > 0) {
+        const long T = s.T;
+        const int bms = T >= 160 ? 256 : 128;
+        const long t1 = (T + bms - 1) / bms * (long)ntn1, t2 = (T + bms - 1) / bms * (long)ntn2;
+        MOE_LAUNCH("ep_plan", one_group_plan_kernel, dim3(1), dim3(64), 0, st, p1, (int)T, (int)t1, (int)t2);
+        const size_t g1 = (size_t)E * 2 * F, g2 = (size_t)E * d;  // rows of W1, W2 before the shared expert
+        uint8_t *hsh = h + (size_t)cap * F;
+        float *hssh = hs + (size_t)cap * (F / 128);
+        const Fp8Args a1 = {xq, xs, nullptr, w1 + g1 * (d / 2), w1s + g1 * (d / 32), hsh, hssh, p1, p1 + 2, 0, 1,
+                            d, 2 * F, F, 1, F};
+        const Fp8Args a2 = {hsh, hssh, nullptr, w2 + g2 * (F / 2), w2s + g2 * (F / 32), y_shared, nullptr, p1,
+                            p1 + 4, 0, 1, F, d, d, 1, F};
+        e = launch_fp8_swiglu_plain("linear1_shared", a1, T, bms, st);
+        if (e == hipSuccess) e = launch_fp8_plain("linear2_shared", a2, T, bms, bn2, st);
+    }
     return e;
 }
 

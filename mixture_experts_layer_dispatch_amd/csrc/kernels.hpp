@@ -42,6 +42,13 @@ hipError_t launch_dispatch(const Shape &s, const int32_t *idx, int32_t *blockcou
                            int32_t *offsets, int32_t *slot_to_row, int32_t *row_to_slot, int32_t *err,
                            const uint16_t *x, uint8_t *xq, float *xs, hipStream_t st);
 int dispatch_blocks(int T);
+// the capacity variant: at most cap slots per routed expert (dbase: E ints of scratch)
+hipError_t launch_dispatch_capacity(const Shape &s, const int32_t *idx, int cap, int32_t *blockcounts,
+                                    int32_t *counts, int32_t *dropped, int32_t *offsets, int32_t *dbase,
+                                    int32_t *slot_to_row, int32_t *row_to_slot, int32_t *err, const uint16_t *x,
+                                    uint8_t *xq, float *xs, hipStream_t st);
+// aux-loss-free bias update from routed per-expert counts
+hipError_t launch_bias_update(const int32_t *counts, int E, float *bias, float gamma, hipStream_t st);
 // stand-alone FP8 quantiser of fp32 (f32) or bf16 rows: nblocks 128-value blocks
 hipError_t launch_quant_e4m3(const void *in, bool f32, long nblocks, uint8_t *q, float *qs, hipStream_t st);
 int xcd_cus();  // CUs per XCD of the current device
@@ -61,6 +68,16 @@ hipError_t launch_ffn(const Shape &s, const FfnPlan &p, const void *w1, const vo
                       const void *w2s, const void *x, const uint8_t *xq, const float *xs, const int32_t *offsets,
                       const int32_t *row_to_slot, void *h, float *hs, void *y_perm, int32_t *tile_start,
                       float *upart, hipStream_t st);
+
+// dense FP8 x MXFP4 GEMM: c [M, N] bf16 = a [M, K] . b [N, K]^T; plan: 6 ints of scratch
+hipError_t launch_gemm_fp8_dense(long M, int N, int K, const uint8_t *a, const float *as, const uint8_t *b,
+                                 const uint8_t *bs, void *c, int32_t *plan, hipStream_t st);
+// one expert-parallel rank's experts over its receive buffer (s.E local experts, s.T own tokens
+// for the shared expert); plan: 3 (E + 1) + 6 ints; h, hs: (cap + S T) rows
+hipError_t launch_ep_ffn(const Shape &s, int nsrc, const int32_t *recv_counts, long cap, const uint8_t *rq,
+                         const float *rs, const uint8_t *w1, const uint8_t *w1s, const uint8_t *w2,
+                         const uint8_t *w2s, void *y_recv, const uint8_t *xq, const float *xs, void *y_shared,
+                         int32_t *plan, uint8_t *h, float *hs, int32_t *err, hipStream_t st);
 
 // combine
 hipError_t launch_combine(const Shape &s, const void *y_perm, const int32_t *slot_to_row, const float *gate,
