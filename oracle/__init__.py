@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-MODES = {"f32": 0, "bf16": 1, "fp8_mxfp4": 2}
+MODES = {"f32": 0, "bf16": 1, "fp8_mxfp4": 2, "fp8_fp8": 3}
 GATINGS = {"softmax": 0, "sigmoid": 1}
 STATUS = {0: "ok", 1: "expert index out of range", 2: "duplicate expert for a token",
           3: "non-finite selection key", 4: "bad shape"}

@@ -35,6 +35,9 @@
  *    scale per 1x128 block, 2^e with e the smallest integer such that
  *    amax <= 448 * 2^e; codes are round-to-nearest-even of v * 2^-e.
  *  - MXFP4 weights are dequantised exactly: e2m1 value * 2^(e8m0 - 127).
+ *  - FP8 e4m3 x e4m3 mode: weights are e4m3 codes with one power-of-two fp32 scale per
+ *    1x128 block along K (the activations' format), dequantised exactly; activations
+ *    and h are quantised as in the FP8 x MXFP4 mode.
  */
 #include <math.h>
 #include <pthread.h>
@@ -43,14 +46,14 @@
 #include <string.h>
 #include <unistd.h>
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8_MXFP4 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8_MXFP4 = 2, ORC_FP8_FP8 = 3 };
 enum { ORC_SOFTMAX = 0, ORC_SIGMOID = 1 };
 enum { ORC_OK = 0, ORC_BAD_INDEX = 1, ORC_DUP_INDEX = 2, ORC_NONFINITE = 3, ORC_SHAPE = 4 };
 
 typedef struct {
     int32_t T, d, E, k, F, S; /* tokens, width, routed experts, top-k, expert hidden, shared */
     int32_t gating;           /* ORC_SOFTMAX or ORC_SIGMOID */
-    int32_t mode;             /* ORC_F32, ORC_BF16, ORC_FP8_MXFP4 */
+    int32_t mode;             /* ORC_F32, ORC_BF16, ORC_FP8_MXFP4, ORC_FP8_FP8 */
 } oracle_cfg;
 
 /* ---- number formats --------------------------------------------------- */
@@ -334,6 +337,9 @@ static double weight(const oracle_cfg *c, const void *w, const void *ws, int g, 
     int64_t flat = ((int64_t)g * R + r) * K + i;
     if (c->mode == ORC_F32) return (double)((const float *)w)[flat];
     if (c->mode == ORC_BF16) return bf16_to_double(((const uint16_t *)w)[flat]);
+    if (c->mode == ORC_FP8_FP8) /* e4m3 code times its 1x128 block's fp32 scale */
+        return oracle_e4m3_decode(((const uint8_t *)w)[flat]) *
+               (double)((const float *)ws)[((int64_t)g * R + r) * (K / 128) + i / 128];
     uint8_t byte = ((const uint8_t *)w)[flat >> 1];
     uint8_t code = (flat & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
     uint8_t sc = ((const uint8_t *)ws)[((int64_t)g * R + r) * (K / 32) + i / 32];
@@ -357,7 +363,7 @@ void oracle_expert_row(const oracle_cfg *c, const oracle_weights *w, int g, cons
         h[f] = ug / (1.0 + exp(-ug)) * uu;
     }
     if (h_out) memcpy(h_out, h, sizeof(double) * F);
-    if (c->mode == ORC_FP8_MXFP4) {
+    if (c->mode == ORC_FP8_MXFP4 || c->mode == ORC_FP8_FP8) {
         float *hf = (float *)malloc(sizeof(float) * F);
         uint8_t *hc = (uint8_t *)malloc((size_t)F);
         float *hs = (float *)malloc(sizeof(float) * (F / 128));
@@ -462,7 +468,7 @@ int oracle_layer(const oracle_cfg *c, const void *x, const void *wr, const float
                  const float *gates_in, const int64_t *tokens, int64_t ntok, double *y, int32_t *idx_out,
                  float *gates_out, int nthreads) {
     if (c->k < 1 || c->k > c->E || c->k > 64) return ORC_SHAPE;
-    if (c->mode == ORC_FP8_MXFP4 && (c->d % 128 || c->F % 128)) return ORC_SHAPE;
+    if ((c->mode == ORC_FP8_MXFP4 || c->mode == ORC_FP8_FP8) && (c->d % 128 || c->F % 128)) return ORC_SHAPE;
     layer_ctx L = {c, x, wr, bias, {w1, w1s, w2, w2s}, idx_in, gates_in, tokens, y, idx_out, gates_out, ORC_OK, NULL};
     run_split(layer_range, &L, ntok, nthreads);
     return L.status;
@@ -479,7 +485,7 @@ int oracle_layer_dropping(const oracle_cfg *c, const void *x, const void *w1, co
                           const void *w2s, const int32_t *idx_in, const float *gates_in, const uint8_t *keep,
                           const int64_t *tokens, int64_t ntok, double *y, int nthreads) {
     if (c->k < 1 || c->k > c->E || c->k > 64 || !idx_in || !gates_in || !keep) return ORC_SHAPE;
-    if (c->mode == ORC_FP8_MXFP4 && (c->d % 128 || c->F % 128)) return ORC_SHAPE;
+    if ((c->mode == ORC_FP8_MXFP4 || c->mode == ORC_FP8_FP8) && (c->d % 128 || c->F % 128)) return ORC_SHAPE;
     layer_ctx L = {c, x, NULL, NULL, {w1, w1s, w2, w2s}, idx_in, gates_in, tokens, y, NULL, NULL, ORC_OK, keep};
     run_split(layer_range, &L, ntok, nthreads);
     return L.status;

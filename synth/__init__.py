@@ -13,6 +13,7 @@ Workloads (sizes from the pages' model shapes and per-rank batch sizes):
                      T in {512, 8192, 32768}
 * ``decode_fp8fp4``  the same layer and tensors (same seed), T in {1, 64}
 * ``dsv3_fp8fp4_zipf`` the same layer and tensors with sigmoid scores and the Zipf bias
+* ``dsv3_fp8fp8``    the same shape with FP8 e4m3 weights (1x128 power-of-two scales), T = 8192
 """
 from __future__ import annotations
 
@@ -154,7 +155,7 @@ def fp8_rows(seed, tid, rows, K, sigma, grid=None, row0=0):
 # workload definitions
 # ---------------------------------------------------------------------------
 
-MODE_F32, MODE_BF16, MODE_FP8 = "f32", "bf16", "fp8_mxfp4"
+MODE_F32, MODE_BF16, MODE_FP8, MODE_FP8X8 = "f32", "bf16", "fp8_mxfp4", "fp8_fp8"
 TID_X, TID_WR, TID_BIASPERM, TID_W1, TID_W2 = 1, 2, 3, 4, 5
 
 
@@ -189,6 +190,9 @@ WORKLOADS = {
                           zipf_alpha=0.25),
     "dsv3_fp8fp4": Workload("dsv3_fp8fp4", 1004, MODE_FP8, 8192, 7168, 256, 8, 2048, 1, "softmax",
                             t_values=(512, 8192, 32768)),
+    # the DeepSeek-V3 shape with FP8 e4m3 weights (1x128 power-of-two scales) as well
+    "dsv3_fp8fp8": Workload("dsv3_fp8fp8", 1006, MODE_FP8X8, 8192, 7168, 256, 8, 2048, 1, "softmax",
+                            t_values=(8192,)),
     # the same layer (same seed, so the same tensors) at decode batch sizes
     "decode_fp8fp4": Workload("decode_fp8fp4", 1004, MODE_FP8, 1, 7168, 256, 8, 2048, 1, "softmax",
                               t_values=(1, 64)),
@@ -215,6 +219,7 @@ def make_inputs(w: Workload, grid: bool = False, zero_gate: bool = False) -> dic
     f32 mode:  x, w_router, w1 [G,2F,d], w2 [G,d,F] as float32.
     bf16 mode: the same as uint16 bf16 bits.
     fp8 mode:  x, w_router bf16 bits; w1/w2 MXFP4 codes with w1_scale/w2_scale e8m0.
+    fp8_fp8:   x, w_router bf16 bits; w1/w2 e4m3 codes with fp32 scales per 1x128.
     grid=True draws small integers instead of normals, so every product sum is exact.
     """
     s, T, d, E, F, G = w.seed, w.T, w.d, w.E, w.F, w.G
@@ -234,6 +239,12 @@ def make_inputs(w: Workload, grid: bool = False, zero_gate: bool = False) -> dic
         else:
             out["w1"], out["w1_scale"] = mxfp4(s, TID_W1, G, 2 * F, d, 1.0 / math.sqrt(d))
             out["w2"], out["w2_scale"] = mxfp4(s, TID_W2, G, d, F, 1.0 / math.sqrt(F))
+    elif w.mode == MODE_FP8X8:
+        g = (-2, 2) if grid else None
+        c1, s1 = fp8_rows(s, TID_W1, G * 2 * F, d, 1.0 / math.sqrt(d), grid=g)
+        c2, s2 = fp8_rows(s, TID_W2, G * d, F, 1.0 / math.sqrt(F), grid=g)
+        out["w1"], out["w1_scale"] = c1.reshape(G, 2 * F, d), s1.reshape(G, 2 * F, d // 128)
+        out["w2"], out["w2_scale"] = c2.reshape(G, d, F), s2.reshape(G, d, F // 128)
     else:
         if grid:
             out["w1"] = intgrid(s, TID_W1, (G, 2 * F, d), -2, 2, act)
@@ -243,10 +254,7 @@ def make_inputs(w: Workload, grid: bool = False, zero_gate: bool = False) -> dic
             out["w2"] = normal(s, TID_W2, (G, d, F), 1.0 / math.sqrt(F), act)
         out["w1_scale"] = out["w2_scale"] = None
     if zero_gate:
-        if w.mode == MODE_FP8:
-            out["w1"][:, :F, :] = 0
-        else:
-            out["w1"][:, :F, :] = 0
+        out["w1"][:, :F, :] = 0
     return out
 
 

@@ -646,3 +646,46 @@ def test_dense_fp8_mxfp4_gemm():
     want = synth.intgrid(3, 3, (5, 128), -3, 3).astype(np.int64) @ \
         synth.intgrid(3, 4, (16, 128), -2, 2).astype(np.int64).T
     np.testing.assert_array_equal(oracle.gemm_fp8_mxfp4(gi, gs, wb[0], ws_[0]), want.astype(np.float64))
+
+
+def test_fp8_fp8_expert_matches_independent_dequantised_ffn():
+    """FP8 e4m3 x e4m3 expert: torch fp64 matmuls on operands dequantised with torch's float8
+    decode times the 1x128 scales; activations and h through torch's float8 cast of v / 2^e."""
+    w = Workload("fp8x8", 42, "fp8_fp8", 4, 256, 2, 1, 256, 1, "softmax")
+    inp = synth.make_inputs(w)
+
+    def deq(codes, scales):
+        return torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy() * \
+            np.repeat(scales.astype(np.float64), 128, axis=-1)
+
+    def q_torch(v):
+        v = np.asarray(v, np.float32).reshape(-1, 128)
+        amax = np.abs(v).max(1).astype(np.float64)
+        e = np.array([oracle.e4m3_block_exponent(float(a)) for a in amax])
+        sc = np.exp2(e)
+        c = torch.from_numpy((v / sc[:, None]).astype(np.float32)).to(torch.float8_e4m3fn)
+        return (c.to(torch.float64).numpy() * sc[:, None]).reshape(-1)
+
+    idx = np.zeros((w.T, 1), np.int32)
+    idx[1::2] = 1
+    gates = np.ones((w.T, 1), np.float32)
+    y, _, _ = oracle.layer(inp, idx=idx, gates=gates)
+    F = w.F
+    for t in range(w.T):
+        xq = q_torch(synth.bf16_to_f32(inp["x"][t]))
+        out = np.zeros(w.d)
+        for g in (int(idx[t, 0]), w.E):
+            W1 = deq(inp["w1"][g], inp["w1_scale"][g])
+            W2 = deq(inp["w2"][g], inp["w2_scale"][g])
+            u = torch.from_numpy(W1) @ torch.from_numpy(xq)
+            h = (torch.nn.functional.silu(u[:F]) * u[F:]).numpy()
+            out += W2 @ q_torch(h.astype(np.float32))
+        np.testing.assert_allclose(y[t], out, rtol=1e-10, atol=1e-12)
+    # integer-grid e4m3 weights (scale 1) and integer activations: exact pre-activations
+    g = synth.make_inputs(w, grid=True)
+    xin = oracle.input_rows(g, [0])
+    _, h = oracle.expert_rows(g, 0, xin, want_h=True)
+    W1 = synth.intgrid(w.seed, synth.TID_W1, (w.G * 2 * F, w.d), -2, 2).reshape(w.G, 2 * F, w.d)[0]
+    u = W1.astype(np.float64) @ xin[0]
+    assert np.all(u == np.round(u))  # integer pre-activations, exact in fp64
+    np.testing.assert_allclose(h[0], u[:F] / (1.0 + np.exp(-u[:F])) * u[F:], rtol=1e-15, atol=0)
