@@ -69,8 +69,11 @@ typedef enum {
  *                      scale byte per 32 consecutive K.  Both linears are FP8 x FP4
  *                      (Mega MoE blog, donniechu.com, spec table), fp32
  *                      accumulation; y_perm bf16.
+ *  MOE_MODE_FP8_FP8:   as MOE_MODE_FP8_MXFP4, with FP8 weights as well: W1, W2 are e4m3
+ *                      codes, one byte each, with one power-of-two fp32 scale per 1x128
+ *                      block along K (the activations' format).  Both linears e4m3 x e4m3.
  */
-typedef enum { MOE_MODE_F32 = 0, MOE_MODE_BF16 = 1, MOE_MODE_FP8_MXFP4 = 2 } moe_mode;
+typedef enum { MOE_MODE_F32 = 0, MOE_MODE_BF16 = 1, MOE_MODE_FP8_MXFP4 = 2, MOE_MODE_FP8_FP8 = 3 } moe_mode;
 
 /*
  * Gating (MoE lesson "Build it, Step 1: router" and "Load balancing"; the
@@ -105,6 +108,8 @@ typedef struct {
  *  fp32 / bf16 modes: values; w1_scale = w2_scale = NULL.
  *  FP8 x MXFP4 mode:  w1 [G, 2F, d/2] and w2 [G, d, F/2] bytes of e2m1 codes;
  *                     w1_scale [G, 2F, d/32], w2_scale [G, d, F/32] e8m0 bytes.
+ *  FP8 x FP8 mode:    w1 [G, 2F, d] and w2 [G, d, F] e4m3 codes; w1_scale [G, 2F, d/128],
+ *                     w2_scale [G, d, F/128] fp32 powers of two.
  */
 typedef struct {
     const void *w1, *w1_scale, *w2, *w2_scale;

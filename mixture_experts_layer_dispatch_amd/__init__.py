@@ -20,7 +20,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-MODES = {"f32": 0, "bf16": 1, "fp8_mxfp4": 2}
+MODES = {"f32": 0, "bf16": 1, "fp8_mxfp4": 2, "fp8_fp8": 3}
+FP8_ACT = ("fp8_mxfp4", "fp8_fp8")  # modes that quantise x and h to e4m3 in-layer
 GATINGS = {"softmax": 0, "sigmoid": 1}
 DEVERR = {0: "none", 1: "expert index out of range", 2: "duplicate expert in a token",
           3: "non-finite selection key", 4: "bounded wait expired"}
@@ -239,7 +240,7 @@ def dispatch(cfg: Config, topk_idx, x=None, *, ws, out=None, stream=None):
     o.setdefault("offsets", torch.empty(cfg.G + 1, dtype=torch.int32, device=dev))
     o.setdefault("slot_to_row", torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev))
     o.setdefault("row_to_slot", torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev))
-    if cfg.mode == "fp8_mxfp4":
+    if cfg.mode in FP8_ACT:
         _expect(x, (cfg.T, cfg.d), torch.bfloat16, "x")
         o.setdefault("xq", torch.empty(cfg.T, cfg.d, dtype=torch.uint8, device=dev))
         o.setdefault("xq_scale", torch.empty(cfg.T, cfg.d // 128, dtype=torch.float32, device=dev))
@@ -269,7 +270,7 @@ def dispatch_capacity(cfg: Config, topk_idx, capacity: int, x=None, *, ws, out=N
     o.setdefault("offsets", torch.empty(cfg.G + 1, dtype=torch.int32, device=dev))
     o.setdefault("slot_to_row", torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev))
     o.setdefault("row_to_slot", torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev))
-    if cfg.mode == "fp8_mxfp4":
+    if cfg.mode in FP8_ACT:
         _expect(x, (cfg.T, cfg.d), torch.bfloat16, "x")
         o.setdefault("xq", torch.empty(cfg.T, cfg.d, dtype=torch.uint8, device=dev))
         o.setdefault("xq_scale", torch.empty(cfg.T, cfg.d // 128, dtype=torch.float32, device=dev))
@@ -349,7 +350,7 @@ def dispatch_noalloc(cfg: Config, topk_idx, x=None, *, err=None, out=None, strea
     o.setdefault("offsets", torch.empty(cfg.G + 1, dtype=torch.int32, device=dev))
     o.setdefault("slot_to_row", torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev))
     o.setdefault("row_to_slot", torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev))
-    if cfg.mode == "fp8_mxfp4":
+    if cfg.mode in FP8_ACT:
         _expect(x, (cfg.T, cfg.d), torch.bfloat16, "x")
         o.setdefault("xq", torch.empty(cfg.T, cfg.d, dtype=torch.uint8, device=dev))
         o.setdefault("xq_scale", torch.empty(cfg.T, cfg.d // 128, dtype=torch.float32, device=dev))
@@ -386,6 +387,11 @@ def _weights(cfg: Config, w1, w2, w1_scale=None, w2_scale=None) -> MoeWeights:
         _expect(w2, (G, d, F // 2), torch.uint8, "w2")
         _expect(w1_scale, (G, 2 * F, d // 32), torch.uint8, "w1_scale")
         _expect(w2_scale, (G, d, F // 32), torch.uint8, "w2_scale")
+    elif cfg.mode == "fp8_fp8":
+        _expect(w1, (G, 2 * F, d), torch.uint8, "w1")
+        _expect(w2, (G, d, F), torch.uint8, "w2")
+        _expect(w1_scale, (G, 2 * F, d // 128), torch.float32, "w1_scale")
+        _expect(w2_scale, (G, d, F // 128), torch.float32, "w2_scale")
     else:
         _expect(w1, (G, 2 * F, d), act_dtype(cfg), "w1")
         _expect(w2, (G, d, F), act_dtype(cfg), "w2")
@@ -429,7 +435,7 @@ def layer_unfused(cfg: Config, x, w_router, w1, w2, w1_scale=None, w2_scale=None
     """route -> dispatch -> ffn -> combine as four library calls.  Returns (y, routing dict)."""
     idx, gate, _, _ = route(cfg, x, w_router, bias, ws=ws, stream=stream)
     dsp = dispatch(cfg, idx, x, ws=ws, stream=stream)
-    yp = ffn(cfg, w1, w2, w1_scale, w2_scale, x=x if cfg.mode != "fp8_mxfp4" else None, xq=dsp["xq"],
+    yp = ffn(cfg, w1, w2, w1_scale, w2_scale, x=x if cfg.mode not in FP8_ACT else None, xq=dsp["xq"],
              xq_scale=dsp["xq_scale"], offsets=dsp["offsets"], row_to_slot=dsp["row_to_slot"], ws=ws, stream=stream)
     y = combine(cfg, yp, dsp["slot_to_row"], gate, stream=stream)
     return y, dict(dsp, topk_idx=idx, topk_gate=gate, y_perm=yp)

@@ -14,9 +14,12 @@ namespace {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// FP8 activations (x and h quantised in-layer): the FP8 x MXFP4 and FP8 x FP8 modes
+bool fp8_mode(const moe_cfg *c) { return c->mode == MOE_MODE_FP8_MXFP4 || c->mode == MOE_MODE_FP8_FP8; }
+
 moe_status validate(const moe_cfg *c) {
     if (!c) return MOE_ERR_NULL;
-    if (c->mode < MOE_MODE_F32 || c->mode > MOE_MODE_FP8_MXFP4) return MOE_ERR_MODE;
+    if (c->mode < MOE_MODE_F32 || c->mode > MOE_MODE_FP8_FP8) return MOE_ERR_MODE;
     if (c->gating < MOE_GATE_SOFTMAX || c->gating > MOE_GATE_SIGMOID) return MOE_ERR_MODE;
     if (c->T < 0 || c->T > (1 << 20)) return MOE_ERR_SHAPE;
     if (c->E < 1 || c->E > 1024 || c->k < 1 || c->k > 16 || c->k > c->E) return MOE_ERR_SHAPE;
@@ -48,7 +51,7 @@ Layout layout_of(const moe_cfg *c) {
     };
     const size_t T = c->T, k = c->k, E = c->E, G = c->E + c->n_shared, d = c->d, F = c->F;
     const size_t rows = T * k + c->n_shared * T;
-    const bool fp8 = c->mode == MOE_MODE_FP8_MXFP4, f32 = c->mode == MOE_MODE_F32;
+    const bool fp8 = fp8_mode(c), f32 = c->mode == MOE_MODE_F32;
     L.err = take(256);  // sticky error word
     L.blockcounts = take((size_t)dispatch_blocks(c->T) * E * 4);
     L.dbase = take(E * 4);  // capacity variant: first dropped row per expert
@@ -158,7 +161,7 @@ moe_status moe_workspace_region(const moe_cfg *cfg, int32_t region, size_t *offs
     if (!offset || !bytes) return MOE_ERR_NULL;
     const Layout L = layout_of(cfg);
     const size_t rows = (size_t)cfg->T * cfg->k + (size_t)cfg->n_shared * cfg->T;
-    const bool fp8 = cfg->mode == MOE_MODE_FP8_MXFP4, f32 = cfg->mode == MOE_MODE_F32;
+    const bool fp8 = fp8_mode(cfg), f32 = cfg->mode == MOE_MODE_F32;
     switch (region) {
         case MOE_WS_ERROR: *offset = L.err; *bytes = 256; return MOE_OK;
         case MOE_WS_H: *offset = L.h; *bytes = rows * cfg->F * (f32 ? 4 : fp8 ? 1 : 2); return MOE_OK;
@@ -294,7 +297,7 @@ moe_status moe_dispatch(const moe_cfg *cfg, const int32_t *topk_idx, const void 
                         void *ws, size_t ws_bytes, hipStream_t stream) {
     MOE_TRY(validate(cfg));
     if (cfg->T == 0) return MOE_OK;
-    const bool fp8 = cfg->mode == MOE_MODE_FP8_MXFP4;
+    const bool fp8 = fp8_mode(cfg);
     if (!topk_idx || !counts || !offsets || !slot_to_row || !row_to_slot) return MOE_ERR_NULL;
     if (fp8 && (!x || !xq || !xq_scale)) return MOE_ERR_NULL;
     for (const void *p : {(const void *)topk_idx, x, (const void *)counts, (const void *)offsets,
@@ -318,7 +321,7 @@ moe_status moe_dispatch_capacity(const moe_cfg *cfg, const int32_t *topk_idx, co
     MOE_TRY(validate(cfg));
     if (capacity < 0) return MOE_ERR_SHAPE;
     if (cfg->T == 0) return MOE_OK;
-    const bool fp8 = cfg->mode == MOE_MODE_FP8_MXFP4;
+    const bool fp8 = fp8_mode(cfg);
     if (!topk_idx || !counts || !dropped || !offsets || !slot_to_row || !row_to_slot) return MOE_ERR_NULL;
     if (fp8 && (!x || !xq || !xq_scale)) return MOE_ERR_NULL;
     for (const void *p : {(const void *)topk_idx, x, (const void *)counts, (const void *)dropped,
@@ -348,7 +351,7 @@ moe_status moe_ffn(const moe_cfg *cfg, const moe_weights *w, const void *x, cons
                    hipStream_t stream) {
     MOE_TRY(validate(cfg));
     if (cfg->T == 0) return MOE_OK;
-    const bool fp8 = cfg->mode == MOE_MODE_FP8_MXFP4;
+    const bool fp8 = fp8_mode(cfg);
     if (!w || !w->w1 || !w->w2 || !offsets || !row_to_slot || !y_perm) return MOE_ERR_NULL;
     if (fp8 && (!w->w1_scale || !w->w2_scale || !xq || !xq_scale)) return MOE_ERR_NULL;
     if (!fp8 && !x) return MOE_ERR_NULL;
@@ -380,7 +383,7 @@ moe_status moe_layer_fused(const moe_cfg *cfg, const moe_weights *w, const void 
                            int32_t *counts_out, void *ws, size_t ws_bytes, hipStream_t stream) {
     MOE_TRY(validate(cfg));
     if (cfg->T == 0) return MOE_OK;
-    const bool fp8 = cfg->mode == MOE_MODE_FP8_MXFP4;
+    const bool fp8 = fp8_mode(cfg);
     if (!w || !w->w1 || !w->w2 || !x || !w_router || !y) return MOE_ERR_NULL;
     if (fp8 && (!w->w1_scale || !w->w2_scale)) return MOE_ERR_NULL;
     for (const void *p : {w->w1, w->w2, w->w1_scale, w->w2_scale, x, w_router, (const void *)bias, (const void *)y,

@@ -14,7 +14,9 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-enum Mode { MODE_F32 = 0, MODE_BF16 = 1, MODE_FP8 = 2 };
+// MODE_FP8: FP8 e4m3 activations x MXFP4 weights; MODE_FP8X8: e4m3 x e4m3 (1x128 scales)
+enum Mode { MODE_F32 = 0, MODE_BF16 = 1, MODE_FP8 = 2, MODE_FP8X8 = 3 };
+__host__ __device__ inline bool fp8_act(int mode) { return mode == MODE_FP8 || mode == MODE_FP8X8; }
 enum Gating { GATE_SOFTMAX = 0, GATE_SIGMOID = 1 };
 enum DevErr {
     DEVERR_NONE = 0,

@@ -71,6 +71,14 @@ FfnPlan ffn_plan(const Shape &s) {
         return p;
     }
     p.ks = 1;
+    if (s.mode == MODE_FP8X8) {  // the 4-wave FP8 x FP8 tiles: 128 x 256 (linear1), 128 x 128
+        p.bm1 = p.bm2 = 128;
+        p.bn1 = 256;
+        p.bn2 = 128;
+        p.ntn1 = s.F / 128;
+        p.ntn2 = s.d / 128;
+        return p;
+    }
     p.bm1 = p.bm2 = per_group >= 160 ? 256 : 128;
     p.bn1 = 256;
     p.bn2 = s.d % 256 == 0 ? 256 : 128;
@@ -135,6 +143,11 @@ hipError_t launch_fp8_ffn(const Shape &s, const FfnPlan &p, const uint8_t *w1, c
                           const int32_t *offsets, const int32_t *row_to_slot, uint8_t *h, float *hs, void *y_perm,
                           const int32_t *ts1, const int32_t *ts2, float *upart, hipStream_t st);
 
+hipError_t launch_fp8x8_ffn(const Shape &s, const FfnPlan &p, const uint8_t *w1, const float *w1s, const uint8_t *w2,
+                            const float *w2s, const uint8_t *xq, const float *xs, const int32_t *offsets,
+                            const int32_t *row_to_slot, uint8_t *h, float *hs, void *y_perm, const int32_t *ts1,
+                            const int32_t *ts2, hipStream_t st);
+
 hipError_t launch_ffn(const Shape &s, const FfnPlan &p, const void *w1, const void *w1s, const void *w2,
                       const void *w2s, const void *x, const uint8_t *xq, const float *xs, const int32_t *offsets,
                       const int32_t *row_to_slot, void *h, float *hs, void *y_perm, int32_t *tile_start,
@@ -155,6 +168,9 @@ hipError_t launch_ffn(const Shape &s, const FfnPlan &p, const void *w1, const vo
     if (!(s.mode == MODE_FP8 && fp8_gemv_ok(s, p)))
         MOE_LAUNCH("tile_plan", tile_plan_kernel, dim3(1), dim3(256), 0, st, offsets, G, p.bm1, ntn1, p.bm2, ntn2, ts1,
                    ts2);
+    if (s.mode == MODE_FP8X8)
+        return launch_fp8x8_ffn(s, p, (const uint8_t *)w1, (const float *)w1s, (const uint8_t *)w2, (const float *)w2s,
+                                xq, xs, offsets, row_to_slot, (uint8_t *)h, hs, y_perm, ts1, ts2, st);
     if (s.mode == MODE_FP8)
         return launch_fp8_ffn(s, p, (const uint8_t *)w1, (const uint8_t *)w1s, (const uint8_t *)w2,
                               (const uint8_t *)w2s, xq, xs, offsets, row_to_slot, (uint8_t *)h, hs, y_perm, ts1, ts2,

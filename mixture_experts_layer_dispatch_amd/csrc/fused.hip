@@ -12,6 +12,7 @@ namespace moe {
 hipError_t launch_fused_bf16(FusedArgs &a, int bm, int bn2, size_t lds, int cu_limit, hipStream_t st);
 hipError_t launch_fused_fp8(FusedArgs &a, bool decode, int bm, int bn2, bool w8, size_t lds, int cu_limit,
                             hipStream_t st);
+hipError_t launch_fused_fp8x8(FusedArgs &a, size_t lds, int cu_limit, hipStream_t st);
 
 namespace {
 
@@ -40,6 +41,7 @@ bool fused_w8(const Shape &s, const FfnPlan &p) {
 
 size_t gemm_lds(const Shape &s, const FfnPlan &p) {
     if (s.mode == MODE_F32 || p.decode) return 0;
+    if (s.mode == MODE_FP8X8) return fp8x8_tile_lds<256>();
     const bool b256 = p.bm1 == 256, n256 = p.bn2 == 256;
     if (b256 && n256 && s.mode == MODE_BF16) return bf16_tile8_lds();
     if (b256 && n256 && fp8_w8(s)) return fp8_tile8_lds();
@@ -119,7 +121,7 @@ hipError_t launch_layer_fused(const Shape &s, const FfnPlan &p, FusedArgs &a, in
     a.ks = p.ks;
     a.rows = s.rows();
     a.nm = fused_row_tiles(s, p);
-    const long lanes_q = s.mode == MODE_FP8 ? (long)s.T * (s.d / 128) * 16 : 0;
+    const long lanes_q = fp8_act(s.mode) ? (long)s.T * (s.d / 128) * 16 : 0;
     const long nq = (lanes_q + 1023) / 1024;
     long nr;
     switch (a.router) {
@@ -145,6 +147,7 @@ hipError_t launch_layer_fused(const Shape &s, const FfnPlan &p, FusedArgs &a, in
     const size_t lds = fused_lds_bytes(s, p);
     if (s.mode == MODE_F32) return launch_fused_kernel<MODE_F32, 128, 128>(a, lds, cu_limit, st);
     if (s.mode == MODE_BF16) return launch_fused_bf16(a, p.bm1, p.bn2, lds, cu_limit, st);
+    if (s.mode == MODE_FP8X8) return launch_fused_fp8x8(a, lds, cu_limit, st);
     return launch_fused_fp8(a, p.decode, p.bm1, p.bn2, fp8_w8(s), lds, cu_limit, st);
 }
 

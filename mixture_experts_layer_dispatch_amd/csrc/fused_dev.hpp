@@ -40,6 +40,7 @@
 #include "dispatch_dev.hpp"
 #include "gemm_bf16_dev.hpp"
 #include "gemm_fp8_dev.hpp"
+#include "gemm_fp8x8_dev.hpp"
 #include "kernels.hpp"
 #include "route_dev.hpp"
 
@@ -493,6 +494,10 @@ __device__ __forceinline__ void fused_tiled(const FusedArgs &a, uint8_t *lds) {
                     GemmArgs g = {(const uint16_t *)a.x, a.r2s, (const uint16_t *)a.w1, (uint16_t *)a.h, a.offsets,
                                   a.ts1, a.T, a.k, a.d, 2 * a.F, a.F, a.G, a.F};
                     bf16_tile<BM, 256, true, true>(g, tile, lds);
+                } else if constexpr (MODE == MODE_FP8X8) {
+                    Fp8Args g = {a.xq, a.xs, a.r2s, (const uint8_t *)a.w1, (const uint8_t *)a.w1s, a.h, a.hs,
+                                 a.offsets, a.ts1, a.T, a.k, a.d, 2 * a.F, a.F, a.G, a.F};
+                    fp8x8_tile<true, true, 256>(g, tile, lds);
                 } else {
                     Fp8Args g = {a.xq, a.xs, a.r2s, (const uint8_t *)a.w1, (const uint8_t *)a.w1s, a.h, a.hs,
                                  a.offsets, a.ts1, a.T, a.k, a.d, 2 * a.F, a.F, a.G, a.F};
@@ -520,6 +525,10 @@ __device__ __forceinline__ void fused_tiled(const FusedArgs &a, uint8_t *lds) {
                     GemmArgs g = {(const uint16_t *)a.h, nullptr, (const uint16_t *)a.w2, (uint16_t *)a.yperm,
                                   a.offsets, a.ts2, a.T, a.k, a.F, a.d, a.d, a.G, a.F};
                     bf16_tile<BM, BN2, false, false>(g, tile, lds);
+                } else if constexpr (MODE == MODE_FP8X8) {
+                    Fp8Args g = {(const uint8_t *)a.h, a.hs, nullptr, (const uint8_t *)a.w2, (const uint8_t *)a.w2s,
+                                 a.yperm, nullptr, a.offsets, a.ts2, a.T, a.k, a.F, a.d, a.d, a.G, a.F};
+                    fp8x8_tile<false, false, 128>(g, tile, lds);
                 } else {
                     Fp8Args g = {(const uint8_t *)a.h, a.hs, nullptr, (const uint8_t *)a.w2, (const uint8_t *)a.w2s,
                                  a.yperm, nullptr, a.offsets, a.ts2, a.T, a.k, a.F, a.d, a.d, a.G, a.F};

@@ -1,4 +1,4 @@
-// Persistent layer kernel, FP8 x MXFP4 instantiations (tiled and decode).
+// Persistent layer kernel, FP8 x MXFP4 instantiations (tiled and decode) and the FP8 x FP8 one.
 #include "fused_dev.hpp"
 
 namespace moe {
@@ -12,6 +12,11 @@ hipError_t launch_fused_fp8(FusedArgs &a, bool decode, int bm, int bn2, bool w8,
     if (bm == 256) return launch_fused_kernel<MODE_FP8, 256, 128>(a, lds, cu_limit, st);
     if (bn2 == 256) return launch_fused_kernel<MODE_FP8, 128, 256>(a, lds, cu_limit, st);
     return launch_fused_kernel<MODE_FP8, 128, 128>(a, lds, cu_limit, st);
+}
+
+// FP8 x FP8: the 256-thread kernel with the 128-row FP8 x FP8 tiles
+hipError_t launch_fused_fp8x8(FusedArgs &a, size_t lds, int cu_limit, hipStream_t st) {
+    return launch_fused_kernel<MODE_FP8X8, 128, 128>(a, lds, cu_limit, st);
 }
 
 }  // namespace moe

@@ -49,13 +49,13 @@ extern "C" moe_status moe_dispatch_noalloc(const moe_cfg *cfg, const int32_t *to
     // shape and mode checks of moe_dispatch (a zero-sized workspace query fails on a bad cfg)
     if (!cfg) return MOE_ERR_NULL;
     if (moe_workspace_bytes(cfg) == 0) {
-        if (cfg->mode < MOE_MODE_F32 || cfg->mode > MOE_MODE_FP8_MXFP4 || cfg->gating < MOE_GATE_SOFTMAX ||
+        if (cfg->mode < MOE_MODE_F32 || cfg->mode > MOE_MODE_FP8_FP8 || cfg->gating < MOE_GATE_SOFTMAX ||
             cfg->gating > MOE_GATE_SIGMOID)
             return MOE_ERR_MODE;
         return MOE_ERR_SHAPE;
     }
     if (cfg->T == 0) return MOE_OK;
-    const bool fp8 = cfg->mode == MOE_MODE_FP8_MXFP4;
+    const bool fp8 = cfg->mode == MOE_MODE_FP8_MXFP4 || cfg->mode == MOE_MODE_FP8_FP8;
     if (!topk_idx || !counts || !offsets || !slot_to_row || !row_to_slot) return MOE_ERR_NULL;
     if (fp8 && (!x || !xq || !xq_scale)) return MOE_ERR_NULL;
     for (const void *p : {(const void *)topk_idx, x, (const void *)counts, (const void *)offsets,

@@ -13,7 +13,8 @@ import oracle
 import synth
 from synth import Workload
 
-TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8_mxfp4": 1e-2}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8_mxfp4": 1e-2, "fp8_fp8": 1e-2}
+FP8 = ("fp8_mxfp4", "fp8_fp8")  # modes with FP8 e4m3 activations (x and h quantised in-layer)
 
 
 def log(msg: str):
@@ -37,7 +38,7 @@ def to_dev(a, kind: str, device="cuda"):
 def upload(inp: dict) -> dict:
     w = inp["workload"]
     act = "f32" if w.mode == "f32" else "bf16"
-    wk = "u8" if w.mode == "fp8_mxfp4" else act
+    wk = "u8" if w.mode in FP8 else act
     return {
         "x": to_dev(inp["x"], act),
         "w_router": to_dev(inp["w_router"], act),
@@ -137,7 +138,7 @@ def check_outputs(w: Workload, inp: dict, y, idx, gate, tokens, tol=None, nthrea
     err = rel_l2(y_gpu, y_ref)
     assert np.all(np.isfinite(y_gpu)), "non-finite GPU output"
     assert err <= tol, f"output rel L2 {err:.3e} > {tol:.1e}"
-    if w.mode != "fp8_mxfp4":
+    if w.mode not in FP8:
         # every token on its own as well (a token's output depends only on its row and the
         # weights); in FP8 mode a token's h codes may sit one step apart at a rounding midpoint,
         # which moves a single token by up to about 1e-2 at small F, so there the per-token check
@@ -217,7 +218,7 @@ def check_rows(w: Workload, inp: dict, dsp: dict, y_perm, rows: np.ndarray, ws=N
     r2s = dsp["row_to_slot"].cpu().numpy()
     groups = row_groups(offs, rows)
     toks = row_tokens(w, r2s, rows)
-    fp8 = w.mode == "fp8_mxfp4"
+    fp8 = w.mode in FP8
     ref, h = oracle_rows(inp, groups, toks, want_h=fp8)
     got = to_f64(y_perm[torch.from_numpy(rows).to(y_perm.device)])
     assert np.all(np.isfinite(got)), "non-finite expert output"

@@ -15,7 +15,7 @@ import mixture_experts_layer_dispatch_amd as moe
 import oracle
 import synth
 from synth import WORKLOADS, Workload
-from moe_testlib import (TOL, cfg_of, check_dispatch, check_outputs, check_routing, check_rows, check_tokens_fp8,
+from moe_testlib import (FP8, TOL, cfg_of, check_dispatch, check_outputs, check_routing, check_rows, check_tokens_fp8,
                          check_xq, cover_rows, log, rel_l2, sample_tokens, to_dev, to_f64, upload)
 
 pytestmark = pytest.mark.gpu
@@ -48,6 +48,12 @@ SMALL = {
     # router, FP8 x FP4 with the tiled router
     "bf16_w8": Workload("bf16_w8", 2014, "bf16", 1024, 256, 8, 2, 256, 0, "softmax"),
     "fp8_w8_tiled_router": Workload("fp8_w8_tiled_router", 2015, "fp8_mxfp4", 5120, 256, 256, 8, 256, 1, "softmax"),
+    # FP8 e4m3 x e4m3: 128-row tiles, ragged groups, 128- and 256-column tiles, decode sizes
+    "fp8x8_softmax_shared": Workload("fp8x8_softmax_shared", 2016, "fp8_fp8", 150, 512, 32, 4, 256, 1, "softmax"),
+    "fp8x8_sigmoid_zipf": Workload("fp8x8_sigmoid_zipf", 2017, "fp8_fp8", 300, 256, 64, 8, 384, 1, "sigmoid",
+                                   zipf_alpha=0.25),
+    "fp8x8_decode_3": Workload("fp8x8_decode_3", 2018, "fp8_fp8", 3, 384, 16, 4, 128, 1, "softmax"),
+    "fp8x8_large_groups": Workload("fp8x8_large_groups", 2019, "fp8_fp8", 1200, 256, 8, 2, 256, 0, "softmax"),
 }
 
 
@@ -56,7 +62,7 @@ def run_unfused(w, d, T=None):
     ws = moe.alloc_workspace(cfg)
     idx, gate, logits, keys = moe.route(cfg, d["x"], d["w_router"], d["bias"], ws=ws, want_logits=True)
     dsp = moe.dispatch(cfg, idx, d["x"], ws=ws)
-    yp = moe.ffn(cfg, d["w1"], d["w2"], d["w1_scale"], d["w2_scale"], x=None if w.mode == "fp8_mxfp4" else d["x"],
+    yp = moe.ffn(cfg, d["w1"], d["w2"], d["w1_scale"], d["w2_scale"], x=None if w.mode in FP8 else d["x"],
                  xq=dsp["xq"], xq_scale=dsp["xq_scale"], offsets=dsp["offsets"], row_to_slot=dsp["row_to_slot"],
                  ws=ws)
     y = moe.combine(cfg, yp, dsp["slot_to_row"], gate)
@@ -85,12 +91,12 @@ def test_small_layer_parity(name):
     cfg, ws, r = run_unfused(w, d)
     near = check_routing(w, inp, r["idx"], r["gate"], r["logits"], r["keys"])
     check_dispatch(w, r["idx"], r["dsp"])
-    if w.mode == "fp8_mxfp4":
+    if w.mode in FP8:
         check_xq(w, inp, r["dsp"]["xq"], r["dsp"]["xq_scale"])
     err = check_outputs(w, inp, r["y"], r["idx"], r["gate"], np.arange(w.T))
     # every expert output row, and in FP8 mode every row's h codes and scales
     check_rows(w, inp, r["dsp"], r["y_perm"], np.arange(w.T * (w.k + w.S)), ws=ws, cfg=cfg)
-    if w.mode == "fp8_mxfp4":
+    if w.mode in FP8:
         check_tokens_fp8(w, inp, r["y"], r["dsp"], r["gate"], ws, cfg, np.arange(w.T))
     # the fused entry point gives the same bits
     y2, idx2, gate2, counts2 = run_fused(w, d, cfg, ws)
@@ -105,7 +111,7 @@ def test_small_layer_parity(name):
 
 
 @pytest.mark.parametrize("name", ["bf16_sigmoid_shared", "f32_sigmoid_shared", "fp8_softmax_shared", "fp8_decode_5",
-                                  "bf16_w8", "fp8_w8_tiled_router"])
+                                  "bf16_w8", "fp8_w8_tiled_router", "fp8x8_sigmoid_zipf"])
 def test_fused_grid_sizes_and_repeats(name):
     """The persistent kernel gives the unfused bits on a full grid, on 8 CUs and on 3 CUs
     (many items per workgroup), call after call (each launch leaves its counters clean for
@@ -225,7 +231,7 @@ def _full_inputs(name):
 
 
 FULL = [("mixtral_bf16", 4096), ("dsv3_bf16", 8192), ("dsv3_fp8fp4", 512), ("dsv3_fp8fp4", 8192),
-        ("dsv3_fp8fp4", 32768), ("decode_fp8fp4", 1), ("decode_fp8fp4", 64)]
+        ("dsv3_fp8fp4", 32768), ("decode_fp8fp4", 1), ("decode_fp8fp4", 64), ("dsv3_fp8fp8", 8192)]
 
 
 @pytest.mark.slow
@@ -241,7 +247,7 @@ def test_full_size_parity(name, T):
     near = check_routing(w, inp, r["idx"], r["gate"], r["logits"], r["keys"])
     check_dispatch(w, r["idx"], r["dsp"])
     toks = sample_tokens(T, 48, seed=T)
-    if w.mode == "fp8_mxfp4":
+    if w.mode in FP8:
         check_xq(w, inp, r["dsp"]["xq"], r["dsp"]["xq_scale"], tokens=toks)
     log(f"oracle on {len(toks)} sampled tokens")
     err = check_outputs(w, inp, r["y"], r["idx"], r["gate"], toks)
@@ -251,7 +257,7 @@ def test_full_size_parity(name, T):
     log(f"oracle on {rows.size} rows covering every 128-row block of every group")
     agg, worst, mism = check_rows(w, inp, r["dsp"], r["y_perm"], rows, ws=ws, cfg=cfg)
     log(f"rows: rel L2 {agg:.2e}, worst row {worst:.2e}, h code mismatches {mism}")
-    if w.mode == "fp8_mxfp4":
+    if w.mode in FP8:
         check_tokens_fp8(w, inp, r["y"], r["dsp"], r["gate"], ws, cfg, toks)
     y2, idx2, _, _ = run_fused(w, d, cfg, ws)
     assert torch.equal(idx2, r["idx"])
