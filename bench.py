@@ -10,10 +10,12 @@ With no workload named, the reported line is the DeepSeek-V3-shaped FP8 e4m3 x M
 layer at T = 32768 tokens (the largest per-rank batch on the pages), and a `sweep` key in
 the same line carries every other workload: the tiny fp32 layer (T = 64), the
 Mixtral-shaped bf16 layer (T = 4096), the DeepSeek-V3-shaped bf16 layer (T = 8192), the
-FP8 x MXFP4 layer at T = 512 and 8192 (and at 8192 with the sigmoid + Zipf-bias router),
-and decode at T = 1 and 64 (whose metric is HBM GB/s).  Every entry carries its own
-median / p10 / p90 step time, roofline of the dominant kernel, per-expert load
-statistics and CPU-oracle rate (all host cores and one thread).
+FP8 x MXFP4 layer at T = 512 and 8192 (and at 8192 with the sigmoid + Zipf-bias router,
+dropless and with a capacity factor of 1.25), decode at T = 1 and 64 (whose metric is HBM
+GB/s), the FP8 e4m3 x e4m3 layer at T = 8192, one expert-parallel rank's experts over the
+rows 8 ranks send it, and the dense FP8 x MXFP4 GEMM.  Every entry carries its own
+median / p10 / p90 step time, roofline of the dominant kernel, load statistics and
+CPU-oracle rate (all host cores and one thread).
 
 Both entry points compute the same layer: the persistent single-launch kernel
 (moe_layer_fused) and the chain of step kernels (route, dispatch, ffn, combine).  Both
@@ -38,24 +40,34 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK = {"bf16": 2500.0, "fp8_mxfp4": 5000.0, "f32": 157.3}  # dense TFLOP/s (MI355X spec)
+# dense TFLOP/s (MI355X spec); FP8 x MXFP4 issues at the FP8 rate on this MFMA (measured), so
+# both FP8 modes take the FP8 peak
+PEAK = {"bf16": 2500.0, "fp8_mxfp4": 5000.0, "fp8_fp8": 5000.0, "f32": 157.3}
 PEAK_HBM = 8000.0  # GB/s
 METRIC = "MoE-layer active TFLOPS & tokens/s at T=1..32768 (bf16, FP8×FP4); GB/s at T=1"
-DTYPE = {"f32": "f32", "bf16": "bf16", "fp8_mxfp4": "fp8e4m3 x mxfp4"}
+DTYPE = {"f32": "f32", "bf16": "bf16", "fp8_mxfp4": "fp8e4m3 x mxfp4", "fp8_fp8": "fp8e4m3 x fp8e4m3"}
+FP8 = ("fp8_mxfp4", "fp8_fp8")
 
-# (workload, T, CPU-oracle seconds on all cores, on one thread) of the default run, in
-# execution order: entries that share weights run together.  The first is the headline.
-HEADLINE = ("dsv3_fp8fp4", 32768)
+# Entries of the default run, in execution order (entries that share weights run together).
+# kind "layer": the whole layer on a workload at T tokens; "capacity": the same with the
+# capacity-factor dispatch; "ep": one expert-parallel rank's experts over its receive
+# buffer; "gemm": the dense FP8 x MXFP4 GEMM.  cpu / cpu1: CPU-oracle seconds on all host
+# cores and on one thread.  The first entry is the headline.
+HEADLINE = ("layer", "dsv3_fp8fp4", 32768)
 SWEEP = [
-    ("dsv3_fp8fp4", 32768, 12.0, 4.0),
-    ("dsv3_fp8fp4", 8192, 4.0, 2.0),
-    ("dsv3_fp8fp4", 512, 4.0, 2.0),
-    ("dsv3_fp8fp4_zipf", 8192, 4.0, 2.0),
-    ("decode_fp8fp4", 1, 2.0, 1.0),
-    ("decode_fp8fp4", 64, 4.0, 2.0),
-    ("dsv3_bf16", 8192, 4.0, 2.0),
-    ("mixtral_bf16", 4096, 4.0, 2.0),
-    ("tiny_f32", 64, 2.0, 1.0),
+    {"kind": "layer", "workload": "dsv3_fp8fp4", "T": 32768, "cpu": 12.0, "cpu1": 4.0},
+    {"kind": "layer", "workload": "dsv3_fp8fp4", "T": 8192, "cpu": 4.0, "cpu1": 2.0},
+    {"kind": "layer", "workload": "dsv3_fp8fp4", "T": 512, "cpu": 4.0, "cpu1": 2.0},
+    {"kind": "layer", "workload": "dsv3_fp8fp4_zipf", "T": 8192, "cpu": 4.0, "cpu1": 2.0},
+    {"kind": "capacity", "workload": "dsv3_fp8fp4_zipf", "T": 8192, "factor": 1.25, "cpu": 4.0, "cpu1": 2.0},
+    {"kind": "layer", "workload": "decode_fp8fp4", "T": 1, "cpu": 2.0, "cpu1": 1.0},
+    {"kind": "layer", "workload": "decode_fp8fp4", "T": 64, "cpu": 4.0, "cpu1": 2.0},
+    {"kind": "ep", "workload": "dsv3_fp8fp4", "T": 8192, "E_local": 32, "n_src": 8, "cpu": 4.0, "cpu1": 2.0},
+    {"kind": "gemm", "workload": "dsv3_fp8fp4", "M": 32768, "N": 4096, "K": 7168, "cpu": 3.0, "cpu1": 1.5},
+    {"kind": "layer", "workload": "dsv3_fp8fp8", "T": 8192, "cpu": 4.0, "cpu1": 2.0},
+    {"kind": "layer", "workload": "dsv3_bf16", "T": 8192, "cpu": 4.0, "cpu1": 2.0},
+    {"kind": "layer", "workload": "mixtral_bf16", "T": 4096, "cpu": 4.0, "cpu1": 2.0},
+    {"kind": "layer", "workload": "tiny_f32", "T": 64, "cpu": 2.0, "cpu1": 1.0},
 ]
 
 
@@ -96,6 +108,8 @@ def flops_of(w):
 def weight_bytes_per_group(w):
     if w.mode == "fp8_mxfp4":
         return 2 * w.F * w.d // 2 + 2 * w.F * w.d // 32 + w.d * w.F // 2 + w.d * w.F // 32
+    if w.mode == "fp8_fp8":
+        return 3 * w.F * w.d + 3 * w.F * w.d // 128 * 4
     eb = 4 if w.mode == "f32" else 2
     return 3 * w.F * w.d * eb
 
@@ -117,6 +131,10 @@ def kernel_work(w, name, counts):
     if w.mode == "fp8_mxfp4":
         w1b = 2 * w.F * w.d // 2 + 2 * w.F * w.d // 32
         w2b = w.d * w.F // 2 + w.d * w.F // 32
+        xb, hb = w.T * w.d * (1 + 4 / 128), rows * w.F * (1 + 4 / 128)
+    elif w.mode == "fp8_fp8":
+        w1b = 2 * w.F * w.d * (1 + 4 / 128)
+        w2b = w.d * w.F * (1 + 4 / 128)
         xb, hb = w.T * w.d * (1 + 4 / 128), rows * w.F * (1 + 4 / 128)
     else:
         w1b, w2b = 2 * w.F * w.d * act, w.d * w.F * act
@@ -169,6 +187,8 @@ _COMMON = ("common.hpp", "dispatch_dev.hpp")
 KERNEL_SOURCES = {
     ("linear1", "fp8_mxfp4"): ("ffn.hip", "ffn_fp8.hip", "gemm_fp8_dev.hpp") + _COMMON,
     ("linear2", "fp8_mxfp4"): ("ffn.hip", "ffn_fp8.hip", "gemm_fp8_dev.hpp") + _COMMON,
+    ("linear1", "fp8_fp8"): ("ffn.hip", "ffn_fp8x8.hip", "gemm_fp8x8_dev.hpp", "gemm_fp8_dev.hpp") + _COMMON,
+    ("linear2", "fp8_fp8"): ("ffn.hip", "ffn_fp8x8.hip", "gemm_fp8x8_dev.hpp", "gemm_fp8_dev.hpp") + _COMMON,
     ("linear1", "bf16"): ("ffn.hip", "gemm_bf16_dev.hpp") + _COMMON,
     ("linear2", "bf16"): ("ffn.hip", "gemm_bf16_dev.hpp") + _COMMON,
     ("combine", None): ("combine.hip", "combine_dev.hpp", "common.hpp"),
@@ -240,7 +260,7 @@ def upload(inp):
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
     act = "f32" if w.mode == "f32" else "bf16"
-    wk = "u8" if w.mode == "fp8_mxfp4" else act
+    wk = "u8" if w.mode in FP8 else act
     return {"x": dev(inp["x"], act), "w_router": dev(inp["w_router"], act), "bias": dev(inp["bias"], "f32"),
             "w1": dev(inp["w1"], wk), "w2": dev(inp["w2"], wk), "w1_scale": dev(inp["w1_scale"], "u8"),
             "w2_scale": dev(inp["w2_scale"], "u8")}
@@ -430,6 +450,294 @@ def measure_layer(w, inp, d, args, steps, warmup, cpu_s, cpu_1t):
     return out
 
 
+def kernel_times(step, steps):
+    """Per-kernel mean durations (HIP events on each launch's own stream) over `steps` steps."""
+    import torch
+
+    import mixture_experts_layer_dispatch_amd as moe
+
+    moe.profile_report()
+    moe.profile_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    prof = moe.profile_report()
+    moe.profile_enable(False)
+    return {n: {"launches_per_step": c / steps, "mean_ms": tt / c} for n, (c, tt) in prof.items()}
+
+
+def roofline_flops(kf, kb, mode, kernel, kms):
+    peak_f = PEAK[mode]
+    ridge = peak_f * 1e12 / (PEAK_HBM * 1e9)
+    if kb > 0 and kf / kb < ridge:
+        roof = {"bound": "hbm", "achieved": kb / (kms * 1e-3) / 1e9, "peak": PEAK_HBM, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": kf / (kms * 1e-3) / 1e12, "peak": peak_f, "unit": "TFLOP/s"}
+    roof.update({"frac": roof["achieved"] / roof["peak"], "traffic": None, "traffic_unit": "bytes per launch",
+                 "kernel": kernel, "launch_ms": kms, "work_per_launch": {"flop": kf, "bytes": kb}})
+    return roof
+
+
+def measure_capacity(w, inp, d, args, steps, warmup, factor, cpu_s, cpu_1t):
+    """The layer with the capacity-factor dispatch (route -> dispatch_capacity -> ffn -> combine):
+    each routed expert takes at most floor(factor * T * k / E) slots.  Also times one
+    aux-loss-free bias update from the step's counts."""
+    import torch
+
+    import mixture_experts_layer_dispatch_amd as moe
+    import oracle
+
+    cfg = moe.Config(T=w.T, d=w.d, E=w.E, k=w.k, F=w.F, n_shared=w.S, gating=w.gating, mode=w.mode)
+    cap = moe.capacity_of(factor, cfg)
+    log(f"{w.name} with capacity factor {factor}: {cap} slots per expert, T={w.T}")
+    ws = moe.alloc_workspace(cfg)
+    fp8 = w.mode in FP8
+    state = {}
+
+    def step():
+        idx, gate, _, _ = moe.route(cfg, d["x"], d["w_router"], d["bias"], ws=ws)
+        dsp = moe.dispatch_capacity(cfg, idx, cap, d["x"] if fp8 else None, ws=ws)
+        yp = moe.ffn(cfg, d["w1"], d["w2"], d["w1_scale"], d["w2_scale"], x=None if fp8 else d["x"], xq=dsp["xq"],
+                     xq_scale=dsp["xq_scale"], offsets=dsp["offsets"], row_to_slot=dsp["row_to_slot"], ws=ws)
+        state["y"] = moe.combine(cfg, yp, dsp["slot_to_row"], gate)
+        state.update(idx=idx, gate=gate, dsp=dsp)
+
+    t = time_steps(step, steps, warmup)
+    assert moe.read_device_error(cfg, ws) == 0
+    kernels = kernel_times(step, steps)
+    dsp = state["dsp"]
+    kept = dsp["counts"].cpu().numpy()
+    dropped = dsp["dropped"].cpu().numpy()
+    raw = kept[: w.E] + dropped
+    # one bias update from the load the router asked for (kept + dropped)
+    bias = torch.zeros(w.E, dtype=torch.float32, device="cuda")
+    load = torch.from_numpy(raw.astype(np.int32)).cuda()
+    tb = time_steps(lambda: moe.bias_update(cfg, load, bias, 1e-3), steps, warmup)
+    ms = t["mean"]
+    rows_kept = int(kept.sum())
+    f_exp = 6.0 * w.d * w.F * rows_kept
+    f_rt = 2.0 * w.T * w.d * w.E
+    dom = max(kernels.items(), key=lambda kv: kv[1]["mean_ms"] * kv[1]["launches_per_step"])[0]
+    kf = (4.0 if dom == "linear1" else 2.0) * rows_kept * w.F * w.d
+    kb = kernel_work(w, dom, kept)[1]
+    out = {
+        "kind": "capacity", "workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "F": w.F, "n_shared": w.S,
+        "gating": w.gating, "zipf_alpha": w.zipf_alpha, "dtype": DTYPE[w.mode], "path": "unfused",
+        "capacity_factor": factor, "capacity": cap, "dropped_slots": int(dropped.sum()),
+        "dropped_frac": float(dropped.sum()) / (w.T * w.k), "experts_over_capacity": int((dropped > 0).sum()),
+        "ms_per_step": ms, "ms_median": t["median"], "ms_p10": t["p10"], "ms_p90": t["p90"],
+        "active_tflops": (f_exp + f_rt) / (ms * 1e-3) / 1e12, "tokens_per_s": w.T / (ms * 1e-3),
+        "load": load_stats(w, raw), "kernels": kernels, "bias_update_ms": tb["median"],
+        "roofline": roofline_flops(kf, kb, w.mode, dom, kernels[dom]["mean_ms"]),
+        "timing": "wall clock over the timed steps; median/p10/p90 from HIP events around each step",
+    }
+    if not args.no_cpu:
+        keep = (dsp["slot_to_row"].cpu().numpy() >= 0).reshape(w.T, w.k)
+        idx, gate = state["idx"].cpu().numpy(), state["gate"].cpu().numpy()
+        cores = len(os.sched_getaffinity(0))
+        per_tok = (f_exp + f_rt) / w.T
+
+        def rate(threads, budget):
+            n0 = min(w.T, threads)
+            ta = time.perf_counter()
+            oracle.layer_dropping(inp, idx, gate, keep, tokens=np.arange(n0), nthreads=threads)
+            tp = time.perf_counter() - ta
+            n = int(min(w.T, max(n0, n0 * budget / max(tp, 1e-6))))
+            toks = np.linspace(0, w.T - 1, n).astype(np.int64)
+            ta = time.perf_counter()
+            oracle.layer_dropping(inp, idx, gate, keep, tokens=toks, nthreads=threads)
+            return n, time.perf_counter() - ta
+
+        n, dt = rate(cores, cpu_s)
+        n1, dt1 = rate(1, cpu_1t)
+        out["cpu_baseline"] = {"value": n / dt * per_tok / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                               "tokens_per_s": n / dt,
+                               "sample": f"{n} of {w.T} tokens (evenly spaced) through the experts with the GPU's "
+                                         f"routing and drops, fp64 C oracle on {cores} threads, {dt:.1f}s",
+                               "one_thread": {"tokens_per_s": n1 / dt1, "value": n1 / dt1 * per_tok / 1e12,
+                                              "unit": "TFLOP/s", "sample": f"{n1} tokens on 1 thread, {dt1:.1f}s"}}
+    else:
+        out["cpu_baseline"] = None
+    log(f"  capacity: {ms:.4f} ms, dropped {out['dropped_slots']} of {w.T * w.k} slots, bias update "
+        f"{tb['median'] * 1e3:.1f} us")
+    return out
+
+
+def ep_receive(w, E_local, n_src, seed=7000):
+    """Counts and rows of one expert-parallel rank: n_src ranks of w.T tokens each route
+    uniformly over w.E experts (top-k), this rank owning experts 0 .. E_local - 1; the rows are
+    seeded FP8 rows (the wire format: e4m3 codes with power-of-two scales per 128)."""
+    import synth
+
+    rng = np.random.default_rng(seed)
+    counts = np.zeros((E_local, n_src), dtype=np.int32)
+    for q in range(n_src):
+        choice = np.argpartition(rng.random((w.T, w.E)), w.k, axis=1)[:, : w.k]
+        counts[:, q] = np.bincount(choice.reshape(-1), minlength=w.E)[:E_local]
+    R = int(counts.sum())
+    rq, rs = synth.fp8_rows(seed, 21, R, w.d, 1.0)
+    xq, xs = synth.fp8_rows(seed, 22, w.T, w.d, 1.0)
+    return counts, (rq, rs), (xq, xs)
+
+
+def measure_ep(w, inp, d, args, steps, warmup, E_local, n_src, cpu_s, cpu_1t):
+    """One expert-parallel rank's share at its real shape: E_local local experts (and the
+    shared one) over the rows n_src ranks of w.T tokens send it, plus its own w.T tokens."""
+    import torch
+
+    import mixture_experts_layer_dispatch_amd as moe
+    import oracle
+
+    counts, recv, own = ep_receive(w, E_local, n_src)
+    R = int(counts.sum())
+    log(f"EP rank: {E_local} local experts + shared, {n_src} sources x {w.T} tokens -> {R} received rows")
+    G = w.E + w.S
+    sel = torch.tensor(list(range(E_local)) + [w.E], device="cuda")  # local experts, then the shared one
+    w1, w2, w1s, w2s = (d[k].index_select(0, sel).contiguous() for k in ("w1", "w2", "w1_scale", "w2_scale"))
+    cfg = moe.Config(T=w.T, d=w.d, E=E_local, k=1, F=w.F, n_shared=w.S, mode=w.mode)
+    ws = moe.ep_workspace(cfg, R)
+    rc = torch.from_numpy(counts).cuda()
+    rq, rs = torch.from_numpy(recv[0]).cuda(), torch.from_numpy(recv[1]).cuda()
+    xq, xs = torch.from_numpy(own[0]).cuda(), torch.from_numpy(own[1]).cuda()
+    yr = torch.empty(R, w.d, dtype=torch.bfloat16, device="cuda")
+    ysh = torch.empty(w.T, w.d, dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        moe.ep_ffn(cfg, w1, w2, w1s, w2s, recv_counts=rc, recv_xq=rq, recv_xs=rs, xq=xq, xs=xs, ws=ws, y_recv=yr,
+                   y_shared=ysh)
+
+    t = time_steps(step, steps, warmup)
+    assert moe.read_device_error(cfg, ws) == 0
+    kernels = kernel_times(step, steps)
+    ms = t["mean"]
+    rows = R + w.S * w.T
+    flop = 6.0 * w.d * w.F * rows
+    wbytes = (E_local + w.S) * weight_bytes_per_group(w)
+    dom = "linear1"
+    kf = 4.0 * R * w.F * w.d
+    kb = E_local * (weight_bytes_per_group(w) * 2 // 3) + R * w.d * (1 + 4 / 128) + R * w.F * (1 + 4 / 128)
+    out = {
+        "kind": "ep", "workload": w.name, "T": w.T, "d": w.d, "E_local": E_local, "n_src": n_src, "F": w.F,
+        "n_shared": w.S, "received_rows": R, "dtype": DTYPE[w.mode], "path": "moe_ep_ffn",
+        "ms_per_step": ms, "ms_median": t["median"], "ms_p10": t["p10"], "ms_p90": t["p90"],
+        "active_tflops": flop / (ms * 1e-3) / 1e12, "rows_per_s": rows / (ms * 1e-3),
+        "algorithmic_GBps": (wbytes + rows * w.d * (1 + 4 / 128) + rows * w.d * 2) / (ms * 1e-3) / 1e9,
+        "mfma_frac": flop / (ms * 1e-3) / 1e12 / PEAK[w.mode], "kernels": kernels,
+        "load": {"rows_per_expert_max": int(counts.sum(1).max()), "rows_per_expert_min": int(counts.sum(1).min())},
+        "roofline": roofline_flops(kf, kb, w.mode, dom, kernels[dom]["mean_ms"]),
+        "timing": "wall clock over the timed steps; median/p10/p90 from HIP events around each step",
+    }
+    if not args.no_cpu:
+        ex = {"workload": w, "w1": inp["w1"][list(range(E_local)) + [w.E]], "w2": inp["w2"][list(range(E_local)) + [w.E]],
+              "w1_scale": inp["w1_scale"][list(range(E_local)) + [w.E]],
+              "w2_scale": inp["w2_scale"][list(range(E_local)) + [w.E]]}
+        import synth as _s
+        ex["workload"] = _s.Workload("ep", w.seed, w.mode, w.T, w.d, E_local, 1, w.F, w.S, "softmax")
+        offs = np.concatenate([[0], np.cumsum(counts.sum(axis=1))])
+        cores = len(os.sched_getaffinity(0))
+
+        def rate(threads, budget):
+            from concurrent.futures import ThreadPoolExecutor
+
+            def run(rws):
+                def one(r):
+                    g = int(np.searchsorted(offs, r, side="right") - 1)
+                    xin = oracle.dequant_e4m3_rows(recv[0][r:r + 1], recv[1][r:r + 1])
+                    oracle.expert_rows(ex, g, xin)
+                with ThreadPoolExecutor(max_workers=threads) as pool:
+                    list(pool.map(one, rws))
+
+            n0 = threads
+            ta = time.perf_counter()
+            run(np.linspace(0, R - 1, n0).astype(np.int64))
+            tp = time.perf_counter() - ta
+            n = int(min(R, max(n0, n0 * budget / max(tp, 1e-6))))
+            ta = time.perf_counter()
+            run(np.linspace(0, R - 1, n).astype(np.int64))
+            return n, time.perf_counter() - ta
+
+        n, dt = rate(cores, cpu_s)
+        n1, dt1 = rate(1, cpu_1t)
+        per_row = 6.0 * w.d * w.F
+        out["cpu_baseline"] = {"value": n / dt * per_row / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                               "rows_per_s": n / dt,
+                               "sample": f"{n} of {R} received rows (evenly spaced) through their expert, fp64 C "
+                                         f"oracle on {cores} threads, {dt:.1f}s",
+                               "one_thread": {"rows_per_s": n1 / dt1, "value": n1 / dt1 * per_row / 1e12,
+                                              "unit": "TFLOP/s", "sample": f"{n1} rows on 1 thread, {dt1:.1f}s"}}
+    else:
+        out["cpu_baseline"] = None
+    log(f"  EP rank: {ms:.4f} ms, {out['active_tflops']:.0f} TFLOP/s")
+    return out
+
+
+def measure_gemm(w, inp, d, args, steps, warmup, M, N, K, cpu_s, cpu_1t):
+    """The dense FP8 x MXFP4 GEMM: A [M, K] seeded FP8 rows, B the first N rows of the layer's
+    (shared expert's) W1 -- an [N, K] MXFP4 matrix."""
+    import torch
+
+    import mixture_experts_layer_dispatch_amd as moe
+    import oracle
+    import synth
+
+    log(f"dense FP8 x MXFP4 GEMM: M={M} N={N} K={K}")
+    a, a_s = synth.fp8_rows(7100, 31, M, K, 1.0)
+    b = d["w1"][w.E][:N].contiguous()
+    b_s = d["w1_scale"][w.E][:N].contiguous()
+    ad, asd = torch.from_numpy(a).cuda(), torch.from_numpy(a_s).cuda()
+    c = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.GEMM_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+
+    def step():
+        moe.gemm_fp8_mxfp4(ad, asd, b, b_s, ws=ws, c=c)
+
+    t = time_steps(step, steps, warmup)
+    kernels = kernel_times(step, steps)
+    ms = t["mean"]
+    flop = 2.0 * M * N * K
+    kb = N * K // 2 + N * K // 32 + M * K * (1 + 4 / 128) + M * N * 2
+    out = {
+        "kind": "gemm", "M": M, "N": N, "K": K, "dtype": "fp8e4m3 x mxfp4", "path": "moe_gemm_fp8_mxfp4",
+        "ms_per_step": ms, "ms_median": t["median"], "ms_p10": t["p10"], "ms_p90": t["p90"],
+        "tflops": flop / (ms * 1e-3) / 1e12, "mfma_frac": flop / (ms * 1e-3) / 1e12 / PEAK["fp8_mxfp4"],
+        "kernels": kernels,
+        "roofline": roofline_flops(flop, kb, "fp8_mxfp4", "gemm_fp8_mxfp4", kernels["gemm_fp8_mxfp4"]["mean_ms"]),
+        "timing": "wall clock over the timed steps; median/p10/p90 from HIP events around each step",
+    }
+    if not args.no_cpu:
+        bh, bsh = inp["w1"][w.E][:N], inp["w1_scale"][w.E][:N]
+        cores = len(os.sched_getaffinity(0))
+
+        def rate(threads, budget):
+            from concurrent.futures import ThreadPoolExecutor
+
+            def run(rws):
+                with ThreadPoolExecutor(max_workers=threads) as pool:
+                    list(pool.map(lambda r: oracle.gemm_fp8_mxfp4(a, a_s, bh, bsh, rows=[r]), rws))
+
+            n0 = threads
+            ta = time.perf_counter()
+            run(np.linspace(0, M - 1, n0).astype(np.int64))
+            tp = time.perf_counter() - ta
+            n = int(min(M, max(n0, n0 * budget / max(tp, 1e-6))))
+            ta = time.perf_counter()
+            run(np.linspace(0, M - 1, n).astype(np.int64))
+            return n, time.perf_counter() - ta
+
+        n, dt = rate(cores, cpu_s)
+        n1, dt1 = rate(1, cpu_1t)
+        per_row = 2.0 * N * K
+        out["cpu_baseline"] = {"value": n / dt * per_row / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                               "rows_per_s": n / dt,
+                               "sample": f"{n} of {M} rows of C, fp64 C oracle on {cores} threads, {dt:.1f}s",
+                               "one_thread": {"rows_per_s": n1 / dt1, "value": n1 / dt1 * per_row / 1e12,
+                                              "unit": "TFLOP/s", "sample": f"{n1} rows on 1 thread, {dt1:.1f}s"}}
+    else:
+        out["cpu_baseline"] = None
+    log(f"  dense GEMM: {ms:.4f} ms, {out['tflops']:.0f} TFLOP/s")
+    return out
+
+
 def line_of(e, args, sweep=None):
     """The JSON line of the headline entry e."""
     decode = e["T"] == 1
@@ -497,22 +805,34 @@ def main(argv=None):
 
     # the default run: the headline entry, then the sweep (entries sharing weights together)
     t_max = {}
-    for name, T, _, _ in SWEEP:
-        key = synth.WORKLOADS[name].seed
-        t_max[key] = max(t_max.get(key, 0), T)
+    for ent in SWEEP:
+        key = synth.WORKLOADS[ent["workload"]].seed
+        t_max[key] = max(t_max.get(key, 0), ent.get("T", 1))
     entries = []
-    for name, T, cpu_s, cpu_1t in SWEEP:
-        w = synth.WORKLOADS[name].with_T(T)
+    for ent in SWEEP:
+        kind = ent["kind"]
+        w = synth.WORKLOADS[ent["workload"]].with_T(ent.get("T", 1))
         inp, d = cache.get(w, t_max[w.seed])
-        headline = (name, T) == HEADLINE
+        headline = (kind, ent["workload"], ent.get("T")) == HEADLINE
         steps = args.steps if headline else min(args.steps, 20)
         warmup = args.warmup if headline else min(args.warmup, 5)
+        cpu_s, cpu_1t = ent["cpu"], ent["cpu1"]
         if args.cpu_seconds is not None:
             cpu_s = args.cpu_seconds if headline else min(cpu_s, args.cpu_seconds)
-        entries.append(measure_layer(w, inp, d, args, steps, warmup, cpu_s, cpu_1t))
+        if kind == "layer":
+            e = measure_layer(w, inp, d, args, steps, warmup, cpu_s, cpu_1t)
+            e["kind"] = "layer"
+        elif kind == "capacity":
+            e = measure_capacity(w, inp, d, args, steps, warmup, ent["factor"], cpu_s, cpu_1t)
+        elif kind == "ep":
+            e = measure_ep(w, inp, d, args, steps, warmup, ent["E_local"], ent["n_src"], cpu_s, cpu_1t)
+        else:
+            e = measure_gemm(w, inp, d, args, steps, warmup, ent["M"], ent["N"], ent["K"], cpu_s, cpu_1t)
+        e["headline"] = headline
+        entries.append(e)
         log(f"  done ({time.time() - t_start:.0f}s since start)")
     cache.release()
-    head = next(e for e in entries if (e["workload"], e["T"]) == HEADLINE)
+    head = next(e for e in entries if e["headline"])
     sweep = [e for e in entries if e is not head]
     print(json.dumps(line_of(head, args, sweep)), flush=True)
 
