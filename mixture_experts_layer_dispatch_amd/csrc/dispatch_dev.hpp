@@ -382,6 +382,44 @@ __device__ __forceinline__ void quant_x_lane(const uint16_t *__restrict__ x, lon
     if (sub == 0) stc<COH>(xs + blk, ldexpf(1.0f, e));
 }
 
+// NB lane tasks gid0 + u * stride (u < NB, stride a multiple of 16) of quant_x_lane, every
+// load issued before the first conversion: a few workgroups looping over many blocks keep NB
+// loads in flight per lane instead of one.  COH: device-coherent stores, as quant_x_lane.
+template <int NB, bool COH>
+__device__ __forceinline__ void quant_x_batch(const uint16_t *__restrict__ x, long nblocks, uint8_t *__restrict__ xq,
+                                              float *__restrict__ xs, long gid0, long stride) {
+    uint4 q[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        const long blk = (gid0 + u * stride) >> 4;
+        const int sub = (int)((gid0 + u * stride) & 15);
+        q[u] = blk < nblocks ? *(const uint4 *)(x + blk * 128 + sub * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        const long blk = (gid0 + u * stride) >> 4;
+        const int sub = (int)((gid0 + u * stride) & 15);
+        const uint16_t *h = (const uint16_t *)&q[u];
+        float v[8];
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[i] = bf16_to_f32(h[i]);
+            amax = fmaxf(amax, fabsf(v[i]));
+        }
+        amax = row16_max(amax);
+        if (blk < nblocks) {
+            const int e = e4m3_block_exponent(amax);
+            const float inv = ldexpf(1.0f, -e);
+            uint2 out;
+            out.x = cvt_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+            out.y = cvt_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+            stc<COH>((uint64_t *)(xq + blk * 128 + sub * 8), (uint64_t)out.x | ((uint64_t)out.y << 32));
+            if (sub == 0) stc<COH>(xs + blk, ldexpf(1.0f, e));
+        }
+    }
+}
+
 // The same quantiser over fp32 values: 16 lanes per 128-value block, 8 values (two 16-byte
 // loads) each.
 __device__ __forceinline__ void quant_f32_lane(const float *__restrict__ v, long nblocks, uint8_t *__restrict__ q,

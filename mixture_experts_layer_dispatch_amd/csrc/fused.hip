@@ -120,9 +120,12 @@ hipError_t launch_layer_fused(const Shape &s, const FfnPlan &p, FusedArgs &a, in
     a.ntn2 = p.ntn2;
     a.ks = p.ks;
     a.rows = s.rows();
-    a.nm = fused_row_tiles(s, p);
-    const long lanes_q = fp8_act(s.mode) ? (long)s.T * (s.d / 128) * 16 : 0;
-    const long nq = (lanes_q + 1023) / 1024;
+    // row-tile counters: only the decode variant's hand-offs use (and clear) them
+    a.nm = p.decode ? fused_row_tiles(s, p) : 0;
+    // FP8 activation items: contiguous ranges of at least 64 blocks of 128, at most 256 items
+    const long nblocks_q = fp8_act(s.mode) ? (long)s.T * (s.d / 128) : 0;
+    long nq = (nblocks_q + 63) / 64;
+    if (nq > 256) nq = 256;
     long nr;
     switch (a.router) {
         case ROUTER_SPLITK: nr = (route_splitk_waves(s, a.nks) + 3) / 4; break;
@@ -130,8 +133,10 @@ hipError_t launch_layer_fused(const Shape &s, const FfnPlan &p, FusedArgs &a, in
         case ROUTER_MFMA: nr = (s.T + kRouteTok - 1) / kRouteTok; break;
         default: nr = (s.T + 3) / 4; break;
     }
-    a.sel4 = router_in_slices(a.router) && route_select_by_wave(s.E, a.nks);
-    const long nsel = !router_in_slices(a.router) ? 0 : a.sel4 ? (s.T + 3) / 4 : s.T;
+    // selection by waves: tokens per item -- 4 at decode sizes (parallel waves), 32 at large T
+    // (each item's hand-off, a few microseconds, is paid once per 32 tokens)
+    a.sel4 = router_in_slices(a.router) && route_select_by_wave(s.E, a.nks) ? (s.T >= 2048 ? 32 : 4) : 0;
+    const long nsel = !router_in_slices(a.router) ? 0 : a.sel4 ? (s.T + a.sel4 - 1) / a.sel4 : s.T;
     a.b_r = nq;
     a.b_sel = a.b_r + nr;
     a.b_cnt = a.b_sel + nsel;

@@ -195,24 +195,24 @@ static __device__ __noinline__ void route_tile8_call(const uint16_t *x, const ui
 template <int MODE, bool W8 = false>
 __device__ __forceinline__ void front_item(const FusedArgs &a, long i, uint8_t *lds, bool &routed) {
     const int nr = (int)(a.b_sel - a.b_r);
-    if (i < a.b_r) {  // FP8 activations: 64 blocks of 128 per item
+    if (i < a.b_r) {  // FP8 activations: a contiguous range of 128-value blocks per item
+        // Coarse items (a counter hand-off each), every thread of the workgroup with 16 loads in
+        // flight per lane, device-coherent stores (no fence).
         const long nblocks = (long)a.T * a.d / 128;
-        if (threadIdx.x < 256) {
-#pragma unroll
-            for (int pass = 0; pass < 4; ++pass)
-                quant_x_lane<true>((const uint16_t *)a.x, nblocks, a.xq, a.xs, (i * 4 + pass) * 256 + threadIdx.x);
-        }
+        const long per = (nblocks + a.b_r - 1) / a.b_r, blk0 = i * per;
+        const long blk1 = blk0 + per < nblocks ? blk0 + per : nblocks;
+        const long nth = blockDim.x;
+        for (long gid = blk0 * 16 + threadIdx.x; gid - threadIdx.x < blk1 * 16; gid += 16 * nth)
+            quant_x_batch<16, true>((const uint16_t *)a.x, blk1, a.xq, a.xs, gid, nth);
         wg_count(a.sync, CNT_QUANT, i);
     } else if (i < a.b_sel) {  // router
         const int b = (int)(i - a.b_r);
         float *lg = (float *)lds;
         if (W8 && a.router == ROUTER_TILE) {
-            // one 256 x 256 tile of one K slice; its partial logits go out with plain stores,
-            // written back by the release fence before the count (selection reads them with
-            // device-coherent loads)
+            // one 256 x 256 tile of one K slice; its partial logits go out with device-coherent
+            // stores, complete before the count (selection reads them with coherent loads)
             if constexpr (W8 && MODE != MODE_F32)
                 route_tile8_call((const uint16_t *)a.x, (const uint16_t *)a.wr, a.T, a.d, a.E, a.nks, b, a.rpart);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         } else if (a.router == ROUTER_SPLITK) {
             const long w = (long)b * 4 + (threadIdx.x >> 6);
             if (threadIdx.x < 256 && w < (long)(a.E / 32) * a.nks * ((a.T + 31) / 32))
@@ -233,9 +233,10 @@ __device__ __forceinline__ void front_item(const FusedArgs &a, long i, uint8_t *
             routed = true;
         }
         if (a.sel4) {
-            const int wave = threadIdx.x >> 6;
-            const long t = (i - a.b_sel) * 4 + wave;
-            if (wave < 4 && t < a.T)
+            // sel4 tokens per item, a wave each in turn (every wave of the workgroup)
+            const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+            const long t0 = (i - a.b_sel) * a.sel4, t1 = t0 + a.sel4 < a.T ? t0 + a.sel4 : a.T;
+            for (long t = t0 + wave; t < t1; t += nw)
                 route_sum_select_wave<true>(a.rpart, a.nks, a.T, a.E, a.k, a.gating, a.bias, t,
                                             (float *)lds + wave * a.E, a.idx, a.gate, nullptr, nullptr, a.err);
         } else {
@@ -375,7 +376,7 @@ static __device__ __noinline__ void route_tile8_call(const uint16_t *x, const ui
     ti.nrows = min(256, T - ti.row0);
     GemmArgs g = {x, nullptr, wr, (uint16_t *)(part + (long)ks * T * E), nullptr, nullptr, T, 1, d, E, E, 1, 0};
     const int kchunk = d / nks;
-    bf16_tile8_rows<false, false, true>(g, ti, d, ks * kchunk, kchunk / 32, lds_dyn);
+    bf16_tile8_rows<false, false, true, true>(g, ti, d, ks * kchunk, kchunk / 32, lds_dyn);
 }
 
 // The steps before the GEMMs, out of line in the 512-thread and decode kernels (inlined

@@ -250,7 +250,9 @@ constexpr size_t bf16_tile8_lds() { return 5 * (size_t)(256 + 256) * 64; }
 // tile runs with TM = 2 (up to 128 rows) or 1 (up to 64), which keeps the wave grid and
 // the LDS layout, loads only the first 128 A rows and multiplies only TM blocks: MFMA work
 // shrinks with the rows present and stays balanced over the SIMDs.
-template <bool SWIGLU, bool GATHER, bool F32OUT, int TM>
+// COH: fp32 outputs go out as device-coherent stores (a consumer in the same launch reads
+// them after a counter hand-off, with no fence)
+template <bool SWIGLU, bool GATHER, bool F32OUT, int TM, bool COH = false>
 __device__ __forceinline__ void bf16_tile8_core(const GemmArgs &a, const TileInfo &ti, long lda, int k0, int nk,
                                                 uint8_t *lds) {
     constexpr int BM = 256, BN = 256, BK = 32, NS = 5;
@@ -413,7 +415,7 @@ __device__ __forceinline__ void bf16_tile8_core(const GemmArgs &a, const TileInf
             } else if (F32OUT) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    ((float *)a.C)[grow * a.ldc + n0 + wn * 64 + j * 32 + (lane & 31)] = acc[i][j][r];
+                    stc<COH>((float *)a.C + grow * a.ldc + n0 + wn * 64 + j * 32 + (lane & 31), acc[i][j][r]);
             } else {
 #pragma unroll
                 for (int j = 0; j < TN; ++j) a.C[grow * a.ldc + n0 + wn * 64 + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][r]);
@@ -423,12 +425,12 @@ __device__ __forceinline__ void bf16_tile8_core(const GemmArgs &a, const TileInf
 }
 
 // the core sized to the tile's rows
-template <bool SWIGLU, bool GATHER, bool F32OUT>
+template <bool SWIGLU, bool GATHER, bool F32OUT, bool COH = false>
 __device__ __forceinline__ void bf16_tile8_rows(const GemmArgs &a, const TileInfo &ti, long lda, int k0, int nk,
                                                 uint8_t *lds) {
-    if (ti.nrows > 128) bf16_tile8_core<SWIGLU, GATHER, F32OUT, 4>(a, ti, lda, k0, nk, lds);
-    else if (ti.nrows > 64) bf16_tile8_core<SWIGLU, GATHER, F32OUT, 2>(a, ti, lda, k0, nk, lds);
-    else bf16_tile8_core<SWIGLU, GATHER, F32OUT, 1>(a, ti, lda, k0, nk, lds);
+    if (ti.nrows > 128) bf16_tile8_core<SWIGLU, GATHER, F32OUT, 4, COH>(a, ti, lda, k0, nk, lds);
+    else if (ti.nrows > 64) bf16_tile8_core<SWIGLU, GATHER, F32OUT, 2, COH>(a, ti, lda, k0, nk, lds);
+    else bf16_tile8_core<SWIGLU, GATHER, F32OUT, 1, COH>(a, ti, lda, k0, nk, lds);
 }
 
 // half: -1 the whole tile, 0 / 1 its rows 0..127 / 128..255 (an empty half returns at once);

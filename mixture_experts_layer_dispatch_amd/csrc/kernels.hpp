@@ -148,7 +148,7 @@ struct FusedArgs {
     float *rpart, *upart;
     // plan
     int router, nks, nblk;
-    int sel4;  // split-K router: 4 tokens per selection item (a wave each), else 1
+    int sel4;  // split-K router: tokens per selection item (a wave each in turn), or 0: one token per item
     int bm, ntn1, ntn2, ks;
     long rows;
     int nm;   // row tiles bound (kRowTileSlots slots each in done1)
