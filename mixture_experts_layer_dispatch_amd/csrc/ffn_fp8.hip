@@ -34,7 +34,7 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel8(Fp8Args a, int xcd_cus) 
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     int half;
     const int tile = pick_tile_split(blockIdx.x, a.tile_start[a.G], xcd_cus, half);
-    if (tile >= 0) fp8_tile8<SWIGLU ? 1 : 2, SWIGLU ? 8 : 4, SWIGLU, GATHER>(a, tile, lds, half);
+    if (tile >= 0) fp8_tile8<1, 8, SWIGLU, GATHER>(a, tile, lds, half);
 }
 
 // 256 x 256 tiles: the 8-wave kernel (the layer's linear1 gathers its rows, linear2 does

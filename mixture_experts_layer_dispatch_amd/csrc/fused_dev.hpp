@@ -350,7 +350,7 @@ __device__ __noinline__ void fp8_tile8_call(Fp8Args a, int tile, int half) {
     a.Bs = unip(a.Bs); a.C = unip(a.C); a.Cs = unip(a.Cs); a.offsets = unip(a.offsets);
     a.tile_start = unip(a.tile_start);
     uniform_ints(a);
-    fp8_tile8<SWIGLU ? 1 : 2, SWIGLU ? 8 : 4, SWIGLU, SWIGLU>(a, uni(tile), lds_dyn, uni(half));
+    fp8_tile8<1, 8, SWIGLU, SWIGLU>(a, uni(tile), lds_dyn, uni(half));
 }
 
 // Router tile b of the tiled router (the stand-alone path's route_tile_kernel without its

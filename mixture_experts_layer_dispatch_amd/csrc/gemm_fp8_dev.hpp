@@ -323,7 +323,7 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args &a, int tile, uint8_t *ld
 //
 // Two waves per SIMD (512 threads), so one wave's MFMAs cover the other's LDS and barrier
 // waits.  linear1: each wave owns 32 rows x (128 gate + 128 up) columns, which keeps the
-// SwiGLU and h-quantisation epilogue inside the wave; linear2: 64 rows x 128 columns.
+// SwiGLU and h-quantisation epilogue inside the wave; linear2 the same 32 rows x 256 columns.
 // K advances 128 per stage (two k64 MFMA steps); NS = 3 stages of 50 KB (A codes 256 x 128,
 // B codes 256 x 64, A scales, B scale dwords).  Each pass multiplies k64 step 0 of stage kt
 // while reading step 1's fragments, passes the one barrier (stage kt + 1 published, every
@@ -331,7 +331,7 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args &a, int tile, uint8_t *ld
 // Loads are split as in the bf16 8-wave tile: stage s's B codes and scale dword go out in
 // the first half of pass s - NS + 1, its A codes in the second half of pass s - NS, both
 // into the buffer freed by the barrier of pass s - NS, interleaved one by one with MFMAs.
-// With one 32-row block per wave (linear1) each B fragment feeds one MFMA per k64 step and
+// With one 32-row block per wave each B fragment feeds one MFMA per k64 step and
 // is refilled right after it, which keeps the wave within 256 VGPRs without spilling.  A
 // wave whose rows all lie past a group's last, partial tile skips its fragment reads and
 // MFMAs (it still loads its share and keeps the barriers), and the row groups are laid out
@@ -343,7 +343,9 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args &a, int tile, uint8_t *ld
 constexpr size_t fp8_tile8_lds() { return 3 * (size_t)(256 * 128 + 256 * 64 + 256 * 4 + 256 * 4); }
 
 // TM x TN blocks of 32x32 per wave; linear1 (SWIGLU): TM = 1, TN = 8 (32 rows, 128 gate + 128 up
-// columns); linear2: TM = 2, TN = 4 (64 rows x 128 columns).  half: -1 the whole tile, 0 / 1
+// columns); linear2 runs TM = 1, TN = 8 as well (32 rows x 256 columns: same DeepSeek-V3 linear2
+// at T = 8192 in 1.39 against 1.56 ms with TM = 2, TN = 4, the same bits); TM = 2, TN = 4 (64
+// rows x 128 columns, double-buffered fragments) stays available.  half: -1 the whole tile, 0 / 1
 // its rows 0..127 / 128..255 (an empty half returns at once); the first 128 rows are one
 // wave per SIMD's, and every output element takes the same k order either way.
 template <int TM, int TN, bool SWIGLU, bool GATHER>
