@@ -49,10 +49,11 @@ FfnPlan ffn_plan(const Shape &s) {
     FfnPlan p;
     const long rows = s.rows();
     const double per_group = (double)rows / s.G();
-    // weight streaming only below one row per group: from there on the tiled kernels, which
-    // stream each weight tile through LDS for several rows, are faster (measured at 2.2 rows
-    // per group: 1.52 against 1.61 ms; at 18: 2.12 against 2.83 ms)
-    p.decode = s.mode == MODE_FP8 && per_group < 1.0 && rows * (s.d > 2 * s.F ? s.d : 2 * s.F) < (1L << 31);
+    // weight streaming below 20 rows per group, the tiled kernels (each weight tile streamed
+    // through LDS for 256 rows) from there on.  DeepSeek-V3 FP8 x FP4 layer on MI355X, weight
+    // streaming against tiled: 1.1 rows per group 0.93 / 1.11 ms, 2.2 1.29 / 1.43, 3.4
+    // 1.43 / 1.66, 9 1.58 / 1.80, 13.4 1.65 / 1.82, 17.9 1.71 / 1.77
+    p.decode = s.mode == MODE_FP8 && per_group < 20.0 && rows * (s.d > 2 * s.F ? s.d : 2 * s.F) < (1L << 31);
     if (p.decode) {
         // One 64-lane wave per (group, 32-row tile, 32 output columns, K slice).  linear1's
         // K slices are whole 256-wide chunks, the fewest that keep a slice within 1024: the

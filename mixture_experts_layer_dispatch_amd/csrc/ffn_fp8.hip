@@ -103,13 +103,17 @@ __global__ __launch_bounds__(256) void fp8_decode_swiglu_kernel(const float *__r
 
 // The workgroup decode kernels apply: K slices of whole 1024-wide blocks (at most 2048),
 // column tiles in fours, and the staged rows (at most min(32, T) per tile) and the plan
-// within 64 KB of LDS.  They build their own tile plan.
+// within 96 KB of LDS (32 rows of a 2048-wide slice take 70 KB: two workgroups per CU).
+// They build their own tile plan.
+constexpr size_t kGemvLdsMax = 96 * 1024;
+
 bool fp8_gemv_ok(const Shape &s, const FfnPlan &p) {
     if (!p.decode) return false;
     const int rmax = s.T < 32 ? s.T : 32, G = s.G();
     const int kc1 = s.d / p.ks, kc2 = s.F;
     return kc1 % 1024 == 0 && kc2 % 1024 == 0 && kc1 <= 2048 && kc2 <= 2048 && p.ntn1 % 4 == 0 &&
-           p.ntn2 % 4 == 0 && fp8_gemv_lds_total(G, rmax, kc1) <= 65536 && fp8_gemv_lds_total(G, rmax, kc2) <= 65536;
+           p.ntn2 % 4 == 0 && fp8_gemv_lds_total(G, rmax, kc1) <= kGemvLdsMax &&
+           fp8_gemv_lds_total(G, rmax, kc2) <= kGemvLdsMax;
 }
 
 template <bool LIN1, int QC, int NB>
@@ -118,7 +122,7 @@ static hipError_t launch_gemv(const char *name, dim3 grid, size_t lds, hipStream
     static bool attr = false;
     if (!attr) {
         hipError_t e = hipFuncSetAttribute((const void *)fp8_gemv_kernel<LIN1, QC, NB>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 65536);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvLdsMax);
         if (e != hipSuccess) return e;
         attr = true;
     }

@@ -904,12 +904,17 @@ __device__ __forceinline__ void fp8_gemv_tile(const DecArgs &a, int wt, int rmax
         for (int c = 0; c < KC / 1024; ++c)
             lds_dma16(a.A + (size_t)src * a.K + kbeg + c * 1024 + lane * 16, la + rw * RS + c * 1024);
     }
-    float sav = 0.0f;  // this thread's activation scale, if any
-    const int sidx = threadIdx.x;
-    if (sidx < nrows * NSC) {
-        const int rw = sidx / NSC, j = sidx % NSC;
-        const long src = LIN1 ? row_token(row0 + rw, a.row_to_slot, a.T, a.k) : (long)row0 + rw;
-        sav = a.As[src * (a.K / 128) + kbeg / 128 + j];
+    // activation scales: nrows x NSC of them (at most 32 x 16), two per thread of the 256
+    static_assert(32 * NSC <= 2 * 256, "two scales per thread cover the tile");
+    float sav[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int sidx = threadIdx.x + 256 * u;
+        if (sidx < nrows * NSC) {
+            const int rw = sidx / NSC, j = sidx % NSC;
+            const long src = LIN1 ? row_token(row0 + rw, a.row_to_slot, a.T, a.k) : (long)row0 + rw;
+            sav[u] = a.As[src * (a.K / 128) + kbeg / 128 + j];
+        }
     }
     // 2. weight blocks (4 x 16 B codes and 2 scale dwords per lane) through the ring
     const long n0 = (long)(4 * qc * QC + wave) * 32 + r;  // this lane's column in quad 0
@@ -935,7 +940,9 @@ __device__ __forceinline__ void fp8_gemv_tile(const DecArgs &a, int wt, int rmax
     for (int j = 0; j < D - 1; ++j) GEMV_LOAD(j, j);
     // everything but the weight blocks has landed (loads complete in order)
     wait_vmcnt<(D - 1) * 6>();
-    if (sidx < nrows * NSC) lsa[sidx] = sav;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+        if (threadIdx.x + 256 * u < nrows * NSC) lsa[threadIdx.x + 256 * u] = sav[u];
     __syncthreads();
 
     const int rr = r < nrows ? r : 0;

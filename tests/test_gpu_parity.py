@@ -54,6 +54,12 @@ SMALL = {
                                    zipf_alpha=0.25),
     "fp8x8_decode_3": Workload("fp8x8_decode_3", 2018, "fp8_fp8", 3, 384, 16, 4, 128, 1, "softmax"),
     "fp8x8_large_groups": Workload("fp8x8_large_groups", 2019, "fp8_fp8", 1200, 256, 8, 2, 256, 0, "softmax"),
+    # weight streaming with 2048-wide K slices and tall row tiles: the shared expert's 20 rows
+    # (more than 16 rows of 16 activation scales each), then up to 2.2 rows per group (row
+    # tiles of 32 rows, several per group)
+    "fp8_decode_tall_20": Workload("fp8_decode_tall_20", 2020, "fp8_mxfp4", 20, 1024, 256, 4, 2048, 1, "softmax"),
+    "fp8_decode_rows_64": Workload("fp8_decode_rows_64", 2021, "fp8_mxfp4", 64, 1024, 256, 8, 2048, 1, "sigmoid",
+                                   zipf_alpha=0.25),
 }
 
 
@@ -111,7 +117,7 @@ def test_small_layer_parity(name):
 
 
 @pytest.mark.parametrize("name", ["bf16_sigmoid_shared", "f32_sigmoid_shared", "fp8_softmax_shared", "fp8_decode_5",
-                                  "bf16_w8", "fp8_w8_tiled_router", "fp8x8_sigmoid_zipf"])
+                                  "bf16_w8", "fp8_w8_tiled_router", "fp8x8_sigmoid_zipf", "fp8_decode_rows_64"])
 def test_fused_grid_sizes_and_repeats(name):
     """The persistent kernel gives the unfused bits on a full grid, on 8 CUs and on 3 CUs
     (many items per workgroup), call after call (each launch leaves its counters clean for
