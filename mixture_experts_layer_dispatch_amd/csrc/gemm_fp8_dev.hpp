@@ -856,8 +856,13 @@ __device__ __forceinline__ void fp8_decode_tile(const DecArgs &a, int tile, cons
 // (tile starts and group offsets) sits in LDS, built once per workgroup.  The MFMA
 // operands and their order per K slice are those of fp8_decode_tile: results are identical
 // bit for bit.  K / ks is a multiple of 1024 and at most 2048.
+//
+// LDS: the tile plan (2 (G + 1) ints), then the staged rows from the next 16-byte boundary
+// (their DMAs and 16-byte reads need it: G + 1 is odd without a shared expert), then their
+// scales.
+__host__ __device__ constexpr size_t fp8_gemv_off_rows(int G) { return ((size_t)8 * (G + 1) + 15) / 16 * 16; }
 __host__ __device__ constexpr size_t fp8_gemv_lds(int G, int rmax, int kc) {
-    return (size_t)2 * (G + 1) * 4 + (size_t)rmax * (kc + 16) + (size_t)rmax * (kc / 128) * 4;
+    return fp8_gemv_off_rows(G) + (size_t)rmax * (kc + 16) + (size_t)rmax * (kc / 128) * 4;
 }
 // the tile plan is built in the same LDS before the rows are staged (scan scratch included)
 __host__ __device__ constexpr size_t fp8_gemv_lds_total(int G, int rmax, int kc) {
@@ -893,7 +898,7 @@ __device__ __forceinline__ void fp8_gemv_tile(const DecArgs &a, int wt, int rmax
     int nrows = min(32, cnt - mt * 32);
     nrows = nrows < rmax ? nrows : rmax;  // rmax >= nrows whenever the routing is valid
     const int kbeg = ksl * KC;
-    uint8_t *la = lds + (size_t)2 * (a.G + 1) * 4;
+    uint8_t *la = lds + fp8_gemv_off_rows(a.G);
     float *lsa = (float *)(la + (size_t)rmax * RS);
     const int lane = lane_id(), kh = lane >> 5, r = lane & 31, wave = threadIdx.x >> 6;
 

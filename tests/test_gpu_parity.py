@@ -60,6 +60,9 @@ SMALL = {
     "fp8_decode_tall_20": Workload("fp8_decode_tall_20", 2020, "fp8_mxfp4", 20, 1024, 256, 4, 2048, 1, "softmax"),
     "fp8_decode_rows_64": Workload("fp8_decode_rows_64", 2021, "fp8_mxfp4", 64, 1024, 256, 8, 2048, 1, "sigmoid",
                                    zipf_alpha=0.25),
+    # no shared expert: G + 1 groups' plan words are an odd count (the staged rows behind them
+    # start on the next 16 bytes)
+    "fp8_decode_noshared": Workload("fp8_decode_noshared", 2022, "fp8_mxfp4", 7, 1024, 64, 4, 1024, 0, "softmax"),
 }
 
 
