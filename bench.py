@@ -91,6 +91,9 @@ def parse(argv=None):
                          "kernel that scales the HBM byte counters) and exit")
     ap.add_argument("--cpu-seconds", type=float, default=None, help="CPU-oracle sample budget (all cores)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--entry", choices=["capacity", "ep", "gemm"], default=None,
+                    help="measure only the sweep entry of this kind (the capacity-factor layer, one EP "
+                         "rank's share, the dense GEMM) and print its JSON")
     ap.add_argument("--flush-mb", type=int, default=None,
                     help="read this many MiB before each step to evict the 256 MB Infinity Cache and "
                          "the L2s (default: on for T <= 64)")
@@ -192,6 +195,7 @@ KERNEL_SOURCES = {
     ("linear1", "bf16"): ("ffn.hip", "gemm_bf16_dev.hpp") + _COMMON,
     ("linear2", "bf16"): ("ffn.hip", "gemm_bf16_dev.hpp") + _COMMON,
     ("combine", None): ("combine.hip", "combine_dev.hpp", "common.hpp"),
+    ("gemm_fp8_mxfp4", None): ("ffn_fp8.hip", "gemm_fp8_dev.hpp", "common.hpp"),
     ("route", None): ("route.hip", "route_dev.hpp", "common.hpp"),
 }
 
@@ -213,20 +217,22 @@ def sources_hash(kernel=None, mode=None) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_of(w, kernel):
-    """HBM bytes per launch of `kernel` on workload w from profiles/traffic.txt: FETCH_SIZE and
-    WRITE_SIZE (KiB per dispatch, mean over the kernel's dispatches) each scaled by the ratio of
-    known bytes to counter bytes for a plain copy.  None when absent or when the sources changed."""
+def traffic_of(w, kernel, label=None):
+    """HBM bytes per launch of `kernel` on workload w (or the sweep entry `label`) from
+    profiles/traffic.txt: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean over the kernel's
+    dispatches) each scaled by the ratio of known bytes to counter bytes for a plain copy.  None
+    when absent or when the sources changed."""
     path = os.path.join(ROOT, "profiles", "traffic.txt")
     if not os.path.exists(path):
         return None
     cur = sources_hash(kernel, w.mode)
+    name = label or w.name
     with open(path) as fh:
         for line in fh:
             if line.startswith("#") or "=" not in line:
                 continue
             kv = dict(tok.split("=", 1) for tok in line.split() if "=" in tok)
-            if kv.get("workload") == w.name and int(kv.get("T", -1)) == w.T and kv.get("kernel") == kernel:
+            if kv.get("workload") == name and int(kv.get("T", -1)) == w.T and kv.get("kernel") == kernel:
                 if kv.get("sources") != cur:
                     return None
                 return (float(kv["fetch_kib"]) * float(kv["fetch_scale"]) +
@@ -466,14 +472,15 @@ def kernel_times(step, steps):
     return {n: {"launches_per_step": c / steps, "mean_ms": tt / c} for n, (c, tt) in prof.items()}
 
 
-def roofline_flops(kf, kb, mode, kernel, kms):
+def roofline_flops(kf, kb, mode, kernel, kms, w=None, label=None):
     peak_f = PEAK[mode]
     ridge = peak_f * 1e12 / (PEAK_HBM * 1e9)
     if kb > 0 and kf / kb < ridge:
         roof = {"bound": "hbm", "achieved": kb / (kms * 1e-3) / 1e9, "peak": PEAK_HBM, "unit": "GB/s"}
     else:
         roof = {"bound": "mfma", "achieved": kf / (kms * 1e-3) / 1e12, "peak": peak_f, "unit": "TFLOP/s"}
-    roof.update({"frac": roof["achieved"] / roof["peak"], "traffic": None, "traffic_unit": "bytes per launch",
+    traffic = traffic_of(w, kernel, label) if w is not None else None
+    roof.update({"frac": roof["achieved"] / roof["peak"], "traffic": traffic, "traffic_unit": "bytes per launch",
                  "kernel": kernel, "launch_ms": kms, "work_per_launch": {"flop": kf, "bytes": kb}})
     return roof
 
@@ -528,7 +535,7 @@ def measure_capacity(w, inp, d, args, steps, warmup, factor, cpu_s, cpu_1t):
         "ms_per_step": ms, "ms_median": t["median"], "ms_p10": t["p10"], "ms_p90": t["p90"],
         "active_tflops": (f_exp + f_rt) / (ms * 1e-3) / 1e12, "tokens_per_s": w.T / (ms * 1e-3),
         "load": load_stats(w, raw), "kernels": kernels, "bias_update_ms": tb["median"],
-        "roofline": roofline_flops(kf, kb, w.mode, dom, kernels[dom]["mean_ms"]),
+        "roofline": roofline_flops(kf, kb, w.mode, dom, kernels[dom]["mean_ms"], w, f"{w.name}+capacity"),
         "timing": "wall clock over the timed steps; median/p10/p90 from HIP events around each step",
     }
     if not args.no_cpu:
@@ -624,7 +631,7 @@ def measure_ep(w, inp, d, args, steps, warmup, E_local, n_src, cpu_s, cpu_1t):
         "algorithmic_GBps": (wbytes + rows * w.d * (1 + 4 / 128) + rows * w.d * 2) / (ms * 1e-3) / 1e9,
         "mfma_frac": flop / (ms * 1e-3) / 1e12 / PEAK[w.mode], "kernels": kernels,
         "load": {"rows_per_expert_max": int(counts.sum(1).max()), "rows_per_expert_min": int(counts.sum(1).min())},
-        "roofline": roofline_flops(kf, kb, w.mode, dom, kernels[dom]["mean_ms"]),
+        "roofline": roofline_flops(kf, kb, w.mode, dom, kernels[dom]["mean_ms"], w, f"{w.name}+ep"),
         "timing": "wall clock over the timed steps; median/p10/p90 from HIP events around each step",
     }
     if not args.no_cpu:
@@ -701,7 +708,8 @@ def measure_gemm(w, inp, d, args, steps, warmup, M, N, K, cpu_s, cpu_1t):
         "ms_per_step": ms, "ms_median": t["median"], "ms_p10": t["p10"], "ms_p90": t["p90"],
         "tflops": flop / (ms * 1e-3) / 1e12, "mfma_frac": flop / (ms * 1e-3) / 1e12 / PEAK["fp8_mxfp4"],
         "kernels": kernels,
-        "roofline": roofline_flops(flop, kb, "fp8_mxfp4", "gemm_fp8_mxfp4", kernels["gemm_fp8_mxfp4"]["mean_ms"]),
+        "roofline": roofline_flops(flop, kb, "fp8_mxfp4", "gemm_fp8_mxfp4", kernels["gemm_fp8_mxfp4"]["mean_ms"],
+                                   w.with_T(M), f"gemm_{M}x{N}x{K}"),
         "timing": "wall clock over the timed steps; median/p10/p90 from HIP events around each step",
     }
     if not args.no_cpu:
@@ -803,13 +811,15 @@ def main(argv=None):
         print(json.dumps(line_of(e, args)), flush=True)
         return
 
-    # the default run: the headline entry, then the sweep (entries sharing weights together)
+    # the default run: the headline entry, then the sweep (entries sharing weights together);
+    # --entry: that one entry alone
+    sweep = [e for e in SWEEP if e["kind"] == args.entry] if args.entry else SWEEP
     t_max = {}
-    for ent in SWEEP:
+    for ent in sweep:
         key = synth.WORKLOADS[ent["workload"]].seed
         t_max[key] = max(t_max.get(key, 0), ent.get("T", 1))
     entries = []
-    for ent in SWEEP:
+    for ent in sweep:
         kind = ent["kind"]
         w = synth.WORKLOADS[ent["workload"]].with_T(ent.get("T", 1))
         inp, d = cache.get(w, t_max[w.seed])
@@ -832,6 +842,9 @@ def main(argv=None):
         entries.append(e)
         log(f"  done ({time.time() - t_start:.0f}s since start)")
     cache.release()
+    if args.entry:
+        print(json.dumps(entries[0]), flush=True)
+        return
     head = next(e for e in entries if e["headline"])
     sweep = [e for e in entries if e is not head]
     print(json.dumps(line_of(head, args, sweep)), flush=True)
