@@ -57,7 +57,7 @@ int xcd_cus();  // CUs per XCD of the current device
 struct FfnPlan {
     int bm1, bn1, bm2, bn2;  // tile shapes of linear1 (N = 2F) and linear2 (N = d)
     int ntn1, ntn2;          // tiles along N per row tile (incl. K slices on the decode path)
-    bool decode;             // FP8 x FP4 with few rows per group: weight-streaming kernels
+    bool decode;             // FP8 x FP4 below 20 rows per group: weight-streaming kernels
     int ks;                  // decode: K slices of linear1
 };
 FfnPlan ffn_plan(const Shape &s);
