@@ -66,6 +66,22 @@ def test_traffic_only_for_the_measured_sources(tmp_path, monkeypatch):
     assert bench.traffic_of(w, "linear1") is None
 
 
+def test_traffic_of_a_sweep_entry_is_keyed_by_its_label(tmp_path, monkeypatch):
+    """The capacity / EP / dense-GEMM entries run the layer's kernels on other shapes: their
+    counters sit under the entry's label and never stand in for the layer's."""
+    _fake_tree(tmp_path, {"ffn.hip": b"l", "ffn_fp8.hip": b"f", "gemm_fp8_dev.hpp": b"t", "common.hpp": b"c",
+                          "dispatch_dev.hpp": b"d"})
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    w = WORKLOADS["dsv3_fp8fp4"].with_T(8192)
+    h = bench.sources_hash("linear1", w.mode)
+    (tmp_path / "profiles" / "traffic.txt").write_text(
+        f"workload=dsv3_fp8fp4+ep T=8192 kernel=linear1 fetch_kib=50.0 write_kib=5.0 fetch_scale=2.0 "
+        f"write_scale=1.0 dispatches=5 sources={h}\n")
+    assert bench.traffic_of(w, "linear1", "dsv3_fp8fp4+ep") == (50.0 * 2.0 + 5.0) * 1024.0
+    assert bench.traffic_of(w, "linear1") is None  # the layer itself was not measured
+    assert bench.parse(["--entry", "ep"]).entry == "ep"
+
+
 def test_load_statistics():
     w = WORKLOADS["dsv3_fp8fp4"].with_T(64)
     even = np.full(w.G, 2, dtype=np.int64)
