@@ -192,10 +192,14 @@ static __device__ __noinline__ void route_tile8_call(const uint16_t *x, const ui
                                              int b, float *part);
 
 // W8: the 512-thread kernel's items (the tiled router runs only there)
-template <int MODE, bool W8 = false>
+// KIND: -1 every kind of item (inlined callers), else only that kind's code (0 FP8
+// activations, 1 router, 2 selection, 3 histogram, 4 plan, 5 scatter), so that each
+// out-of-line instantiation is a compact function of its own.
+template <int MODE, bool W8 = false, int KIND = -1>
 __device__ __forceinline__ void front_item(const FusedArgs &a, long i, uint8_t *lds, bool &routed) {
+    constexpr bool ALL = KIND < 0;
     const int nr = (int)(a.b_sel - a.b_r);
-    if (i < a.b_r) {  // FP8 activations: a contiguous range of 128-value blocks per item
+    if ((ALL || KIND == 0) && i < a.b_r) {  // FP8 activations: a contiguous range of 128-value blocks per item
         // Coarse items (a counter hand-off each), every thread of the workgroup with 16 loads in
         // flight per lane, device-coherent stores (no fence).
         const long nblocks = (long)a.T * a.d / 128;
@@ -205,7 +209,7 @@ __device__ __forceinline__ void front_item(const FusedArgs &a, long i, uint8_t *
         for (long gid = blk0 * 16 + threadIdx.x; gid - threadIdx.x < blk1 * 16; gid += 16 * nth)
             quant_x_batch<16, true>((const uint16_t *)a.x, blk1, a.xq, a.xs, gid, nth);
         wg_count(a.sync, CNT_QUANT, i);
-    } else if (i < a.b_sel) {  // router
+    } else if ((ALL || KIND == 1) && i < a.b_sel) {  // router
         const int b = (int)(i - a.b_r);
         float *lg = (float *)lds;
         if (W8 && a.router == ROUTER_TILE) {
@@ -227,7 +231,7 @@ __device__ __forceinline__ void front_item(const FusedArgs &a, long i, uint8_t *
                                                         a.idx, a.gate, nullptr, nullptr, a.err);
         }
         wg_count(a.sync, CNT_ROUTE, b);
-    } else if (i < a.b_cnt) {  // sliced router: selection, four tokens (a wave each) or one
+    } else if ((ALL || KIND == 2) && i < a.b_cnt) {  // sliced router: selection, sel4 tokens or one
         if (!routed) {
             wg_counter_wait(a.sync, CNT_ROUTE, nr, a.err);
             routed = true;
@@ -244,13 +248,13 @@ __device__ __forceinline__ void front_item(const FusedArgs &a, long i, uint8_t *
                                    a.gate, nullptr, nullptr, a.err);
         }
         wg_count(a.sync, CNT_SELECT, i - a.b_sel);
-    } else if (i < a.b_plan) {  // dispatch histogram of one block
+    } else if ((ALL || KIND == 3) && i < a.b_plan) {  // dispatch histogram of one block
         if (router_in_slices(a.router)) wg_counter_wait(a.sync, CNT_SELECT, (int)(a.b_cnt - a.b_sel), a.err);
         else wg_counter_wait(a.sync, CNT_ROUTE, nr, a.err);
         count_block<true>(a.idx, a.T, a.k, a.E, (int)(i - a.b_cnt), (unsigned long long *)lds, a.blockcounts,
                           a.err);
         wg_count(a.sync, CNT_COUNT, i - a.b_cnt);
-    } else if (i == a.b_plan) {  // scan, tile plans, cleared row-tile counters
+    } else if ((ALL || KIND == 4) && i == a.b_plan) {  // scan, tile plans, cleared row-tile counters
         int32_t *sh = (int32_t *)lds;
         if (a.nblk == 1) {
             // one dispatch block: histogram, scan and scatter through LDS, then the plan
@@ -271,7 +275,7 @@ __device__ __forceinline__ void front_item(const FusedArgs &a, long i, uint8_t *
         } else {
             wg_flag_raise(a.sync, FLAG_PLAN);
         }
-    } else if (a.nblk > 1 && i < a.b_plan + 1 + a.nblk) {  // dispatch scatter of one block
+    } else if ((ALL || KIND == 5) && a.nblk > 1 && i < a.b_plan + 1 + a.nblk) {  // dispatch scatter of one block
         wg_flag_wait(a.sync, FLAG_PLAN, a.err);
         scatter_block<true>(a.idx, a.T, a.k, a.E, (int)(i - a.b_plan - 1), a.blockcounts, a.s2r, a.r2s,
                             (unsigned long long *)lds);
@@ -382,7 +386,7 @@ static __device__ __noinline__ void route_tile8_call(const uint16_t *x, const ui
 // The steps before the GEMMs, out of line in the 512-thread and decode kernels (inlined
 // there, they would share those kernels' register allocation and spill); the kernel
 // arguments are read back as uniform values.  W8: the 512-thread kernel's items.
-template <int MODE, bool W8 = true>
+template <int MODE, bool W8, int KIND>
 __device__ __noinline__ int front_item_call(FusedArgs a, long i, int routed) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
     static_assert(sizeof(FusedArgs) % 4 == 0, "argument words");
@@ -393,8 +397,33 @@ __device__ __noinline__ int front_item_call(FusedArgs a, long i, int routed) {
     for (int w = 0; w < (int)(sizeof(FusedArgs) / 4); ++w) dst[w] = uni(src[w]);
     const long iu = ((long)uni((int)(i >> 32)) << 32) | (uint32_t)uni((int)i);
     bool r = uni(routed) != 0;
-    front_item<MODE, W8>(u, iu, lds_dyn, r);
+    front_item<MODE, W8, KIND>(u, iu, lds_dyn, r);
     return r ? 1 : 0;
+}
+
+// Item i's kind (see front_item), -1 for the padding items; each kind runs in a function of
+// its own: one function holding every kind measured ~10 us per call even for a padding item
+// (a padding item now makes no call).
+__device__ __forceinline__ int front_kind(const FusedArgs &a, long i) {
+    if (i < a.b_r) return 0;
+    if (i < a.b_sel) return 1;
+    if (i < a.b_cnt) return 2;
+    if (i < a.b_plan) return 3;
+    if (i == a.b_plan) return 4;
+    return a.nblk > 1 && i < a.b_plan + 1 + a.nblk ? 5 : -1;
+}
+template <int MODE, bool W8>
+__device__ __forceinline__ bool front_item_out(const FusedArgs &a, long i, bool routed) {
+    const int r = routed ? 1 : 0;
+    switch (front_kind(a, i)) {
+        case 0: return front_item_call<MODE, W8, 0>(a, i, r) != 0;
+        case 1: return front_item_call<MODE, W8, 1>(a, i, r) != 0;
+        case 2: return front_item_call<MODE, W8, 2>(a, i, r) != 0;
+        case 3: return front_item_call<MODE, W8, 3>(a, i, r) != 0;
+        case 4: return front_item_call<MODE, W8, 4>(a, i, r) != 0;
+        case 5: return front_item_call<MODE, W8, 5>(a, i, r) != 0;
+        default: return routed;
+    }
 }
 
 // ---- tiled variants (bf16, FP8 x FP4, fp32): every item is a workgroup item ------------
@@ -410,7 +439,7 @@ __device__ __forceinline__ void fused_tiled(const FusedArgs &a, uint8_t *lds) {
     bool routed = false;
     for (; i < a.b_end; i += P) {
         __syncthreads();  // the previous item may still read its LDS
-        if constexpr (W8) routed = front_item_call<MODE>(a, i, routed ? 1 : 0) != 0;
+        if constexpr (W8) routed = front_item_out<MODE, true>(a, i, routed);
         else front_item<MODE>(a, i, lds, routed);
     }
     // everything before linear1, then one acquire: the GEMMs read it with cached loads
@@ -580,7 +609,7 @@ __device__ __forceinline__ void fused_decode(const FusedArgs &a, uint8_t *lds) {
     bool routed = false;
     for (; i < a.b_end; i += P) {
         __syncthreads();
-        routed = front_item_call<MODE_FP8, false>(a, i, routed ? 1 : 0) != 0;
+        routed = front_item_out<MODE_FP8, false>(a, i, routed);
     }
     wg_flag_wait(a.sync, FLAG_FRONT, a.err);
     // the plan in LDS: tile prefixes of both GEMMs and the group offsets
