@@ -67,16 +67,16 @@ __global__ __launch_bounds__(64) void fp8_decode_kernel(DecArgs a) {
     for (int tile = blockIdx.x; tile < total; tile += gridDim.x) fp8_decode_tile<LIN1, false, true>(a, tile, a.tile_start, a.offsets);
 }
 
-// Weight ring depth (a divisor of the slice's blocks).  Measured on MI355X at decode shapes
-// (9 groups, T = 1): eight blocks in flight per wave instead of four did not stream faster
-// (linear2, 9 x 7168 x 2048: 19.4-22.9 us against 17.5-19.2 us), so four.
-constexpr int gemv_ring(int, int) { return 4; }
-
 // workgroup tiles: ts[G] / 4 of them
 // ntn: 32-column tiles per row tile and group (the K slices included).  The tile plan --
-// the prefix over groups of ceil(rows / 32) * ntn -- is built in LDS from the offsets.
-template <bool LIN1, int QC, int NB>
-__global__ __launch_bounds__(256) void fp8_gemv_kernel(DecArgs a, int rmax, int ntn) {
+// the prefix over groups of ceil(rows / 32) * ntn -- is built in LDS from the offsets; then
+// each workgroup streams its tiles (blockIdx.x, + gridDim.x, ...).  D: weight blocks in
+// flight per wave -- 4 at two workgroups per CU (eight blocks instead of four streamed no
+// faster there, measured on MI355X), 8 when the two activation buffers take more than half
+// the LDS and one workgroup (a wave per SIMD) keeps the CU's loads in flight alone.
+template <bool LIN1, int QC, int NB, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 4 ? 2 : 1))) void fp8_gemv_kernel(
+    DecArgs a, int rmax, int ntn) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     int32_t *plan = (int32_t *)lds;  // tile starts, then group offsets
     for (int i = threadIdx.x; i <= a.G; i += blockDim.x) plan[a.G + 1 + i] = a.offsets[i];
@@ -87,11 +87,7 @@ __global__ __launch_bounds__(256) void fp8_gemv_kernel(DecArgs a, int rmax, int 
     const int tot = block_exclusive_scan(plan, a.G, plan + 2 * (a.G + 1));
     if (threadIdx.x == 0) plan[a.G] = tot;
     __syncthreads();
-    const int total = plan[a.G] / (4 * QC);
-    for (int wt = blockIdx.x; wt < total; wt += gridDim.x) {
-        fp8_gemv_tile<LIN1, QC, NB, gemv_ring(QC, NB)>(a, wt, rmax, plan, lds);
-        __syncthreads();  // the next tile restages the LDS rows
-    }
+    fp8_gemv_run<LIN1, QC, NB, D>(a, rmax, plan, lds, plan[a.G] / (4 * QC));
 }
 
 __global__ __launch_bounds__(256) void fp8_decode_swiglu_kernel(const float *__restrict__ part, long rows, int F,
@@ -102,10 +98,11 @@ __global__ __launch_bounds__(256) void fp8_decode_swiglu_kernel(const float *__r
 }
 
 // The workgroup decode kernels apply: K slices of whole 1024-wide blocks (at most 2048),
-// column tiles in fours, and the staged rows (at most min(32, T) per tile) and the plan
-// within 96 KB of LDS (32 rows of a 2048-wide slice take 70 KB: two workgroups per CU).
+// column tiles in fours, and the plan, two sets of row_to_slot entries and two buffers of
+// staged rows (at most min(32, T) per tile) within the 160 KB of LDS a workgroup can hold.
+// Up to half of it (2 x 32 rows of a 1024-wide slice take 71 KB) two workgroups share a CU.
 // They build their own tile plan.
-constexpr size_t kGemvLdsMax = 96 * 1024;
+constexpr size_t kGemvLdsMax = 160 * 1024, kGemvLdsTwo = 80 * 1024;
 
 bool fp8_gemv_ok(const Shape &s, const FfnPlan &p) {
     if (!p.decode) return false;
@@ -116,32 +113,38 @@ bool fp8_gemv_ok(const Shape &s, const FfnPlan &p) {
            fp8_gemv_lds_total(G, rmax, kc2) <= kGemvLdsMax;
 }
 
-template <bool LIN1, int QC, int NB>
+template <bool LIN1, int QC, int NB, int D>
 static hipError_t launch_gemv(const char *name, dim3 grid, size_t lds, hipStream_t st, const DecArgs &a, int rmax,
                               int ntn) {
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)fp8_gemv_kernel<LIN1, QC, NB>,
+        hipError_t e = hipFuncSetAttribute((const void *)fp8_gemv_kernel<LIN1, QC, NB, D>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvLdsMax);
         if (e != hipSuccess) return e;
         attr = true;
     }
-    MOE_LAUNCH(name, (fp8_gemv_kernel<LIN1, QC, NB>), grid, dim3(256), lds, st, a, rmax, ntn);
+    MOE_LAUNCH(name, (fp8_gemv_kernel<LIN1, QC, NB, D>), grid, dim3(256), lds, st, a, rmax, ntn);
     return hipGetLastError();
 }
 
-// qc column quads per workgroup tile (1, 2 or 4); nb 256-wide blocks per K slice (4 or 8)
+// qc column quads per workgroup tile (1, 2 or 4); nb 256-wide blocks per K slice (4 or 8);
+// two: two workgroups per CU (the ring of 4), else one (the ring of 8; 2048-wide slices only)
 template <bool LIN1>
-static hipError_t launch_gemv_any(int qc, int nb, const char *name, dim3 grid, size_t lds, hipStream_t st,
+static hipError_t launch_gemv_any(int qc, int nb, bool two, const char *name, dim3 grid, size_t lds, hipStream_t st,
                                   const DecArgs &a, int rmax, int ntn) {
     if (nb == 4) {
-        if (qc == 4) return launch_gemv<LIN1, 4, 4>(name, grid, lds, st, a, rmax, ntn);
-        if (qc == 2) return launch_gemv<LIN1, 2, 4>(name, grid, lds, st, a, rmax, ntn);
-        return launch_gemv<LIN1, 1, 4>(name, grid, lds, st, a, rmax, ntn);
+        if (qc == 4) return launch_gemv<LIN1, 4, 4, 4>(name, grid, lds, st, a, rmax, ntn);
+        if (qc == 2) return launch_gemv<LIN1, 2, 4, 4>(name, grid, lds, st, a, rmax, ntn);
+        return launch_gemv<LIN1, 1, 4, 4>(name, grid, lds, st, a, rmax, ntn);
     }
-    if (qc == 4) return launch_gemv<LIN1, 4, 8>(name, grid, lds, st, a, rmax, ntn);
-    if (qc == 2) return launch_gemv<LIN1, 2, 8>(name, grid, lds, st, a, rmax, ntn);
-    return launch_gemv<LIN1, 1, 8>(name, grid, lds, st, a, rmax, ntn);
+    if (two) {
+        if (qc == 4) return launch_gemv<LIN1, 4, 8, 4>(name, grid, lds, st, a, rmax, ntn);
+        if (qc == 2) return launch_gemv<LIN1, 2, 8, 4>(name, grid, lds, st, a, rmax, ntn);
+        return launch_gemv<LIN1, 1, 8, 4>(name, grid, lds, st, a, rmax, ntn);
+    }
+    if (qc == 4) return launch_gemv<LIN1, 4, 8, 8>(name, grid, lds, st, a, rmax, ntn);
+    if (qc == 2) return launch_gemv<LIN1, 2, 8, 8>(name, grid, lds, st, a, rmax, ntn);
+    return launch_gemv<LIN1, 1, 8, 8>(name, grid, lds, st, a, rmax, ntn);
 }
 
 static hipError_t launch_fp8_decode(const Shape &s, const FfnPlan &p, const uint8_t *w1, const uint8_t *w1s,
@@ -174,12 +177,16 @@ static hipError_t launch_fp8_decode(const Shape &s, const FfnPlan &p, const uint
             while ((ntn / 4) % qc) qc /= 2;
             return qc;
         };
+        // one workgroup per resident slot (two or one per CU), each streaming its tiles
+        const int cus = 8 * xcd_cus();
+        if (cus <= 0) return hipErrorInvalidDevice;
         auto launch = [&](bool lin1, int ntn, const DecArgs &args, size_t lds) {
             const int qc = qc_for(ntn), nb = (lin1 ? kc1 : kc2) / 256;
-            const unsigned tiles = (unsigned)((grid_for(ntn).x / 4 + qc - 1) / qc), cap = 256 * 4;
+            const bool two = nb == 4 || lds <= kGemvLdsTwo;
+            const unsigned tiles = (unsigned)((grid_for(ntn).x / 4 + qc - 1) / qc), cap = (two ? 2 : 1) * cus;
             const dim3 grid(tiles < cap ? tiles : cap);
-            return lin1 ? launch_gemv_any<true>(qc, nb, "linear1", grid, lds, st, args, rmax, ntn)
-                        : launch_gemv_any<false>(qc, nb, "linear2", grid, lds, st, args, rmax, ntn);
+            return lin1 ? launch_gemv_any<true>(qc, nb, two, "linear1", grid, lds, st, args, rmax, ntn)
+                        : launch_gemv_any<false>(qc, nb, two, "linear2", grid, lds, st, args, rmax, ntn);
         };
         hipError_t e = launch(true, p.ntn1, a1, l1);
         if (e != hipSuccess) return e;

@@ -847,154 +847,271 @@ __device__ __forceinline__ void fp8_decode_tile(const DecArgs &a, int tile, cons
 // tile, K slice) and take four neighbouring 32-column tiles, so workgroup tile w covers
 // wave tiles whose order matches fp8_decode_tile's (row tile fastest, then K slice, then
 // column tile) -- every group has a multiple of 4 column tiles, so the group's first
-// workgroup tile is ts[g] / 4.  The group's activation rows for the K slice (at most rmax
-// rows: a group never holds more rows than there are tokens) are copied into LDS by DMA,
-// issued together with the column's e8m0 scales for the slice and the first weight blocks,
-// so their latencies overlap; the weights then are the only global loads, D = 4 blocks of
-// 256 K ahead through a register ring (about 16 KB in flight per wave), running across the
-// QC column quads of the tile.  The tile plan
-// (tile starts and group offsets) sits in LDS, built once per workgroup.  The MFMA
-// operands and their order per K slice are those of fp8_decode_tile: results are identical
-// bit for bit.  K / ks is a multiple of 1024 and at most 2048.
+// workgroup tile is ts[g] / 4.  The MFMA operands and their order per K slice are those of
+// fp8_decode_tile: results are identical bit for bit.  K / ks is a multiple of 1024 and at
+// most 2048.
 //
-// LDS: the tile plan (2 (G + 1) ints), then the staged rows from the next 16-byte boundary
-// (their DMAs and 16-byte reads need it: G + 1 is odd without a shared expert), then their
-// scales.
-__host__ __device__ constexpr size_t fp8_gemv_off_rows(int G) { return ((size_t)8 * (G + 1) + 15) / 16 * 16; }
-__host__ __device__ constexpr size_t fp8_gemv_lds(int G, int rmax, int kc) {
-    return fp8_gemv_off_rows(G) + (size_t)rmax * (kc + 16) + (size_t)rmax * (kc / 128) * 4;
+// Each workgroup runs a sequence of tiles (blockIdx.x, + gridDim.x, ...) as one stream:
+// the weights are the only global loads of the K loop, D blocks of 256 K ahead through a
+// register ring that runs on into the next tile's first blocks, and a tile's activation
+// rows (at most rmax: a group never holds more rows than there are tokens) and their
+// scales are copied into one of two LDS buffers by DMA while the previous tile streams.
+// So a tile starts with its activations in LDS and its first weights in flight, instead of
+// paying a chain of dependent round trips (the row's token, then its activations, then
+// the weights) before its stream starts.  linear1 gathers its rows: the row_to_slot
+// entries of a tile are copied into LDS one tile earlier still.  Every wait on that data
+// rests on loads completing in order: a buffer's DMAs are issued before the weight loads
+// of the tile before it, so the wait for that tile's last weight block covers them, and
+// the barrier between tiles publishes every wave's copies.
+//
+// LDS: the tile plan (2 (G + 1) ints), then at the next 16-byte boundary two sets of 64
+// row_to_slot entries, then two activation buffers, each rmax rows of K / ks + 16 bytes
+// followed by their e8m0-carrying fp32 scales (rounded up to a whole 64-lane copy).
+__host__ __device__ constexpr size_t fp8_gemv_off_src(int G) { return ((size_t)8 * (G + 1) + 15) / 16 * 16; }
+__host__ __device__ constexpr size_t fp8_gemv_off_buf(int G) { return fp8_gemv_off_src(G) + 2 * 64 * 4; }
+__host__ __device__ constexpr size_t fp8_gemv_scales(int rmax, int kc) {
+    return ((size_t)rmax * (kc / 128) + 63) / 64 * 64;
 }
-// the tile plan is built in the same LDS before the rows are staged (scan scratch included)
+__host__ __device__ constexpr size_t fp8_gemv_buf(int rmax, int kc) {
+    return (size_t)rmax * (kc + 16) + fp8_gemv_scales(rmax, kc) * 4;
+}
+__host__ __device__ constexpr size_t fp8_gemv_lds(int G, int rmax, int kc) {
+    return fp8_gemv_off_buf(G) + 2 * fp8_gemv_buf(rmax, kc);
+}
+// the tile plan is built in the same LDS before anything is staged (scan scratch included)
 __host__ __device__ constexpr size_t fp8_gemv_lds_total(int G, int rmax, int kc) {
     const size_t a = fp8_gemv_lds(G, rmax, kc), b = (size_t)2 * (G + 1) * 4 + 256 * 4;
     return a > b ? a : b;
 }
 
-// lds: fp8_gemv_lds(G, rmax, K / ks) bytes; plan[] = tile starts then offsets, loaded.
-// QC column quads (4 x 32 columns each) per workgroup tile, NB 256-wide K blocks per slice
-// (K / ks = 256 NB), D blocks in the weight ring (D divides NB).  Block t of the tile is K
-// block t % NB of quad t / NB: each quad's 32 weight rows are streamed through in turn
-// (measured on MI355X, 9 x 4096 x 7168: 32.5 us in this order against 43 us when every K
-// block visits all four quads first), one accumulator per quad, the stores at the end (a
-// store between the loads would break the in-order count the ring waits on).
-template <bool LIN1, int QC, int NB, int D>
-__device__ __forceinline__ void fp8_gemv_tile(const DecArgs &a, int wt, int rmax, const int32_t *plan,
-                                              uint8_t *lds) {
-    constexpr int KC = NB * 256, RS = KC + 16, NSC = KC / 128, NBT = QC * NB;
-    static_assert(NB == 4 || NB == 8, "K slices of 1024 or 2048");
-    static_assert(NB % D == 0 && D >= 2, "ring slot of block t is t % D");
-    const int32_t *ts = plan, *offs = plan + a.G + 1;
-    int lo = 0, hi = a.G - 1;
+struct GemvTile {
+    int g, row0, nrows, ksl, qc;
+};
+
+// Workgroup tile wt of the plan (tile starts, then group offsets); wave-uniform.
+template <int QC>
+__device__ __forceinline__ GemvTile gemv_tile(const int32_t *plan, int G, int ks, int rmax, int wt) {
+    const int32_t *ts = plan, *offs = plan + G + 1;
+    int lo = 0, hi = G - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (ts[mid] / (4 * QC) <= wt) lo = mid; else hi = mid - 1;
     }
-    const int g = lo;
-    const int rb = offs[g], cnt = offs[g + 1] - rb;
-    const int mtiles = (cnt + 31) / 32, local = wt - ts[g] / (4 * QC);
+    GemvTile t;
+    t.g = __builtin_amdgcn_readfirstlane(lo);
+    const int rb = __builtin_amdgcn_readfirstlane(offs[t.g]);
+    const int cnt = __builtin_amdgcn_readfirstlane(offs[t.g + 1]) - rb;
+    const int mtiles = (cnt + 31) / 32, local = wt - __builtin_amdgcn_readfirstlane(ts[t.g]) / (4 * QC);
     const int mt = local % mtiles, rest = local / mtiles;
-    const int ksl = rest % a.ks, qc = rest / a.ks;
-    const int row0 = rb + mt * 32;
-    int nrows = min(32, cnt - mt * 32);
-    nrows = nrows < rmax ? nrows : rmax;  // rmax >= nrows whenever the routing is valid
-    const int kbeg = ksl * KC;
-    uint8_t *la = lds + fp8_gemv_off_rows(a.G);
-    float *lsa = (float *)(la + (size_t)rmax * RS);
-    const int lane = lane_id(), kh = lane >> 5, r = lane & 31, wave = threadIdx.x >> 6;
+    t.ksl = rest % ks;
+    t.qc = rest / ks;
+    t.row0 = rb + mt * 32;
+    const int n = min(32, cnt - mt * 32);
+    t.nrows = n < rmax ? n : rmax;  // rmax >= nrows whenever the routing is valid
+    return t;
+}
 
-    // 1. activation rows of the slice: one 1 KB DMA per (row, chunk), rows dealt to waves
-    for (int rw = wave; rw < nrows; rw += 4) {
-        const long src = LIN1 ? row_token(row0 + rw, a.row_to_slot, a.T, a.k) : (long)row0 + rw;
-#pragma unroll
-        for (int c = 0; c < KC / 1024; ++c)
-            lds_dma16(a.A + (size_t)src * a.K + kbeg + c * 1024 + lane * 16, la + rw * RS + c * 1024);
-    }
-    // activation scales: nrows x NSC of them (at most 32 x 16), two per thread of the 256
-    static_assert(32 * NSC <= 2 * 256, "two scales per thread cover the tile");
-    float sav[2] = {0.0f, 0.0f};
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int sidx = threadIdx.x + 256 * u;
-        if (sidx < nrows * NSC) {
-            const int rw = sidx / NSC, j = sidx % NSC;
-            const long src = LIN1 ? row_token(row0 + rw, a.row_to_slot, a.T, a.k) : (long)row0 + rw;
-            sav[u] = a.As[src * (a.K / 128) + kbeg / 128 + j];
+// The workgroup barrier of the weight stream: s_barrier with compiler fences only.  The
+// memory-model barrier would wait for every outstanding load -- the LDS copies count as
+// LDS writes -- and so drain the weight ring at each tile; here every wave waits for its
+// own copies itself before the barrier (no LDS is written otherwise).
+__device__ __forceinline__ void gemv_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// lds: fp8_gemv_lds_total(G, rmax, K / ks) bytes, the plan loaded; total workgroup tiles.
+// QC column quads (4 x 32 columns each) per workgroup tile, NB 256-wide K blocks per slice
+// (K / ks = 256 NB), D blocks in the weight ring (D divides NB).  Block t of a tile is K
+// block t % NB of quad t / NB: each quad's 32 weight rows are streamed through in turn
+// (measured on MI355X, 9 x 4096 x 7168: 32.5 us in this order against 43 us when every K
+// block visits all four quads first), one accumulator per quad.
+template <bool LIN1, int QC, int NB, int D>
+__device__ __forceinline__ void fp8_gemv_run(const DecArgs &a, int rmax, const int32_t *plan, uint8_t *lds,
+                                             int total) {
+    constexpr int KC = NB * 256, RS = KC + 16, NSC = KC / 128, NBT = QC * NB;
+    constexpr int LPB = 5;  // global loads per weight block: four 16-byte code loads, one 8-byte scale load
+    static_assert(NB == 4 || NB == 8, "K slices of 1024 or 2048");
+    static_assert(NB % D == 0 && D >= 2, "ring slot of block t is t % D");
+    const int P = gridDim.x, b0 = blockIdx.x;
+    if (b0 >= total) return;
+    const int ntile = (total - 1 - b0) / P + 1;
+    const int lane = lane_id(), kh = lane >> 5, r = lane & 31, wave = threadIdx.x >> 6;
+    const size_t BUF = fp8_gemv_buf(rmax, KC), SCA = (size_t)rmax * RS;
+    int32_t *srcb = (int32_t *)(lds + fp8_gemv_off_src(a.G));
+    uint8_t *buf0 = lds + fp8_gemv_off_buf(a.G);
+    const long tk = (long)a.T * a.k;
+
+    // the row_to_slot entries of tile n's rows into srcb[n % 2] (lanes past the rows and
+    // 32..63 re-read the first row)
+    auto copy_src = [&](int n, const GemvTile &t) {
+        if (LIN1 && wave == 0) {
+            const long rr = t.row0 + (r < t.nrows ? r : 0);
+            lds_dma4_hidden(a.row_to_slot + (rr < tk ? rr : 0), (uint8_t *)(srcb + (n & 1) * 64));
         }
-    }
-    // 2. weight blocks (4 x 16 B codes and 2 scale dwords per lane) through the ring
-    const long n0 = (long)(4 * qc * QC + wave) * 32 + r;  // this lane's column in quad 0
-    const uint8_t *pb0 = a.B + ((long)g * a.N + n0) * (a.K / 2) + kbeg / 2 + 16 * kh;
-    const uint8_t *ps0 = a.Bs + ((long)g * a.N + n0) * (a.K / 32) + kbeg / 32;
+    };
+    // token feeding row rw of tile n (rows of the shared expert follow the routed ones);
+    // clamped as row_token clamps.  The first tile's entries come from one load per lane
+    // (raw0, lane r: row r) -- no copy to wait for before the tile's own copies -- later
+    // tiles' from the entries staged in LDS.
+    int raw0 = 0;
+    auto src_of = [&](int n, const GemvTile &t, int rw) -> long {
+        const long rr = (long)t.row0 + rw;
+        if (!LIN1) return rr;
+        long tok;
+        if (rr < tk) {
+            long s = n == 0 ? __shfl(raw0, rw, 64) : srcb[(n & 1) * 64 + rw];
+            s = s < 0 ? 0 : (s >= tk ? tk - 1 : s);
+            tok = s / a.k;
+        } else {
+            tok = rr - tk;
+        }
+        return tok < 0 ? 0 : (tok >= a.T ? a.T - 1 : tok);
+    };
+    // tile n's activation rows (1 KB copies, rows dealt to waves) and scales (64 per copy)
+    // into buffer n % 2
+    auto copy_act = [&](int n, const GemvTile &t) {
+        uint8_t *la = buf0 + (n & 1) * BUF;
+        const int kbeg = t.ksl * KC;
+        for (int rw = wave; rw < t.nrows; rw += 4) {
+            const long s = src_of(n, t, rw);
+            const int shi = __builtin_amdgcn_readfirstlane((int)(s >> 32)),
+                      slo = __builtin_amdgcn_readfirstlane((int)s);
+            const long src = ((long)shi << 32) | (uint32_t)slo;
+#pragma unroll
+            for (int c = 0; c < KC / 1024; ++c)
+                lds_dma16_hidden(a.A + (size_t)src * a.K + kbeg + c * 1024 + lane * 16, la + rw * RS + c * 1024);
+        }
+        const int nsc = t.nrows * NSC;
+        float *lsa = (float *)(la + SCA);
+        for (int q = wave; q * 64 < nsc; q += 4) {
+            const int idx = q * 64 + lane < nsc ? q * 64 + lane : 0;
+            const long src = src_of(n, t, idx / NSC);
+            lds_dma4_hidden(a.As + src * (a.K / 128) + kbeg / 128 + idx % NSC, (uint8_t *)(lsa + q * 64));
+        }
+    };
     const long qsb = 128L * (a.K / 2), qss = 128L * (a.K / 32);  // the next quad: 128 columns on
+    // this lane's weight codes and scales in quad 0 of a tile
+    auto wptr = [&](const GemvTile &t, const uint8_t *&pb, const uint8_t *&ps) {
+        const long n0 = (long)(4 * t.qc * QC + wave) * 32 + r;
+        const int kbeg = t.ksl * KC;
+        pb = a.B + ((long)t.g * a.N + n0) * (a.K / 2) + kbeg / 2 + 16 * kh;
+        ps = a.Bs + ((long)t.g * a.N + n0) * (a.K / 32) + kbeg / 32;
+    };
+
+    // after the last tile the "next" blocks re-read the last quad's blocks NB - D .. NB - 2,
+    // read moments before (in bounds, cached, unused)
+    const uint8_t *pbC, *psC, *pbN, *psN;
+    auto wptr_last = [&](const uint8_t *&pb, const uint8_t *&ps) {
+        pb = pbC + (QC - 1) * qsb + (NB - D) * 128;
+        ps = psC + (QC - 1) * qss + (NB - D) * 8;
+    };
     i32x4 bq[D][4];
-    uint32_t sbw[D][2];
-    // block t_ of the tile into ring slot slot; past the last block it re-reads the last one
-    // (in bounds, never used)
-#define GEMV_LOAD(slot, t_)                                                                         \
-    do {                                                                                            \
-        int tt_ = (t_) < NBT ? (t_) : NBT - 1;                                                      \
-        asm volatile("" : "+v"(tt_)); /* opaque: the loads issue here, are not hoisted */           \
-        const int c_ = tt_ / NB, i_ = tt_ % NB;                                                     \
-        const uint8_t *pb_ = pb0 + c_ * qsb + i_ * 128;                                             \
-        const uint8_t *ps_ = ps0 + c_ * qss + i_ * 8;                                               \
+    uint2 sbw[D];
+    // block tl of the stream position: tl < NBT the current tile's block tl, else the next
+    // tile's block tl - NBT
+#define GEMV_LOAD(slot, tl_)                                                                      \
+    do {                                                                                          \
+        int tl = (tl_);                                                                           \
+        asm volatile("" : "+v"(tl)); /* opaque: the loads issue here, are not hoisted */          \
+        const bool nx_ = tl >= NBT;                                                               \
+        const int tt_ = nx_ ? tl - NBT : tl;                                                      \
+        const int c_ = tt_ / NB, i_ = tt_ % NB;                                                   \
+        const uint8_t *pb_ = (nx_ ? pbN : pbC) + c_ * qsb + i_ * 128;                             \
+        const uint8_t *ps_ = (nx_ ? psN : psC) + c_ * qss + i_ * 8;                               \
         _Pragma("unroll") for (int u = 0; u < 4; ++u) bq[slot][u] = *(const i32x4 *)(pb_ + 32 * u); \
-        sbw[slot][0] = *(const uint32_t *)(ps_);                                                    \
-        sbw[slot][1] = *(const uint32_t *)(ps_ + 4);                                                \
+        sbw[slot] = *(const uint2 *)ps_;                                                          \
     } while (0)
+
+    GemvTile cur = gemv_tile<QC>(plan, a.G, a.ks, rmax, b0);
+    GemvTile nxt = ntile > 1 ? gemv_tile<QC>(plan, a.G, a.ks, rmax, b0 + P) : cur;
+    if (LIN1) {
+        const long rr = cur.row0 + (r < cur.nrows ? r : 0);
+        raw0 = a.row_to_slot[rr < tk ? rr : 0];
+    }
+    copy_act(0, cur);
+    if (ntile > 1) copy_src(1, nxt);
+    wptr(cur, pbC, psC);
+    if (ntile > 1) wptr(nxt, pbN, psN);
+    else wptr_last(pbN, psN);
 #pragma unroll
     for (int j = 0; j < D - 1; ++j) GEMV_LOAD(j, j);
-    // everything but the weight blocks has landed (loads complete in order)
-    wait_vmcnt<(D - 1) * 6>();
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-        if (threadIdx.x + 256 * u < nrows * NSC) lsa[threadIdx.x + 256 * u] = sav[u];
-    __syncthreads();
+    // tile 0's copies and tile 1's row_to_slot entries landed: everything older than the
+    // ring's loads
+    wait_vmcnt<(D - 1) * LPB>();
+    gemv_barrier();
 
-    const int rr = r < nrows ? r : 0;
-    const uint8_t *arow = la + rr * RS;
-    const float *asr = lsa + rr * NSC;
-    f32x16 acc[QC];
+    for (int n = 0; n < ntile; ++n) {
+        // the next tile's activations (their row_to_slot entries landed before this tile
+        // began), then the row_to_slot entries of the tile after it into the set this tile's
+        // copies are done with
+        GemvTile nn = nxt;
+        if (n + 1 < ntile) {
+            copy_act(n + 1, nxt);
+            if (n + 2 < ntile) {
+                nn = gemv_tile<QC>(plan, a.G, a.ks, rmax, b0 + (n + 2) * P);
+                copy_src(n + 2, nn);
+            }
+        }
+        const uint8_t *la = buf0 + (n & 1) * BUF;
+        const int rr = r < cur.nrows ? r : 0;
+        const uint8_t *arow = la + rr * RS;
+        const float *asr = (const float *)(la + SCA) + rr * NSC;
+        f32x16 acc[QC];
 #pragma unroll
-    for (int c = 0; c < QC; ++c) acc[c] = (f32x16){};
-    // an opaque trip count keeps the K loop a loop: unrolled over a whole tile, the compiler
-    // hoists the ring's loads and runs out of registers
-    int nbr = NB;
-    asm volatile("" : "+s"(nbr));
+        for (int c = 0; c < QC; ++c) acc[c] = (f32x16){};
+        // an opaque trip count keeps the K loop a loop: unrolled over a whole tile, the
+        // compiler hoists the ring's loads and runs out of registers
+        int nbr = NB;
+        asm volatile("" : "+s"(nbr));
 #pragma unroll
-    for (int c = 0; c < QC; ++c) {
-        for (int i0 = 0; i0 < nbr; i0 += D) {
+        for (int c = 0; c < QC; ++c) {
+            for (int i0 = 0; i0 < nbr; i0 += D) {
 #pragma unroll
-            for (int j = 0; j < D; ++j) {
-                const int i = i0 + j, t = c * NB + i;
-                GEMV_LOAD((j + D - 1) % D, t + D - 1);  // into the slot block t - 1 freed
-                wait_vmcnt<(D - 1) * 6>();               // block t landed: 6 loads per block, in order
+                for (int j = 0; j < D; ++j) {
+                    const int i = i0 + j, t = c * NB + i;
+                    GEMV_LOAD((j + D - 1) % D, t + D - 1);  // into the slot block t - 1 freed
+                    wait_vmcnt<(D - 1) * LPB>();             // block t landed: LPB loads per block, in order
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const i32x4 lo4 = *(const i32x4 *)(arow + i * 256 + 64 * u + 16 * kh);
-                    const i32x4 hi4 = *(const i32x4 *)(arow + i * 256 + 64 * u + 32 + 16 * kh);
-                    i32x8 av = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-                    i32x8 bv = {bq[j][u][0], bq[j][u][1], bq[j][u][2], bq[j][u][3], 0, 0, 0, 0};
-                    const int sb = (int)((sbw[j][u >> 1] >> (8 * (2 * (u & 1) + kh))) & 0xFF);
-                    const int sa = (int)((__float_as_uint(asr[2 * i + (u >> 1)]) >> 23) & 0xFF);
-                    acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[c], 0, 4, 0, sa, 0, sb);
+                    for (int u = 0; u < 4; ++u) {
+                        const i32x4 lo4 = *(const i32x4 *)(arow + i * 256 + 64 * u + 16 * kh);
+                        const i32x4 hi4 = *(const i32x4 *)(arow + i * 256 + 64 * u + 32 + 16 * kh);
+                        i32x8 av = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+                        i32x8 bv = {bq[j][u][0], bq[j][u][1], bq[j][u][2], bq[j][u][3], 0, 0, 0, 0};
+                        const uint32_t sw = (u >> 1) ? sbw[j].y : sbw[j].x;
+                        const int sb = (int)((sw >> (8 * (2 * (u & 1) + kh))) & 0xFF);
+                        const int sa = (int)((__float_as_uint(asr[2 * i + (u >> 1)]) >> 23) & 0xFF);
+                        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[c], 0, 4, 0, sa, 0, sb);
+                    }
                 }
             }
         }
+        // this tile's last block landed, and with it every copy issued before it (the next
+        // tile's activations); the stores below come after the wait
+        wait_vmcnt<(D - 1) * LPB>();
+#pragma unroll
+        for (int c = 0; c < QC; ++c) {
+            const long ncol = (long)(4 * cur.qc * QC + wave) * 32 + r + (long)c * 128;
+#pragma unroll
+            for (int qq = 0; qq < 16; ++qq) {
+                const int row = 8 * (qq >> 2) + 4 * kh + (qq & 3);
+                if (row >= cur.nrows) continue;
+                const long orow = cur.row0 + row;
+                if (LIN1) a.part[((long)cur.ksl * a.rows + orow) * a.N + ncol] = acc[c][qq];
+                else a.Y[orow * a.N + ncol] = f32_to_bf16(acc[c][qq]);
+            }
+        }
+        cur = nxt;
+        nxt = nn;
+        pbC = pbN;
+        psC = psN;
+        if (n + 2 < ntile) wptr(nxt, pbN, psN);
+        else wptr_last(pbN, psN);
+        gemv_barrier();  // every wave's copies for the next tile landed; this tile's buffer is free
     }
     wait_vmcnt<0>();
 #undef GEMV_LOAD
-#pragma unroll
-    for (int c = 0; c < QC; ++c) {
-        const long n = n0 + (long)c * 128;
-#pragma unroll
-        for (int qq = 0; qq < 16; ++qq) {
-            const int row = 8 * (qq >> 2) + 4 * kh + (qq & 3);
-            if (row >= nrows) continue;
-            const long orow = row0 + row;
-            if (LIN1) a.part[((long)ksl * a.rows + orow) * a.N + n] = acc[c][qq];
-            else a.Y[orow * a.N + n] = f32_to_bf16(acc[c][qq]);
-        }
-    }
 }
 
 // Sums the K slices of linear1 in order, applies SwiGLU and quantises h to e4m3 with one
