@@ -911,6 +911,30 @@ __device__ __forceinline__ GemvTile gemv_tile(const int32_t *plan, int G, int ks
     return t;
 }
 
+// The LDS copies of the weight stream, written as instructions the compiler does not see.
+// It treats a pending global_load_lds as a FLAT access that may touch LDS and then answers
+// every vmcnt wait it needs -- also the ones for the register loads of the weight ring --
+// with vmcnt(0) until one has retired it; at a loop head this holds on every trip.  Hidden
+// from it, the copies only make its own waits stricter than needed (loads complete in
+// order), never too weak, and the caller waits for them itself.  M0 holds the LDS address;
+// the LDS DMA reads M0 one wait state after the SALU write.  No output registers.  (m0 is
+// reserved: nothing keeps a value in it across these -- every other LDS copy sets it right
+// before its instruction.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ int lds_u32(const void *lds_block) {
+    return __builtin_amdgcn_readfirstlane((int)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_block);
+}
+__device__ __forceinline__ void lds_dma16_hidden(const void *g, uint8_t *lds_block) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_u32(lds_block))
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4_hidden(const void *g, uint8_t *lds_block) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_u32(lds_block))
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // The workgroup barrier of the weight stream: s_barrier with compiler fences only.  The
 // memory-model barrier would wait for every outstanding load -- the LDS copies count as
 // LDS writes -- and so drain the weight ring at each tile; here every wave waits for its
