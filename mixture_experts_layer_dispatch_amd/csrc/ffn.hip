@@ -72,12 +72,12 @@ FfnPlan ffn_plan(const Shape &s) {
         return p;
     }
     p.ks = 1;
-    if (s.mode == MODE_FP8X8) {  // the 4-wave FP8 x FP8 tiles: 128 x 256 (linear1), 128 x 128
-        p.bm1 = p.bm2 = 128;
+    if (s.mode == MODE_FP8X8) {  // the 4-wave FP8 x FP8 tiles: 128 x 256 (linear1), 128 x 256
+        p.bm1 = p.bm2 = 128;     // (linear2; 128 x 128 when d is no multiple of 256)
         p.bn1 = 256;
-        p.bn2 = 128;
+        p.bn2 = s.d % 256 == 0 ? 256 : 128;
         p.ntn1 = s.F / 128;
-        p.ntn2 = s.d / 128;
+        p.ntn2 = s.d / p.bn2;
         return p;
     }
     p.bm1 = p.bm2 = per_group >= 160 ? 256 : 128;

@@ -27,7 +27,7 @@ static hipError_t launch_fp8x8(const char *name, dim3 grid, const Fp8Args &a, hi
     return hipGetLastError();
 }
 
-// linear1 + SwiGLU (128 x 256 tiles: 128 gate + 128 up columns), then linear2 (128 x 128),
+// linear1 + SwiGLU (128 x 256 tiles: 128 gate + 128 up columns), then linear2 (128 x p.bn2),
 // over the tile plans ts1, ts2 of the dispatched groups.
 hipError_t launch_fp8x8_ffn(const Shape &s, const FfnPlan &p, const uint8_t *w1, const float *w1s, const uint8_t *w2,
                             const float *w2s, const uint8_t *xq, const float *xs, const int32_t *offsets,
@@ -45,6 +45,7 @@ hipError_t launch_fp8x8_ffn(const Shape &s, const FfnPlan &p, const uint8_t *w1,
                         s.d, G, s.F};
     hipError_t e = launch_fp8x8<true, true, 256>("linear1", grid_for(p.bm1, p.ntn1), a1, st);
     if (e != hipSuccess) return e;
+    if (p.bn2 == 256) return launch_fp8x8<false, false, 256>("linear2", grid_for(p.bm2, p.ntn2), a2, st);
     return launch_fp8x8<false, false, 128>("linear2", grid_for(p.bm2, p.ntn2), a2, st);
 }
 

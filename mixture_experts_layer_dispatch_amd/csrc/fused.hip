@@ -12,7 +12,7 @@ namespace moe {
 hipError_t launch_fused_bf16(FusedArgs &a, int bm, int bn2, size_t lds, int cu_limit, hipStream_t st);
 hipError_t launch_fused_fp8(FusedArgs &a, bool decode, int bm, int bn2, bool w8, size_t lds, int cu_limit,
                             hipStream_t st);
-hipError_t launch_fused_fp8x8(FusedArgs &a, size_t lds, int cu_limit, hipStream_t st);
+hipError_t launch_fused_fp8x8(FusedArgs &a, int bn2, size_t lds, int cu_limit, hipStream_t st);
 
 namespace {
 
@@ -152,7 +152,7 @@ hipError_t launch_layer_fused(const Shape &s, const FfnPlan &p, FusedArgs &a, in
     const size_t lds = fused_lds_bytes(s, p);
     if (s.mode == MODE_F32) return launch_fused_kernel<MODE_F32, 128, 128>(a, lds, cu_limit, st);
     if (s.mode == MODE_BF16) return launch_fused_bf16(a, p.bm1, p.bn2, lds, cu_limit, st);
-    if (s.mode == MODE_FP8X8) return launch_fused_fp8x8(a, lds, cu_limit, st);
+    if (s.mode == MODE_FP8X8) return launch_fused_fp8x8(a, p.bn2, lds, cu_limit, st);
     return launch_fused_fp8(a, p.decode, p.bm1, p.bn2, fp8_w8(s), lds, cu_limit, st);
 }
 

@@ -558,7 +558,7 @@ __device__ __forceinline__ void fused_tiled(const FusedArgs &a, uint8_t *lds) {
                 } else if constexpr (MODE == MODE_FP8X8) {
                     Fp8Args g = {(const uint8_t *)a.h, a.hs, nullptr, (const uint8_t *)a.w2, (const uint8_t *)a.w2s,
                                  a.yperm, nullptr, a.offsets, a.ts2, a.T, a.k, a.F, a.d, a.d, a.G, a.F};
-                    fp8x8_tile<false, false, 128>(g, tile, lds);
+                    fp8x8_tile<false, false, BN2>(g, tile, lds);
                 } else {
                     Fp8Args g = {(const uint8_t *)a.h, a.hs, nullptr, (const uint8_t *)a.w2, (const uint8_t *)a.w2s,
                                  a.yperm, nullptr, a.offsets, a.ts2, a.T, a.k, a.F, a.d, a.d, a.G, a.F};

@@ -14,8 +14,9 @@ hipError_t launch_fused_fp8(FusedArgs &a, bool decode, int bm, int bn2, bool w8,
     return launch_fused_kernel<MODE_FP8, 128, 128>(a, lds, cu_limit, st);
 }
 
-// FP8 x FP8: the 256-thread kernel with the 128-row FP8 x FP8 tiles
-hipError_t launch_fused_fp8x8(FusedArgs &a, size_t lds, int cu_limit, hipStream_t st) {
+// FP8 x FP8: the 256-thread kernel with the 128-row FP8 x FP8 tiles (linear2 bn2 columns wide)
+hipError_t launch_fused_fp8x8(FusedArgs &a, int bn2, size_t lds, int cu_limit, hipStream_t st) {
+    if (bn2 == 256) return launch_fused_kernel<MODE_FP8X8, 128, 256>(a, lds, cu_limit, st);
     return launch_fused_kernel<MODE_FP8X8, 128, 128>(a, lds, cu_limit, st);
 }
 

@@ -98,16 +98,6 @@ __device__ __forceinline__ void fp8x8_tile(const Fp8Args &a, int tile, uint8_t *
             sdst[q] = OFF_SPARE;
         }
     }
-    auto dma = [&](int s) {  // stage s (clamped: the tail re-loads the last stage into a free buffer)
-        uint8_t *st = lds + (s % NS) * STAGE;
-        const int kt = s < KB ? s : KB - 1;
-#pragma unroll
-        for (int q = 0; q < PA; ++q) lds_dma16(pa[q] + kt * 128, st + (wave * PA + q) * 1024);
-#pragma unroll
-        for (int q = 0; q < PB; ++q) lds_dma16(pb[q] + kt * 128, st + OFF_B + (wave * PB + q) * 1024);
-#pragma unroll
-        for (int q = 0; q < PS; ++q) lds_dma4(psc[q] + kt * 4, st + sdst[q]);
-    };
 
     // ---- fragments: A of rows arow[i], B of tile rows brow[j]; for k64 half h, lane half kh
     // holds K {16 kh .. 16 kh + 15} and {32 + 16 kh .. 32 + 16 kh + 15} of the step (the fp8
@@ -120,6 +110,17 @@ __device__ __forceinline__ void fp8x8_tile(const Fp8Args &a, int tile, uint8_t *
         if (SWIGLU) brow[j] = (j < TN / 2 ? wn * 64 + j * 32 : BN / 2 + wn * 64 + (j - TN / 2) * 32) + (lane & 31);
         else brow[j] = wn * (BN / 2) + j * 32 + (lane & 31);
     }
+    int aoff[2][TM][2], boff[2][TN][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) aoff[h][i][c] = sw128(arow[i], h * 4 + 2 * c + khalf);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) boff[h][j][c] = OFF_B + sw128(brow[j], h * 4 + 2 * c + khalf);
+        }
+    }
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -127,47 +128,114 @@ __device__ __forceinline__ void fp8x8_tile(const Fp8Args &a, int tile, uint8_t *
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){};
 
+    // One wave per SIMD, so the wave interleaves its own work: the k64 half h = 0 of stage kt
+    // is multiplied while the DMAs of stage kt + 2 and the half h = 1 fragments are issued
+    // between its MFMAs; after the one barrier per stage (stage kt + 1 published, every wave
+    // done with stage kt), half h = 1 is multiplied while stage kt + 1's h = 0 fragments are
+    // read.  Every accumulator still takes its MFMAs stage by stage, h = 0 before h = 1, with
+    // the same operands and scales, so the results are those of the plain pipeline.
+#define X8_DMA(q, stg, kt_)                                                                          \
+    do {                                                                                             \
+        uint8_t *s_ = lds + (stg) * STAGE;                                                           \
+        const int kt2_ = (kt_);                                                                      \
+        if ((q) < PA) lds_dma16(pa[(q) < PA ? (q) : 0] + kt2_ * 128, s_ + (wave * PA + (q)) * 1024); \
+        else if ((q) < PA + PB)                                                                      \
+            lds_dma16(pb[(q) >= PA && (q) < PA + PB ? (q) - PA : 0] + kt2_ * 128,                    \
+                      s_ + OFF_B + (wave * PB + (q) - PA) * 1024);                                   \
+        else {                                                                                       \
+            const int p_ = (q) - PA - PB < PS ? (q) - PA - PB : 0;                                   \
+            lds_dma4(psc[p_] + kt2_ * 4, s_ + sdst[p_]);                                             \
+        }                                                                                            \
+    } while (0)
+#define X8_FRAG(FA, FB, u, stg, h)                                                                   \
+    do {                                                                                             \
+        const uint8_t *s_ = lds + (stg) * STAGE;                                                     \
+        if ((u) < 2 * TM) {                                                                          \
+            const int i_ = ((u) >> 1) < TM ? ((u) >> 1) : 0, c_ = (u) & 1;                          \
+            FA[i_][c_] = *(const i32x4 *)(s_ + aoff[h][i_][c_]);                                     \
+        } else {                                                                                     \
+            const int j_ = (((u) - 2 * TM) >> 1) < TN ? (((u) - 2 * TM) >> 1) : 0, c_ = (u) & 1;     \
+            FB[j_][c_] = *(const i32x4 *)(s_ + boff[h][j_][c_]);                                     \
+        }                                                                                            \
+    } while (0)
+#define X8_SCALES(SA, SB, stg)                                                                       \
+    do {                                                                                             \
+        const uint8_t *s_ = lds + (stg) * STAGE;                                                     \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i)                                               \
+            SA[i] = (int)((*(const uint32_t *)(s_ + OFF_SA + arow[i] * 4) >> 23) & 0xFF);            \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j)                                               \
+            SB[j] = (int)((*(const uint32_t *)(s_ + OFF_SB + brow[j] * 4) >> 23) & 0xFF);            \
+    } while (0)
+#define X8_MFMA(FA, FB, m)                                                                           \
+    do {                                                                                             \
+        const int i_ = (m) / TN, j_ = (m) % TN;                                                      \
+        const i32x8 av_ = {FA[i_][0][0], FA[i_][0][1], FA[i_][0][2], FA[i_][0][3],                   \
+                           FA[i_][1][0], FA[i_][1][1], FA[i_][1][2], FA[i_][1][3]};                  \
+        const i32x8 bv_ = {FB[j_][0][0], FB[j_][0][1], FB[j_][0][2], FB[j_][0][3],                   \
+                           FB[j_][1][0], FB[j_][1][1], FB[j_][1][2], FB[j_][1][3]};                  \
+        acc[i_][j_] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av_, bv_, acc[i_][j_], 0, 0, 0, \
+                                                                      sa0[i_], 0, sb0[j_]);          \
+    } while (0)
+#define X8_BARRIER()                           \
+    do {                                       \
+        asm volatile("" ::: "memory");         \
+        __builtin_amdgcn_s_barrier();          \
+        asm volatile("" ::: "memory");         \
+    } while (0)
+
+    constexpr int NR = 2 * TM + 2 * TN;  // fragment reads per k64 half
+    constexpr int NG = TM * TN;          // issue groups per k64 half (one MFMA each)
+    i32x4 fa0[TM][2], fb0[TN][2], fa1[TM][2], fb1[TN][2];
+    int sa0[TM], sb0[TN];
+
 #pragma unroll
-    for (int s0 = 0; s0 < PD; ++s0) dma(s0);
+    for (int s0 = 0; s0 < PD; ++s0)
+#pragma unroll
+        for (int q = 0; q < PER; ++q) X8_DMA(q, s0, s0 < KB ? s0 : KB - 1);
+    wait_vmcnt<(PD - 1) * PER>();  // this wave's loads of stage 0 have landed
+    X8_BARRIER();                  // ... and every wave's
+#pragma unroll
+    for (int u = 0; u < NR; ++u) X8_FRAG(fa0, fb0, u, 0, 0);
+    X8_SCALES(sa0, sb0, 0);
+
     for (int kt = 0; kt < KB; ++kt) {
-        wait_vmcnt<(PD - 1) * PER>();  // this wave's loads of stage kt have landed
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();  // ... and every wave's; all are done with stage kt - 1
-        asm volatile("" ::: "memory");
-        dma(kt + PD);                  // into the buffer stage kt - 1 used
-        const uint8_t *st = lds + (kt % NS) * STAGE;
-        int sa[TM], sb[TN];
+        const int cur = kt % NS, nxt = (kt + 1) % NS, pre = (kt + PD) % NS;
+        const int kpre = kt + PD < KB ? kt + PD : KB - 1;  // the tail re-loads the last stage
+        wait_lgkmcnt0();
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) sa[i] = (int)((*(const uint32_t *)(st + OFF_SA + arow[i] * 4) >> 23) & 0xFF);
+        for (int gi = 0; gi < NG; ++gi) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) sb[j] = (int)((*(const uint32_t *)(st + OFF_SB + brow[j] * 4) >> 23) & 0xFF);
+            for (int q = gi * PER / NG; q < (gi + 1) * PER / NG; ++q) X8_DMA(q, pre, kpre);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            i32x4 fa[TM][2], fb[TN][2];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                fa[i][0] = *(const i32x4 *)(st + sw128(arow[i], h * 4 + khalf));
-                fa[i][1] = *(const i32x4 *)(st + sw128(arow[i], h * 4 + 2 + khalf));
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                fb[j][0] = *(const i32x4 *)(st + OFF_B + sw128(brow[j], h * 4 + khalf));
-                fb[j][1] = *(const i32x4 *)(st + OFF_B + sw128(brow[j], h * 4 + 2 + khalf));
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const i32x8 av = {fa[i][0][0], fa[i][0][1], fa[i][0][2], fa[i][0][3],
-                                      fa[i][1][0], fa[i][1][1], fa[i][1][2], fa[i][1][3]};
-                    const i32x8 bv = {fb[j][0][0], fb[j][0][1], fb[j][0][2], fb[j][0][3],
-                                      fb[j][1][0], fb[j][1][1], fb[j][1][2], fb[j][1][3]};
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 0, 0, 0, sa[i],
-                                                                                0, sb[j]);
-                }
+            for (int u = gi * NR / NG; u < (gi + 1) * NR / NG; ++u) X8_FRAG(fa1, fb1, u, cur, 1);
+            X8_MFMA(fa0, fb0, gi);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        wait_lgkmcnt0();
+        wait_vmcnt<(PD - 1) * PER>();  // stage kt + 1 landed (this wave's loads)
+        X8_BARRIER();                  // every wave's; and every wave is done with stage kt
+        __builtin_amdgcn_sched_barrier(0);
+        int sa1[TM], sb1[TN];
+        X8_SCALES(sa1, sb1, nxt);
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+            for (int u = gi * NR / NG; u < (gi + 1) * NR / NG; ++u) X8_FRAG(fa0, fb0, u, nxt, 0);
+            X8_MFMA(fa1, fb1, gi);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) sa0[i] = sa1[i];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) sb0[j] = sb1[j];
     }
     wait_vmcnt<0>();
+#undef X8_DMA
+#undef X8_FRAG
+#undef X8_SCALES
+#undef X8_MFMA
+#undef X8_BARRIER
 
     // ---- epilogue ------------------------------------------------------------------------
     if constexpr (SWIGLU) {
