@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float *__restri
                                                           int k, int gating, const float *__restrict__ bias,
                                                           int32_t *idx, float *gate, float *logits, float *keys,
                                                           int32_t *err) {
-    extern __shared__ float lg[];  // [E]
+    extern __shared__ float lg[];  // [2][E]: logits, then the bias
     route_sum_select<false>(part, nks, T, E, k, gating, bias, blockIdx.x, lg, idx, gate, logits, keys, err);
 }
 
@@ -84,7 +84,7 @@ static hipError_t launch_route_select(const Shape &s, int nks, const float *part
                    (size_t)4 * s.E * sizeof(float), st, part, nks, s.T, s.E, s.k, s.gating, bias, idx, gate, logits,
                    keys, err);
     else
-        MOE_LAUNCH("route_select", route_select_kernel, dim3(s.T), dim3(256), (size_t)s.E * sizeof(float), st, part,
+        MOE_LAUNCH("route_select", route_select_kernel, dim3(s.T), dim3(256), (size_t)2 * s.E * sizeof(float), st, part,
                    nks, s.T, s.E, s.k, s.gating, bias, idx, gate, logits, keys, err);
     return hipGetLastError();
 }

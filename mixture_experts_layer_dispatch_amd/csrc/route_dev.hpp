@@ -369,16 +369,21 @@ __device__ __forceinline__ void route_sum_select_wave(const float *__restrict__ 
 }
 
 // 256 threads, token t: thread e adds expert e's K slices (all of them in one round trip
-// when there are more than 16), then wave 0 selects.  lg: E floats of LDS.
+// when there are more than 16) and copies the expert's bias beside them (its load in flight
+// with the slices', not after them), then wave 0 selects.  lg: 2 E floats of LDS.
 template <bool COH>
 __device__ __forceinline__ void route_sum_select(const float *__restrict__ part, int nks, int T, int E, int k,
                                                  int gating, const float *__restrict__ bias, long t, float *lg,
                                                  int32_t *idx, float *gate, float *logits, float *keys,
                                                  int32_t *err) {
-    for (int e = threadIdx.x; e < E; e += blockDim.x)
+    float *lb = lg + E;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        const float b = bias ? bias[e] : 0.0f;
         lg[e] = nks > 16 ? sum_slices<COH, 64>(part, nks, T, E, t, e) : sum_slices<COH, 16>(part, nks, T, E, t, e);
+        lb[e] = b;
+    }
     __syncthreads();
-    if (threadIdx.x < kWave) select_token<COH>(lg, E, k, gating, bias, t, idx, gate, logits, keys, err);
+    if (threadIdx.x < kWave) select_token<COH>(lg, E, k, gating, bias ? lb : nullptr, t, idx, gate, logits, keys, err);
 }
 
 }  // namespace moe
