@@ -499,15 +499,21 @@ def measure_capacity(w, inp, d, args, steps, warmup, factor, cpu_s, cpu_1t):
     log(f"{w.name} with capacity factor {factor}: {cap} slots per expert, T={w.T}")
     ws = moe.alloc_workspace(cfg)
     fp8 = w.mode in FP8
-    state = {}
+    # every output allocated once, as a serving loop would: the timed steps launch kernels only
+    idx = torch.empty(w.T, w.k, dtype=torch.int32, device="cuda")
+    gate = torch.empty(w.T, w.k, dtype=torch.float32, device="cuda")
+    dsp = moe.dispatch_capacity(cfg, moe.route(cfg, d["x"], d["w_router"], d["bias"], ws=ws, topk_idx=idx,
+                                               topk_gate=gate)[0], cap, d["x"] if fp8 else None, ws=ws)
+    yp = torch.empty(cfg.rows, w.d, dtype=torch.float32 if w.mode == "f32" else torch.bfloat16, device="cuda")
+    y = torch.empty(w.T, w.d, dtype=moe.act_dtype(cfg), device="cuda")
+    state = {"idx": idx, "gate": gate, "dsp": dsp, "y": y}
 
     def step():
-        idx, gate, _, _ = moe.route(cfg, d["x"], d["w_router"], d["bias"], ws=ws)
-        dsp = moe.dispatch_capacity(cfg, idx, cap, d["x"] if fp8 else None, ws=ws)
-        yp = moe.ffn(cfg, d["w1"], d["w2"], d["w1_scale"], d["w2_scale"], x=None if fp8 else d["x"], xq=dsp["xq"],
-                     xq_scale=dsp["xq_scale"], offsets=dsp["offsets"], row_to_slot=dsp["row_to_slot"], ws=ws)
-        state["y"] = moe.combine(cfg, yp, dsp["slot_to_row"], gate)
-        state.update(idx=idx, gate=gate, dsp=dsp)
+        moe.route(cfg, d["x"], d["w_router"], d["bias"], ws=ws, topk_idx=idx, topk_gate=gate)
+        moe.dispatch_capacity(cfg, idx, cap, d["x"] if fp8 else None, ws=ws, out=dsp)
+        moe.ffn(cfg, d["w1"], d["w2"], d["w1_scale"], d["w2_scale"], x=None if fp8 else d["x"], xq=dsp["xq"],
+                xq_scale=dsp["xq_scale"], offsets=dsp["offsets"], row_to_slot=dsp["row_to_slot"], ws=ws, y_perm=yp)
+        moe.combine(cfg, yp, dsp["slot_to_row"], gate, y=y)
 
     t = time_steps(step, steps, warmup)
     assert moe.read_device_error(cfg, ws) == 0
