@@ -147,6 +147,18 @@ static hipError_t launch_gemv_any(int qc, int nb, bool two, const char *name, di
     return launch_gemv<LIN1, 1, 8, 8>(name, grid, lds, st, a, rmax, ntn);
 }
 
+int fp8_gemv_qc(const Shape &s, int ntn) {
+    const long rows = s.rows();
+    const int G = s.G();
+    // the one-wave-per-tile grid bound of launch_fp8_decode, in quads of four waves
+    long ub = ((rows + 31) / 32 + (G < rows ? G : rows)) * (long)ntn;
+    if (ub > kDecodeMaxWaves) ub = kDecodeMaxWaves;
+    const long quads = ub / 4;
+    int qc = quads >= 1536 ? 4 : quads >= 768 ? 2 : 1;
+    while ((ntn / 4) % qc) qc /= 2;
+    return qc;
+}
+
 static hipError_t launch_fp8_decode(const Shape &s, const FfnPlan &p, const uint8_t *w1, const uint8_t *w1s,
                                     const uint8_t *w2, const uint8_t *w2s, const uint8_t *xq, const float *xs,
                                     const int32_t *offsets, const int32_t *row_to_slot, uint8_t *h, float *hs,
@@ -171,12 +183,7 @@ static hipError_t launch_fp8_decode(const Shape &s, const FfnPlan &p, const uint
         // two workgroup tiles per CU (measured, 9 experts x 4096 x 7168: 42.6 us with one
         // quad, 36 with two, 32.5 with four); every group's quad count (ntn / 4) is a
         // multiple of the choice
-        auto qc_for = [&](int ntn) {
-            const long quads = (long)(grid_for(ntn).x) / 4;
-            int qc = quads >= 1536 ? 4 : quads >= 768 ? 2 : 1;
-            while ((ntn / 4) % qc) qc /= 2;
-            return qc;
-        };
+        auto qc_for = [&](int ntn) { return fp8_gemv_qc(s, ntn); };
         // one workgroup per resident slot (two or one per CU), each streaming its tiles
         const int cus = 8 * xcd_cus();
         if (cus <= 0) return hipErrorInvalidDevice;

@@ -57,6 +57,16 @@ size_t gemm_lds(const Shape &s, const FfnPlan &p) {
     return l1 > l2 ? l1 : l2;
 }
 
+// The decode variant runs the stand-alone kernels' workgroup weight streams as its linear
+// phases: the shapes whose streams it instantiates (1024-wide K slices of linear1, 2048-wide
+// rows of W2, whole quads of column tiles in every group), from two tokens on.  With one
+// token its per-wave tiles and per-row-tile hand-offs were the faster ones (DeepSeek-V3
+// shape: 142 against 149 us); from 64 tokens the streams are (1.38 against 1.99 ms).
+bool fused_stream_ok(const Shape &s, const FfnPlan &p) {
+    if (s.mode != MODE_FP8 || !p.decode || !fp8_gemv_ok(s, p) || s.T < 2) return false;
+    return s.d / p.ks == 1024 && s.F == 2048 && (p.ntn1 / 4) % 4 == 0 && (p.ntn2 / 4) % 4 == 0;
+}
+
 }  // namespace
 
 int fused_row_tiles(const Shape &s, const FfnPlan &p) {
@@ -78,6 +88,10 @@ size_t fused_lds_bytes(const Shape &s, const FfnPlan &p) {
     const size_t m = (size_t)4 * s.E * 8 + (size_t)(s.E + 256) * 4, plan = (2 * 1032 + 256) * 4;
     const size_t cached = p.decode ? (size_t)3 * (s.G() + 1) * 4 : 0;  // the plan, kept in LDS
     for (size_t v : {r, m, plan, cached}) b = v > b ? v : b;
+    if (fused_stream_ok(s, p)) {  // the weight streams' plan and staging buffers
+        const int rmax = s.T < 32 ? s.T : 32;
+        for (size_t v : {fp8_gemv_lds(s.G(), rmax, 1024), fp8_gemv_lds(s.G(), rmax, 2048)}) b = v > b ? v : b;
+    }
     return b;
 }
 
@@ -149,6 +163,14 @@ hipError_t launch_layer_fused(const Shape &s, const FfnPlan &p, FusedArgs &a, in
     const int V = s.mode == MODE_F32 ? 4 : 8;
     const long lanes_c = (long)s.T * (s.d / V);
     a.ncb = p.decode ? (lanes_c + kWave - 1) / kWave : (lanes_c + 255) / 256;
+    // decode: workgroup weight streams where their shapes apply (column quads per tile as in
+    // the stand-alone kernels, 1 where those take 2); the blocks in flight follow from the
+    // occupancy at launch
+    a.sq1 = a.sq2 = a.sd1 = a.sd2 = 0;
+    if (fused_stream_ok(s, p)) {
+        a.sq1 = fp8_gemv_qc(s, p.ntn1) == 4 ? 4 : 1;
+        a.sq2 = fp8_gemv_qc(s, p.ntn2) == 4 ? 4 : 1;
+    }
     const size_t lds = fused_lds_bytes(s, p);
     if (s.mode == MODE_F32) return launch_fused_kernel<MODE_F32, 128, 128>(a, lds, cu_limit, st);
     if (s.mode == MODE_BF16) return launch_fused_bf16(a, p.bm1, p.bn2, lds, cu_limit, st);

@@ -28,7 +28,9 @@
 // last linear1 tile, one acquire before its first linear2 tile, and the same again around
 // the combine.
 //
-// Decode (FP8 x FP4, few rows per group): after the plan, items are single waves --
+// Decode (FP8 x FP4, few rows per group): from two tokens on, where the shapes allow, the
+// linear phases are the stand-alone kernels' workgroup weight streams, separated by
+// workgroup counts (linear1, SwiGLU, linear2).  Otherwise items are single waves --
 // weight-streaming tiles of linear1 (K slices), then of linear2, then combine chunks --
 // and every hand-off is coherent: the wave that completes the last linear1 slice of a
 // 32-row tile adds the slices, applies SwiGLU and quantises h for those rows, and then
@@ -603,6 +605,88 @@ __device__ __noinline__ void fp8_decode_tile_call(DecArgs d, int tile, int G) {
     fp8_decode_tile<LIN1, true, true>(d, uni(tile), lts, loffs);
 }
 
+// ---- decode with workgroup weight streams ----------------------------------------------
+//
+// The linear phases are the stand-alone kernels' workgroup weight streams (fp8_gemv_run:
+// a row tile's activations staged in LDS once for all of the workgroup's column tiles),
+// with coherent outputs; the phases are separated by workgroup counts (linear1, SwiGLU,
+// linear2, each waited for by every workgroup), so every hand-off is a coherent one and no
+// fence is needed.  Same tiles, same K slices, same k order per output element as the
+// stand-alone kernels: the same bits.
+
+// One workgroup's stream over the tile plan in LDS, out of line (its own register
+// allocation); the arguments are read back as uniform values.
+template <bool LIN1, int QC, int NB, int D>
+__device__ __noinline__ void gemv_stream_call(DecArgs d, int rmax, int total) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+    d.A = unip(d.A); d.As = unip(d.As); d.row_to_slot = unip(d.row_to_slot); d.offsets = unip(d.offsets);
+    d.tile_start = unip(d.tile_start); d.B = unip(d.B); d.Bs = unip(d.Bs); d.part = unip(d.part); d.Y = unip(d.Y);
+    d.T = uni(d.T); d.k = uni(d.k); d.K = uni(d.K); d.N = uni(d.N); d.G = uni(d.G); d.ks = uni(d.ks);
+    d.rows = ((long)uni((int)(d.rows >> 32)) << 32) | (uint32_t)uni((int)d.rows);
+    fp8_gemv_run<LIN1, QC, NB, D, true>(d, uni(rmax), (const int32_t *)lds_dyn, lds_dyn, uni(total));
+}
+
+// linear1 streams 1024-wide K slices (NB = 4), linear2 2048-wide ones (NB = 8); qc column
+// quads per workgroup tile (4, else 1), dd weight blocks in flight per wave (8 at one
+// workgroup per CU, else 4)
+template <bool LIN1>
+__device__ __forceinline__ void gemv_stream(const DecArgs &d, int rmax, int total, int qc, int dd) {
+    constexpr int NB = LIN1 ? 4 : 8;
+    if (qc == 4) {
+        if (dd == 8) gemv_stream_call<LIN1, 4, NB, 8>(d, rmax, total);
+        else gemv_stream_call<LIN1, 4, NB, 4>(d, rmax, total);
+    } else {
+        if constexpr (!LIN1) {
+            if (dd == 8) {
+                gemv_stream_call<LIN1, 1, NB, 8>(d, rmax, total);
+                return;
+            }
+        }
+        gemv_stream_call<LIN1, 1, NB, 4>(d, rmax, total);
+    }
+}
+
+// After the steps before the GEMMs (the front flag seen).  LDS: the current phase's tile
+// plan (tile starts, then group offsets, loaded from the workspace), then the stream's
+// staging buffers.
+__device__ __forceinline__ void fused_decode_stream(const FusedArgs &a, uint8_t *lds) {
+    const long P = gridDim.x;
+    const int G = a.G, lane = lane_id(), wave = threadIdx.x >> 6;
+    const int rmax = a.T < 32 ? a.T : 32;
+    int32_t *plan = (int32_t *)lds;
+    auto load_plan = [&](const int32_t *ts) {
+        __syncthreads();  // the previous phase is done with the LDS
+        for (int g = threadIdx.x; g <= G; g += blockDim.x) {
+            plan[g] = ldc<true>(ts + g);
+            plan[G + 1 + g] = ldc<true>(a.offsets + g);
+        }
+        __syncthreads();
+    };
+    load_plan(a.ts1);
+    const DecArgs d1 = {a.xq, a.xs, a.r2s, a.offsets, a.ts1, (const uint8_t *)a.w1, (const uint8_t *)a.w1s,
+                        a.upart, nullptr, a.rows, a.T, a.k, a.d, 2 * a.F, G, a.ks};
+    gemv_stream<true>(d1, rmax, plan[G] / (4 * a.sq1), a.sq1, a.sd1);
+    wg_count(a.sync, CNT_LIN1, blockIdx.x);
+    // SwiGLU and h's e4m3 codes: one wave per (row, 128-column block)
+    wg_counter_wait<16>(a.sync, CNT_LIN1, (int)P, a.err);
+    const long nsw = a.rows * (a.F / 128);
+    for (long w = blockIdx.x * 4 + wave; w < nsw; w += 4 * P)
+        decode_swiglu_wave<true>(a.upart, a.rows, a.F, a.ks, (uint8_t *)a.h, a.hs, w);
+    wg_count(a.sync, CNT_SWIGLU, blockIdx.x);
+    wg_counter_wait<16>(a.sync, CNT_SWIGLU, (int)P, a.err);
+    load_plan(a.ts2);
+    const DecArgs d2 = {(const uint8_t *)a.h, a.hs, nullptr, a.offsets, a.ts2, (const uint8_t *)a.w2,
+                        (const uint8_t *)a.w2s, nullptr, (uint16_t *)a.yperm, a.rows, a.T, a.k, a.F, a.d, G, 1};
+    gemv_stream<false>(d2, rmax, plan[G] / (4 * a.sq2), a.sq2, a.sd2);
+    wg_count(a.sync, CNT_LIN2, blockIdx.x);
+    // combine: 64 lanes x 8 columns per wave item; y_perm lines were written by two
+    // linear2 tiles each, all finished before this read
+    wg_counter_wait<16>(a.sync, CNT_LIN2, (int)P, a.err);
+    for (long w = blockIdx.x * 4 + wave; w < a.ncb; w += 4 * P)
+        combine_lane<false, false>(a.yperm, a.s2r, a.gate, a.y, a.T, a.k, a.d, a.S, w * kWave + lane);
+    fused_exit(a, lds);
+}
+
 __device__ __forceinline__ void fused_decode(const FusedArgs &a, uint8_t *lds) {
     const long P = gridDim.x;
     long i = blockIdx.x;
@@ -612,6 +696,10 @@ __device__ __forceinline__ void fused_decode(const FusedArgs &a, uint8_t *lds) {
         routed = front_item_out<MODE_FP8, false>(a, i, routed);
     }
     wg_flag_wait(a.sync, FLAG_FRONT, a.err);
+    if (a.sq1 > 0) {
+        fused_decode_stream(a, lds);
+        return;
+    }
     // the plan in LDS: tile prefixes of both GEMMs and the group offsets
     const int G = a.G;
     int32_t *lts1 = (int32_t *)lds, *lts2 = lts1 + (G + 1), *loffs = lts2 + (G + 1);

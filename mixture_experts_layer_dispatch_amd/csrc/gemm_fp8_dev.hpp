@@ -933,6 +933,12 @@ __device__ __forceinline__ void lds_dma4_hidden(const void *g, uint8_t *lds_bloc
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_u32(lds_block))
                  : "memory", "m0");
 }
+// the same copy at device scope (sc1): past the XCD's L2, for data other XCDs wrote
+// coherently during the same launch
+__device__ __forceinline__ void lds_dma4_hidden_sc1(const void *g, uint8_t *lds_block) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off sc1" ::"v"(g), "s"(lds_u32(lds_block))
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // The workgroup barrier of the weight stream: s_barrier with compiler fences only.  The
@@ -950,14 +956,19 @@ __device__ __forceinline__ void gemv_barrier() {
 // (K / ks = 256 NB), D blocks in the weight ring (D divides NB).  Block t of a tile is K
 // block t % NB of quad t / NB: each quad's 32 weight rows are streamed through in turn
 // (measured on MI355X, 9 x 4096 x 7168: 32.5 us in this order against 43 us when every K
-// block visits all four quads first), one accumulator per quad.
-template <bool LIN1, int QC, int NB, int D>
+// block visits all four quads first), one accumulator per quad.  A ring deeper than a
+// quad's slice (D = 2 NB) streams the quads in passes of D / NB, each pass with its own
+// accumulators, stored as soon as the pass's last block has landed.
+// COH (the persistent kernel): the outputs -- linear1 partial sums, linear2 rows -- are
+// stored device-coherently, and linear2's activation scales (an h-scale line holds rows
+// finished by different waves) are copied at device scope.
+template <bool LIN1, int QC, int NB, int D, bool COH = false>
 __device__ __forceinline__ void fp8_gemv_run(const DecArgs &a, int rmax, const int32_t *plan, uint8_t *lds,
                                              int total) {
     constexpr int KC = NB * 256, RS = KC + 16, NSC = KC / 128, NBT = QC * NB;
     constexpr int LPB = 5;  // global loads per weight block: four 16-byte code loads, one 8-byte scale load
     static_assert(NB == 4 || NB == 8, "K slices of 1024 or 2048");
-    static_assert(NB % D == 0 && D >= 2, "ring slot of block t is t % D");
+    static_assert((NB % D == 0 || (D % NB == 0 && QC % (D / NB) == 0)) && D >= 2, "ring slot of block t is t % D");
     const int P = gridDim.x, b0 = blockIdx.x;
     if (b0 >= total) return;
     const int ntile = (total - 1 - b0) / P + 1;
@@ -1012,7 +1023,10 @@ __device__ __forceinline__ void fp8_gemv_run(const DecArgs &a, int rmax, const i
         for (int q = wave; q * 64 < nsc; q += 4) {
             const int idx = q * 64 + lane < nsc ? q * 64 + lane : 0;
             const long src = src_of(n, t, idx / NSC);
-            lds_dma4_hidden(a.As + src * (a.K / 128) + kbeg / 128 + idx % NSC, (uint8_t *)(lsa + q * 64));
+            if (COH && !LIN1)
+                lds_dma4_hidden_sc1(a.As + src * (a.K / 128) + kbeg / 128 + idx % NSC, (uint8_t *)(lsa + q * 64));
+            else
+                lds_dma4_hidden(a.As + src * (a.K / 128) + kbeg / 128 + idx % NSC, (uint8_t *)(lsa + q * 64));
         }
     };
     const long qsb = 128L * (a.K / 2), qss = 128L * (a.K / 32);  // the next quad: 128 columns on
@@ -1025,11 +1039,17 @@ __device__ __forceinline__ void fp8_gemv_run(const DecArgs &a, int rmax, const i
     };
 
     // after the last tile the "next" blocks re-read the last quad's blocks NB - D .. NB - 2,
-    // read moments before (in bounds, cached, unused)
+    // read moments before (in bounds, cached, unused); a ring deeper than a quad re-reads the
+    // tile's first D - 1 blocks instead
     const uint8_t *pbC, *psC, *pbN, *psN;
     auto wptr_last = [&](const uint8_t *&pb, const uint8_t *&ps) {
-        pb = pbC + (QC - 1) * qsb + (NB - D) * 128;
-        ps = psC + (QC - 1) * qss + (NB - D) * 8;
+        if constexpr (D > NB) {
+            pb = pbC;
+            ps = psC;
+        } else {
+            pb = pbC + (QC - 1) * qsb + (NB - D) * 128;
+            ps = psC + (QC - 1) * qss + (NB - D) * 8;
+        }
     };
     i32x4 bq[D][4];
     uint2 sbw[D];
@@ -1082,6 +1102,7 @@ __device__ __forceinline__ void fp8_gemv_run(const DecArgs &a, int rmax, const i
         const int rr = r < cur.nrows ? r : 0;
         const uint8_t *arow = la + rr * RS;
         const float *asr = (const float *)(la + SCA) + rr * NSC;
+        if constexpr (D <= NB) {
         f32x16 acc[QC];
 #pragma unroll
         for (int c = 0; c < QC; ++c) acc[c] = (f32x16){};
@@ -1122,8 +1143,59 @@ __device__ __forceinline__ void fp8_gemv_run(const DecArgs &a, int rmax, const i
                 const int row = 8 * (qq >> 2) + 4 * kh + (qq & 3);
                 if (row >= cur.nrows) continue;
                 const long orow = cur.row0 + row;
-                if (LIN1) a.part[((long)cur.ksl * a.rows + orow) * a.N + ncol] = acc[c][qq];
-                else a.Y[orow * a.N + ncol] = f32_to_bf16(acc[c][qq]);
+                if constexpr (COH) {
+                    if (LIN1) stc<true>(a.part + ((long)cur.ksl * a.rows + orow) * a.N + ncol, acc[c][qq]);
+                    else stc16<true>(a.Y, (size_t)(orow * a.N + ncol), f32_to_bf16(acc[c][qq]));
+                } else {
+                    if (LIN1) a.part[((long)cur.ksl * a.rows + orow) * a.N + ncol] = acc[c][qq];
+                    else a.Y[orow * a.N + ncol] = f32_to_bf16(acc[c][qq]);
+                }
+            }
+        }
+        } else {
+            // the four MFMAs of K block i (256 wide) of a quad, weights from ring slot j
+            auto mma_block = [&](f32x16 &acc_, int i, int j) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const i32x4 lo4 = *(const i32x4 *)(arow + i * 256 + 64 * u + 16 * kh);
+                    const i32x4 hi4 = *(const i32x4 *)(arow + i * 256 + 64 * u + 32 + 16 * kh);
+                    i32x8 av = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+                    i32x8 bv = {bq[j][u][0], bq[j][u][1], bq[j][u][2], bq[j][u][3], 0, 0, 0, 0};
+                    const uint32_t sw = (u >> 1) ? sbw[j].y : sbw[j].x;
+                    const int sb = (int)((sw >> (8 * (2 * (u & 1) + kh))) & 0xFF);
+                    const int sa = (int)((__float_as_uint(asr[2 * i + (u >> 1)]) >> 23) & 0xFF);
+                    acc_ = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc_, 0, 4, 0, sa, 0, sb);
+                }
+            };
+            // the rows of quad c's 32 columns
+            auto store_quad = [&](const f32x16 &acc_, int c) {
+                const long ncol = (long)(4 * cur.qc * QC + wave) * 32 + r + (long)c * 128;
+#pragma unroll
+                for (int qq = 0; qq < 16; ++qq) {
+                    const int row = 8 * (qq >> 2) + 4 * kh + (qq & 3);
+                    if (row >= cur.nrows) continue;
+                    const long orow = cur.row0 + row;
+                    if (LIN1) stc<COH>(a.part + ((long)cur.ksl * a.rows + orow) * a.N + ncol, acc_[qq]);
+                    else stc16<COH>(a.Y, (size_t)(orow * a.N + ncol), f32_to_bf16(acc_[qq]));
+                }
+            };
+            // passes of D / NB quads: block t = p D + j sits in ring slot j
+            constexpr int QPR = D / NB;
+            int npass = QC / QPR;
+            asm volatile("" : "+s"(npass));  // a loop, not unrolled (see above)
+            for (int p = 0; p < npass; ++p) {
+                f32x16 accp[QPR];
+#pragma unroll
+                for (int c2 = 0; c2 < QPR; ++c2) accp[c2] = (f32x16){};
+#pragma unroll
+                for (int j = 0; j < D; ++j) {
+                    GEMV_LOAD((j + D - 1) % D, p * D + j + D - 1);  // into the slot block t - 1 freed
+                    wait_vmcnt<(D - 1) * LPB>();                      // block t landed
+                    mma_block(accp[j / NB], j % NB, j);
+                }
+                // the pass's last block landed, and with it every copy issued before it
+#pragma unroll
+                for (int c2 = 0; c2 < QPR; ++c2) store_quad(accp[c2], p * QPR + c2);
             }
         }
         cur = nxt;

@@ -64,6 +64,9 @@ FfnPlan ffn_plan(const Shape &s);
 size_t ffn_partial_bytes(const Shape &s);  // decode: fp32 linear1 partials [ks][rows][2F]
 // FP8 decode: the workgroup kernels run (and need no tile plan from tile_plan)
 bool fp8_gemv_ok(const Shape &s, const FfnPlan &p);
+// column quads per workgroup tile of the workgroup decode kernels (1, 2 or 4), for the
+// 32-column tiles ntn per row tile of linear1 (lin1) or linear2
+int fp8_gemv_qc(const Shape &s, int ntn);
 hipError_t launch_ffn(const Shape &s, const FfnPlan &p, const void *w1, const void *w1s, const void *w2,
                       const void *w2s, const void *x, const uint8_t *xq, const float *xs, const int32_t *offsets,
                       const int32_t *row_to_slot, void *h, float *hs, void *y_perm, int32_t *tile_start,
@@ -110,6 +113,7 @@ enum SyncCounter {
     CNT_LIN2,       // linear2 items (decode) or workgroups past linear2 (tiled) done
     CNT_EXIT,       // workgroups finished
     CNT_QUEUE,      // 512-thread tiled path: GEMM items taken, one sub-counter per queue
+    CNT_SWIGLU,     // decode with weight streams: workgroups past SwiGLU
     NUM_COUNTERS
 };
 enum SyncFlag {
@@ -157,6 +161,9 @@ struct FusedArgs {
     long b_r, b_sel, b_cnt, b_plan, b_end;
     long n1, n2;  // fp32 path: linear1 and linear2 items
     long ncb;     // combine items (workgroups of 256 lanes; waves of 64 on the decode path)
+    // decode with workgroup weight streams: column quads per workgroup tile and weight blocks
+    // in flight per wave of linear1 and linear2 (0: the decode path's per-wave tiles)
+    int sq1, sd1, sq2, sd2;
 };
 
 size_t fused_lds_bytes(const Shape &s, const FfnPlan &p);

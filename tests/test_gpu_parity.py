@@ -58,6 +58,11 @@ SMALL = {
     # (more than 16 rows of 16 activation scales each), then up to 2.2 rows per group (row
     # tiles of 32 rows, several per group)
     "fp8_decode_tall_20": Workload("fp8_decode_tall_20", 2020, "fp8_mxfp4", 20, 1024, 256, 4, 2048, 1, "softmax"),
+    # the persistent kernel's weight-stream phases at two workgroups per CU (few rows, small
+    # staging buffers: four weight blocks in flight per wave), one and four column quads per
+    # linear1 tile; tall_20 and rows_64 above take them at one workgroup per CU (eight blocks)
+    "fp8_decode_stream_4": Workload("fp8_decode_stream_4", 2030, "fp8_mxfp4", 4, 1024, 64, 4, 2048, 1, "sigmoid"),
+    "fp8_decode_stream_6": Workload("fp8_decode_stream_6", 2031, "fp8_mxfp4", 6, 1024, 256, 8, 2048, 1, "softmax"),
     "fp8_decode_rows_64": Workload("fp8_decode_rows_64", 2021, "fp8_mxfp4", 64, 1024, 256, 8, 2048, 1, "sigmoid",
                                    zipf_alpha=0.25),
     # no shared expert: G + 1 groups' plan words are an odd count (the staged rows behind them
@@ -120,7 +125,8 @@ def test_small_layer_parity(name):
 
 
 @pytest.mark.parametrize("name", ["bf16_sigmoid_shared", "f32_sigmoid_shared", "fp8_softmax_shared", "fp8_decode_5",
-                                  "bf16_w8", "fp8_w8_tiled_router", "fp8x8_sigmoid_zipf", "fp8_decode_rows_64"])
+                                  "bf16_w8", "fp8_w8_tiled_router", "fp8x8_sigmoid_zipf", "fp8_decode_rows_64",
+                                  "fp8_decode_tall_20", "fp8_decode_stream_6"])
 def test_fused_grid_sizes_and_repeats(name):
     """The persistent kernel gives the unfused bits on a full grid, on 8 CUs and on 3 CUs
     (many items per workgroup), call after call (each launch leaves its counters clean for
@@ -271,4 +277,11 @@ def test_full_size_parity(name, T):
     y2, idx2, _, _ = run_fused(w, d, cfg, ws)
     assert torch.equal(idx2, r["idx"])
     assert torch.equal(y2.view(torch.int16), r["y"].view(torch.int16)), "fused != unfused"
+    if w.mode == "fp8_mxfp4" and T <= 512:
+        # the persistent kernel's weight-stream phases on few workgroups (a stream of many
+        # tiles each), bitwise against the step chain again
+        for cu_limit in (8, 3):
+            log(f"full {name} T={T}: persistent kernel on {cu_limit} CUs")
+            y3, _, _, _ = run_fused(w, d, dataclasses.replace(cfg, cu_limit=cu_limit), ws)
+            assert torch.equal(y3.view(torch.int16), r["y"].view(torch.int16)), f"fused on {cu_limit} CUs != unfused"
     log(f"full {name} T={T}: rel L2 {err:.2e}, near-tie tokens {near}")
